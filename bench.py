@@ -1,0 +1,225 @@
+#!/usr/bin/env python3
+"""Benchmark of the W4A8 hot path on one MI355X.
+
+Workload: W4A8 int8 per-channel GEMM at N=8192, K=21760 (the GEMM shape the
+W4A8 Marlin PR benchmarks), M in {1, 16, 64, 256, 1024, 4096}.  One step is
+one pass of the per-call path over every M: dynamic per-token int8
+quantisation of fp16 activations [M, K], then the W4A8 GEMM with int4 weights
+(prepacked once, PB-v1) and fp32 per-channel scales, fp16 output.  All inputs
+are seeded synthetic data resident in HBM before timing starts; each M reads
+its own weight copy, so consecutive launches never find their weight in the
+256 MB last-level cache.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+Prints one JSON line.  value = total GEMM ops of a step (2*M*N*K summed over
+the M sweep) / step time, in TOPS (int8).  The line also carries per-M
+timings, the roofline of the dominant kernel, the prepack (a load-time step)
+and the CPU oracle timed on a bounded sample as a baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+N, K = 8192, 21760
+MS = (1, 16, 64, 256, 1024, 4096)
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+INT8_PEAK_TOPS = 5000.0         # MI355X dense int8 MFMA
+METRIC = "W4A8 GEMM TOPS + weight GB/s (% roofline), N=8192 K=21760, M=1..4096"
+
+
+def gemm_alg_bytes(M: int) -> int:
+    """Algorithmic bytes of one W4A8 GEMM launch: packed weight, fp32 channel
+    scales, int8 activations + fp32 row scales, fp16 output."""
+    return N * K // 2 + 4 * N + M * K + 4 * M + 2 * M * N
+
+
+def quant_alg_bytes(M: int) -> int:
+    return 2 * M * K + M * K + 4 * M
+
+
+def cpu_baseline(seconds: float) -> dict:
+    """The oracle as it stands (numpy, float64 BLAS) on a bounded sample of
+    the same workload: 64 rows x 1024 output columns at the full K."""
+    import numpy as np
+    import threadpoolctl
+
+    import workloads
+    from oracle import w4_oracle as O
+    wl = workloads.WORKLOADS["w4a8_i8_pc_8192x21760"]
+    Ms, Ns = 64, 1024
+    case = workloads.make_case(wl, Ms, N=Ns, K=K, seed_base=42)
+    ab = case.a.view(__import__("torch").int16).numpy().view(np.uint16)
+    wl_np = case.w_logical.numpy()
+    s = case.w_scales.numpy()
+    iters, t0 = 0, time.perf_counter()
+    while True:
+        codes, sa = O.quant_act_per_token(ab, "f16", "i8")
+        O.w4a8_gemm(codes, "i8", sa, wl_np, K, "int4", s, "f32", K, "f16")
+        iters += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    info = threadpoolctl.threadpool_info()
+    threads = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
+    ops = 2.0 * Ms * Ns * K * iters
+    return {"value": round(ops / el / 1e12, 6), "unit": "TOPS", "cores": int(threads), "kind": "oracle",
+            "sample": f"M={Ms} rows x N={Ns} columns x K={K} (int8 per-token quant + exact int4 GEMM + "
+                      f"fp64 epilogue), {iters} runs in {el:.1f} s; host has {os.cpu_count()} CPUs"}
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--ms", default=",".join(str(m) for m in MS))
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: the kernels run on a single MI355X and this build has no "
+              f"multi-GPU path (asked for --gpus {args.gpus}).", file=sys.stderr)
+        return 2
+    Ms = tuple(int(x) for x in args.ms.split(","))
+
+    import torch
+
+    import mixed_precision_quantized_prepack_amd as w4
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w4.lib()
+    wl = workloads.WORKLOADS["w4a8_i8_pc_8192x21760"]
+
+    # ---- inputs, resident in HBM ------------------------------------------
+    case = workloads.make_case(wl, max(Ms), seed_base=2024)
+    a = case.a.to(dev)
+    w0 = case.w_logical.to(dev)
+    scales = case.w_scales.to(dev)
+    copies = len(Ms)
+    logical = [workloads.weight_copy(w0, i).contiguous() for i in range(copies)]
+    packed = [torch.empty(N * K // 2, dtype=torch.uint8, device=dev) for _ in range(copies)]
+    aq = {M: torch.empty((M, K), dtype=torch.int8, device=dev) for M in Ms}
+    sa = {M: torch.empty((M,), dtype=torch.float32, device=dev) for M in Ms}
+    out = {M: torch.empty((M, N), dtype=torch.float16, device=dev) for M in Ms}
+    ws_bytes = max(w4.gemm_workspace_bytes(M, N, K, -1, w4.I8) for M in Ms)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    plans = {M: w4.gemm_plan(M, N, K, -1, w4.I8) for M in Ms}
+
+    # prepack (load-time): one launch per weight copy, timed with events
+    pev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(copies)]
+    for i in range(copies):
+        pev[i][0].record()
+        w4.prepack_B(logical[i], "i8", out=packed[i])
+        pev[i][1].record()
+    torch.cuda.synchronize()
+    prepack_us = sorted(s.elapsed_time(e) * 1e3 for s, e in pev)
+    del logical
+
+    def step(evs):
+        for i, M in enumerate(Ms):
+            if evs is not None:
+                evs[i][0].record()
+            w4.quant_act_per_token(a[:M], "i8", out=aq[M], scales=sa[M])
+            if evs is not None:
+                evs[i][1].record()
+            w4.w4a8_gemm(aq[M], sa[M], packed[i % copies], scales, -1, torch.float16, out=out[M],
+                         workspace=ws)
+            if evs is not None:
+                evs[i][2].record()
+
+    for _ in range(args.warmup):
+        step(None)
+    torch.cuda.synchronize()
+
+    mk = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    all_evs = [[(mk(), mk(), mk()) for _ in Ms] for _ in range(args.steps)]
+    t_start, t_end = mk(), mk()
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record()
+    for s in range(args.steps):
+        step(all_evs[s])
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_per_step = t_start.elapsed_time(t_end) / args.steps
+
+    # ---- per-M figures ----------------------------------------------------
+    per_m = []
+    total_ops = 0.0
+    for i, M in enumerate(Ms):
+        q_us = sum(all_evs[s][i][0].elapsed_time(all_evs[s][i][1]) for s in range(args.steps)) * 1e3 / args.steps
+        g_us = sum(all_evs[s][i][1].elapsed_time(all_evs[s][i][2]) for s in range(args.steps)) * 1e3 / args.steps
+        ops = 2.0 * M * N * K
+        total_ops += ops
+        path, split = plans[M]
+        tops = ops / (g_us * 1e-6) / 1e12
+        wgbps = (N * K / 2) / (g_us * 1e-6) / 1e9
+        agbps = gemm_alg_bytes(M) / (g_us * 1e-6) / 1e9
+        per_m.append({"M": M, "kernel": "small_m" if path == 1 else "tiled", "k_split": split,
+                      "gemm_us": round(g_us, 2), "quant_us": round(q_us, 2), "gemm_tops": round(tops, 2),
+                      "weight_GBps": round(wgbps, 1), "alg_GBps": round(agbps, 1),
+                      "hbm_frac": round(agbps / HBM_PEAK_GBPS, 4),
+                      "mfma_frac": round(tops / INT8_PEAK_TOPS, 4)})
+    value = total_ops / (ms_per_step * 1e-3) / 1e12
+
+    # dominant kernel: the tiled kernel without K split (the large-M launches)
+    dom = [(pm["M"], pm["gemm_us"]) for pm in per_m if pm["kernel"] == "tiled" and pm["k_split"] == 1]
+    if dom:
+        flops = sum(2.0 * M * N * K for M, _ in dom) / len(dom)
+        dur = sum(us for _, us in dom) / len(dom)
+        ach = flops / (dur * 1e-6) / 1e12
+        roofline = {"bound": "mfma", "achieved": round(ach, 2), "peak": INT8_PEAK_TOPS, "unit": "TFLOP/s",
+                    "frac": round(ach / INT8_PEAK_TOPS, 4), "traffic": None,
+                    "kernel": "w4_gemm_tiled<int8, per-channel, no K split>",
+                    "launches": [M for M, _ in dom], "avg_launch_us": round(dur, 2),
+                    "note": "int8 ops (2 per multiply-add) per second"}
+    else:
+        roofline = None
+    small = [pm for pm in per_m if pm["kernel"] == "small_m"]
+    roofline_small = None
+    if small:
+        b = sum(gemm_alg_bytes(pm["M"]) for pm in small) / len(small)
+        dur = sum(pm["gemm_us"] for pm in small) / len(small)
+        gb = b / (dur * 1e-6) / 1e9
+        roofline_small = {"bound": "hbm", "achieved": round(gb, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                          "frac": round(gb / HBM_PEAK_GBPS, 4), "traffic": None,
+                          "kernel": "w4_gemm_skinny<int8, per-channel>", "launches": [pm["M"] for pm in small],
+                          "avg_launch_us": round(dur, 2)}
+
+    line = {
+        "metric": METRIC, "value": round(value, 3), "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "int8", "data": "synthetic",
+        "config": {"workload": "w4a8_i8_pc_8192x21760", "N": N, "K": K, "Ms": list(Ms),
+                   "activations": "fp16 ~N(0,1), dynamic per-token int8", "weights": "int4 uniform [-8,7], PB-v1",
+                   "scales": "fp32 per channel ~U(0.005,0.02)", "out": "fp16", "weight_copies": copies},
+        "weight_GBps_step": round(copies * (N * K / 2) / (ms_per_step * 1e-3) / 1e9, 1),
+        "per_m": per_m,
+        "roofline": roofline,
+        "roofline_small_m": roofline_small,
+        "prepack": {"median_us": round(prepack_us[len(prepack_us) // 2], 2),
+                    "GBps_read_plus_write": round(N * K / (prepack_us[len(prepack_us) // 2] * 1e-6) / 1e9, 1)},
+        "wall_s_timed": round(wall, 3),
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

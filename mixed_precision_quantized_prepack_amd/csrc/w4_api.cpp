@@ -1,0 +1,413 @@
+// C ABI of the 4-bit-weight GEMM library: argument validation, kernel
+// selection and launch.  Validation runs entirely on the host and returns
+// before any HIP call, so a rejected call enqueues nothing.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "w4.h"
+#include "w4_internal.h"
+
+namespace {
+
+using namespace w4;
+
+thread_local std::string g_last_error;
+
+std::atomic<int64_t> g_force_path{0};
+std::atomic<int64_t> g_splitk{0};
+
+int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+int ok() {
+  g_last_error.clear();
+  return W4_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(W4_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Compute units of the current device, cached per device.  Falls back to the
+// MI355X count when no device can be queried (planning-only calls on a host
+// without a GPU).
+int cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) {
+    (void)hipGetLastError();
+    v = 256;
+  }
+  cache[dev].store(v, std::memory_order_relaxed);
+  return v;
+}
+
+int64_t resolve_group(int64_t group_size, int64_t K) { return group_size == -1 ? K : group_size; }
+
+int op_of(int a_dtype) {
+  switch (a_dtype) {
+    case W4_I8: return OP_I8;
+    case W4_FP8_E4M3: return OP_FP8;
+    case W4_F16: return OP_F16;
+    case W4_BF16: return OP_BF16;
+    default: return -1;
+  }
+}
+
+int check_shape(int64_t M, int64_t N, int64_t K) {
+  if (M < 0 || N <= 0 || K <= 0)
+    return fail(W4_E_SHAPE, "need M >= 0, N > 0, K > 0 (got M=%lld N=%lld K=%lld)", (long long)M,
+                (long long)N, (long long)K);
+  if (N % 16) return fail(W4_E_SHAPE, "N=%lld must be a multiple of 16", (long long)N);
+  if (K % 128) return fail(W4_E_SHAPE, "K=%lld must be a multiple of 128", (long long)K);
+  if (M > (int64_t)1 << 30 || N > (int64_t)1 << 30 || K > (int64_t)1 << 30)
+    return fail(W4_E_SHAPE, "sizes above 2^30 are not supported");
+  return W4_OK;
+}
+
+int check_group(int64_t group_size, int64_t K) {
+  const int64_t g = resolve_group(group_size, K);
+  if (g != K && g != 128)
+    return fail(W4_E_GROUP, "group_size=%lld: supported values are K, -1 and 128", (long long)group_size);
+  if (K % g) return fail(W4_E_GROUP, "group_size=%lld does not divide K=%lld", (long long)g, (long long)K);
+  return W4_OK;
+}
+
+// Kernel choice.  Small M is bound by the weight stream and uses the skinny
+// kernel with enough K-splitting waves to keep ~16 waves per CU in flight;
+// larger M uses the tiled kernel, split along K while there are fewer tiles
+// than CUs.
+int make_plan(int64_t M, int64_t N, int64_t K, bool grouped, int op, GemmPlan* plan) {
+  const int64_t fp = g_force_path.load(), fs = g_splitk.load();
+  const int64_t KB = K / 128;
+  const int cu = cu_count();
+  plan->path = fp ? (int)fp : (M <= 16 ? PATH_SKINNY : PATH_TILED);
+  tiled_tile(op, grouped, &plan->bm, &plan->bn);
+  if (plan->path == PATH_SKINNY) {
+    if (M > 16) return fail(W4_E_UNSUPPORTED, "the small-M kernel handles M <= 16 (M=%lld)", (long long)M);
+    int64_t s;
+    if (fs) {
+      s = fs;
+    } else {
+      const int64_t strips = N / 16;
+      const int64_t want = (16LL * cu + strips - 1) / strips;
+      s = 1;
+      while (s < want && s < 16) s *= 2;
+      while (s > 1 && KB / s < 2) s /= 2;
+    }
+    if (s < 1 || s > 16 || s > KB)
+      return fail(W4_E_SHAPE, "small-M kernel: %lld K-splitting waves not in [1, min(16, K/128)]", (long long)s);
+    plan->splitk = (int)s;
+  } else {
+    int64_t s;
+    if (fs) {
+      s = fs;
+    } else {
+      const int64_t tiles = ((M + plan->bm - 1) / plan->bm) * ((N + plan->bn - 1) / plan->bn);
+      s = 1;
+      while (tiles * s < cu && s * 2 <= 16 && KB / (s * 2) >= 4) s *= 2;
+    }
+    if (s < 1 || s > 64 || s > KB)
+      return fail(W4_E_SHAPE, "tiled kernel: K split %lld not in [1, min(64, K/128)]", (long long)s);
+    plan->splitk = (int)s;
+  }
+  return W4_OK;
+}
+
+size_t workspace_for(const GemmPlan& plan, int64_t M, int64_t N) {
+  if (plan.path != PATH_TILED || plan.splitk <= 1) return 0;
+  return (size_t)plan.splitk * (size_t)M * (size_t)N * 4u;
+}
+
+// Shared front end of the four GEMM entry points.
+int run_gemm(GemmArgs& args, int op, bool grouped, bool flip, void* workspace, size_t workspace_bytes,
+             void* stream) {
+  GemmPlan plan;
+  if (int st = make_plan(args.M, args.N, args.K, grouped, op, &plan)) return st;
+  const size_t need = workspace_for(plan, args.M, args.N);
+  if (need) {
+    if (!workspace || workspace_bytes < need)
+      return fail(W4_E_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need,
+                  workspace ? workspace_bytes : (size_t)0);
+    if (!aligned(workspace, 16)) return fail(W4_E_ALIGN, "workspace must be 16-byte aligned");
+  }
+  args.ws = workspace;
+  if (args.M == 0) return ok();
+  hipError_t e = launch_gemm(args, op, grouped, flip, plan, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "GEMM launch");
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int w4_abi_version(void) { return W4_ABI_VERSION; }
+int w4_layout_version(void) { return W4_LAYOUT_VERSION; }
+
+const char* w4_status_string(int status) {
+  switch (status) {
+    case W4_OK: return "W4_OK";
+    case W4_E_NULL: return "W4_E_NULL: required pointer is NULL";
+    case W4_E_SHAPE: return "W4_E_SHAPE: invalid size";
+    case W4_E_DTYPE: return "W4_E_DTYPE: unsupported dtype combination";
+    case W4_E_ALIGN: return "W4_E_ALIGN: pointer not 16-byte aligned";
+    case W4_E_GROUP: return "W4_E_GROUP: unsupported group size";
+    case W4_E_WORKSPACE: return "W4_E_WORKSPACE: workspace missing or too small";
+    case W4_E_UNSUPPORTED: return "W4_E_UNSUPPORTED: not implemented for these arguments";
+    case W4_E_HIP: return "W4_E_HIP: HIP runtime error";
+    default: return "unknown w4_status";
+  }
+}
+
+const char* w4_last_error(void) { return g_last_error.c_str(); }
+
+size_t w4_prepack_B_bytes(int64_t N, int64_t K) {
+  if (N <= 0 || K <= 0) return 0;
+  return (size_t)N * (size_t)K / 2u;
+}
+
+int w4_prepack_B(const void* w_logical, void* w_packed, int64_t N, int64_t K, int operand,
+                 void* stream) {
+  if (!w_logical || !w_packed) return fail(W4_E_NULL, "w_logical and w_packed are required");
+  if (int st = check_shape(0, N, K)) return st;
+  if (operand != W4_OPERAND_I8 && operand != W4_OPERAND_F16)
+    return fail(W4_E_DTYPE, "operand must be W4_OPERAND_I8 or W4_OPERAND_F16");
+  if (!aligned(w_logical, 16) || !aligned(w_packed, 16))
+    return fail(W4_E_ALIGN, "w_logical and w_packed must be 16-byte aligned");
+  const char* a = static_cast<const char*>(w_logical);
+  const char* b = static_cast<const char*>(w_packed);
+  const size_t bytes = w4_prepack_B_bytes(N, K);
+  if (a < b + bytes && b < a + bytes) return fail(W4_E_SHAPE, "input and output overlap");
+  hipError_t e = launch_prepack(w_logical, w_packed, N, K, operand, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "prepack launch");
+  return ok();
+}
+
+int w4_quant_act_per_token(const void* x, int x_dtype, void* xq, int q_dtype, float* scales,
+                           int64_t M, int64_t K, void* stream) {
+  if (x_dtype != W4_F16 && x_dtype != W4_BF16) return fail(W4_E_DTYPE, "x_dtype must be W4_F16 or W4_BF16");
+  if (q_dtype != W4_I8 && q_dtype != W4_FP8_E4M3)
+    return fail(W4_E_DTYPE, "q_dtype must be W4_I8 or W4_FP8_E4M3");
+  if (M < 0 || K <= 0 || K % 8 || M > ((int64_t)1 << 31) - 1 || K > ((int64_t)1 << 30))
+    return fail(W4_E_SHAPE, "need M >= 0, 0 < K <= 2^30, K %% 8 == 0 (M=%lld K=%lld)", (long long)M,
+                (long long)K);
+  if (M == 0) return ok();
+  if (!x || !xq || !scales) return fail(W4_E_NULL, "x, xq and scales are required");
+  if (!aligned(x, 16) || !aligned(xq, 16) || !aligned(scales, 4))
+    return fail(W4_E_ALIGN, "x and xq must be 16-byte aligned, scales 4-byte aligned");
+  hipError_t e = launch_quant(x, x_dtype, xq, q_dtype, scales, M, K, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "quant launch");
+  return ok();
+}
+
+size_t w4_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t group_size, int a_dtype) {
+  const int op = op_of(a_dtype);
+  if (op < 0 || check_shape(M, N, K) || check_group(group_size, K)) return 0;
+  GemmPlan plan;
+  const bool grouped = resolve_group(group_size, K) != K;
+  if (make_plan(M, N, K, grouped, op, &plan)) return 0;
+  return workspace_for(plan, M, N);
+}
+
+int w4_gemm_plan(int64_t M, int64_t N, int64_t K, int64_t group_size, int a_dtype, int* path, int* splitk) {
+  const int op = op_of(a_dtype);
+  if (op < 0) return fail(W4_E_DTYPE, "unknown a_dtype");
+  if (int st = check_shape(M, N, K)) return st;
+  if (int st = check_group(group_size, K)) return st;
+  GemmPlan plan;
+  if (int st = make_plan(M, N, K, resolve_group(group_size, K) != K, op, &plan)) return st;
+  if (path) *path = plan.path;
+  if (splitk) *splitk = plan.splitk;
+  return ok();
+}
+
+static int validate_w4a8(const void* aq, int a_dtype, const void* b_packed, int wtype, int64_t group_size,
+                         int64_t M, int64_t N, int64_t K) {
+  if (a_dtype != W4_I8 && a_dtype != W4_FP8_E4M3)
+    return fail(W4_E_DTYPE, "a_dtype must be W4_I8 or W4_FP8_E4M3");
+  if (wtype != W4_INT4 && wtype != W4_UINT4B8)
+    return fail(W4_E_DTYPE, "W4A8 weights are W4_INT4 or W4_UINT4B8 (symmetric)");
+  if (int st = check_shape(M, N, K)) return st;
+  if (int st = check_group(group_size, K)) return st;
+  if (a_dtype == W4_I8 && resolve_group(group_size, K) == K && K > 131072)
+    return fail(W4_E_SHAPE, "int8 per-channel accumulation needs K <= 131072 (int32 range)");
+  if (!b_packed || (M > 0 && !aq)) return fail(W4_E_NULL, "aq and b_packed are required");
+  if (!aligned(aq, 16) || !aligned(b_packed, 16)) return fail(W4_E_ALIGN, "aq and b_packed must be 16-byte aligned");
+  return W4_OK;
+}
+
+int w4a8_gemm(const void* aq, int a_dtype, const float* a_scales, const void* b_packed, int wtype,
+              const void* b_scales, int s_dtype, int64_t group_size, const void* bias, void* out,
+              int out_dtype, int64_t M, int64_t N, int64_t K, void* workspace, size_t workspace_bytes,
+              void* stream) {
+  if (int st = validate_w4a8(aq, a_dtype, b_packed, wtype, group_size, M, N, K)) return st;
+  if (s_dtype != W4_F32 && s_dtype != W4_F16 && s_dtype != W4_BF16)
+    return fail(W4_E_DTYPE, "s_dtype must be W4_F32, W4_F16 or W4_BF16");
+  if (out_dtype != W4_F16 && out_dtype != W4_BF16) return fail(W4_E_DTYPE, "out_dtype must be W4_F16 or W4_BF16");
+  if (!b_scales || (M > 0 && (!a_scales || !out))) return fail(W4_E_NULL, "a_scales, b_scales and out are required");
+  if (!aligned(out, 16) || !aligned(a_scales, 4) || !aligned(b_scales, s_dtype == W4_F32 ? 4 : 2) ||
+      !aligned(bias, 2))
+    return fail(W4_E_ALIGN, "out must be 16-byte aligned; scales and bias naturally aligned");
+  const int64_t g = resolve_group(group_size, K);
+  GemmArgs args{};
+  args.a = aq;
+  args.a_scales = a_scales;
+  args.b = static_cast<const uint32_t*>(b_packed);
+  args.s = b_scales;
+  args.bias = bias;
+  args.out = out;
+  args.M = M;
+  args.N = N;
+  args.K = K;
+  args.G = (int)(K / g);
+  args.s_dtype = s_dtype;
+  args.out_dtype = out_dtype;
+  args.mode = MODE_OUTPUT;
+  return run_gemm(args, op_of(a_dtype), g != K, wtype == W4_UINT4B8, workspace, workspace_bytes, stream);
+}
+
+static int validate_w4a16(const void* a, int a_dtype, const void* b_packed, int wtype, const void* zeros,
+                          int64_t group_size, int64_t M, int64_t N, int64_t K) {
+  if (a_dtype != W4_F16 && a_dtype != W4_BF16) return fail(W4_E_DTYPE, "a_dtype must be W4_F16 or W4_BF16");
+  if (wtype != W4_UINT4 && wtype != W4_UINT4B8)
+    return fail(W4_E_DTYPE, "W4A16 weights are W4_UINT4 or W4_UINT4B8");
+  if (wtype == W4_UINT4B8 && zeros) return fail(W4_E_DTYPE, "W4_UINT4B8 weights take no zero-points");
+  if (int st = check_shape(M, N, K)) return st;
+  if (int st = check_group(group_size, K)) return st;
+  if (!b_packed || (M > 0 && !a)) return fail(W4_E_NULL, "a and b_packed are required");
+  if (!aligned(a, 16) || !aligned(b_packed, 16)) return fail(W4_E_ALIGN, "a and b_packed must be 16-byte aligned");
+  if (!aligned(zeros, 2)) return fail(W4_E_ALIGN, "zeros must be 2-byte aligned");
+  return W4_OK;
+}
+
+int w4a16_gemm(const void* a, int a_dtype, const void* b_packed, int wtype, const void* scales,
+               const void* zeros, int64_t group_size, const void* bias, void* out, int64_t M, int64_t N,
+               int64_t K, void* workspace, size_t workspace_bytes, void* stream) {
+  if (int st = validate_w4a16(a, a_dtype, b_packed, wtype, zeros, group_size, M, N, K)) return st;
+  if (!scales || (M > 0 && !out)) return fail(W4_E_NULL, "scales and out are required");
+  if (!aligned(out, 16) || !aligned(scales, 2) || !aligned(bias, 2))
+    return fail(W4_E_ALIGN, "out must be 16-byte aligned; scales and bias 2-byte aligned");
+  const int64_t g = resolve_group(group_size, K);
+  GemmArgs args{};
+  args.a = a;
+  args.b = static_cast<const uint32_t*>(b_packed);
+  args.s = scales;
+  args.z = zeros;
+  args.bias = bias;
+  args.out = out;
+  args.M = M;
+  args.N = N;
+  args.K = K;
+  args.G = (int)(K / g);
+  args.s_dtype = a_dtype;
+  args.out_dtype = a_dtype;
+  args.mode = MODE_OUTPUT;
+  return run_gemm(args, op_of(a_dtype), g != K, false, workspace, workspace_bytes, stream);
+}
+
+static int check_window(int64_t M, int64_t N, int64_t m0, int64_t m1, int64_t n0, int64_t n1) {
+  if (m0 < 0 || m0 > m1 || m1 > M || n0 < 0 || n0 > n1 || n1 > N)
+    return fail(W4_E_SHAPE, "window rows [%lld,%lld) cols [%lld,%lld) outside [0,%lld) x [0,%lld)",
+                (long long)m0, (long long)m1, (long long)n0, (long long)n1, (long long)M, (long long)N);
+  return W4_OK;
+}
+
+int w4a8_gemm_partials(const void* aq, int a_dtype, const void* b_packed, int wtype, int64_t group_size,
+                       int64_t M, int64_t N, int64_t K, int64_t m0, int64_t m1, int64_t n0, int64_t n1,
+                       void* partials, void* workspace, size_t workspace_bytes, void* stream) {
+  if (int st = validate_w4a8(aq, a_dtype, b_packed, wtype, group_size, M, N, K)) return st;
+  if (int st = check_window(M, N, m0, m1, n0, n1)) return st;
+  if (m1 > m0 && n1 > n0 && !partials) return fail(W4_E_NULL, "partials is required");
+  if (!aligned(partials, 4)) return fail(W4_E_ALIGN, "partials must be 4-byte aligned");
+  const int64_t g = resolve_group(group_size, K);
+  GemmArgs args{};
+  args.a = aq;
+  args.b = static_cast<const uint32_t*>(b_packed);
+  args.partials = partials;
+  args.M = M;
+  args.N = N;
+  args.K = K;
+  args.G = (int)(K / g);
+  args.s_dtype = W4_F32;
+  args.out_dtype = W4_F16;
+  args.mode = MODE_PARTIALS;
+  args.m0 = m0;
+  args.m1 = m1;
+  args.n0 = n0;
+  args.n1 = n1;
+  return run_gemm(args, op_of(a_dtype), g != K, wtype == W4_UINT4B8, workspace, workspace_bytes, stream);
+}
+
+int w4a16_gemm_partials(const void* a, int a_dtype, const void* b_packed, int wtype, const void* zeros,
+                        int64_t group_size, int64_t M, int64_t N, int64_t K, int64_t m0, int64_t m1,
+                        int64_t n0, int64_t n1, void* partials, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  if (int st = validate_w4a16(a, a_dtype, b_packed, wtype, zeros, group_size, M, N, K)) return st;
+  if (int st = check_window(M, N, m0, m1, n0, n1)) return st;
+  if (m1 > m0 && n1 > n0 && !partials) return fail(W4_E_NULL, "partials is required");
+  if (!aligned(partials, 4)) return fail(W4_E_ALIGN, "partials must be 4-byte aligned");
+  const int64_t g = resolve_group(group_size, K);
+  GemmArgs args{};
+  args.a = a;
+  args.b = static_cast<const uint32_t*>(b_packed);
+  args.z = zeros;
+  args.partials = partials;
+  args.M = M;
+  args.N = N;
+  args.K = K;
+  args.G = (int)(K / g);
+  args.s_dtype = a_dtype;
+  args.out_dtype = a_dtype;
+  args.mode = MODE_PARTIALS;
+  args.m0 = m0;
+  args.m1 = m1;
+  args.n0 = n0;
+  args.n1 = n1;
+  return run_gemm(args, op_of(a_dtype), g != K, false, workspace, workspace_bytes, stream);
+}
+
+int w4_set_option(const char* key, int64_t value) {
+  if (!key) return fail(W4_E_NULL, "key is required");
+  if (!strcmp(key, "force_path")) {
+    if (value < 0 || value > 2) return fail(W4_E_SHAPE, "force_path must be 0, 1 or 2");
+    g_force_path.store(value);
+    return ok();
+  }
+  if (!strcmp(key, "splitk")) {
+    if (value < 0 || value > 64) return fail(W4_E_SHAPE, "splitk must be in [0, 64]");
+    g_splitk.store(value);
+    return ok();
+  }
+  return fail(W4_E_UNSUPPORTED, "unknown option '%s'", key);
+}
+
+int64_t w4_get_option(const char* key) {
+  if (!key) return -1;
+  if (!strcmp(key, "force_path")) return g_force_path.load();
+  if (!strcmp(key, "splitk")) return g_splitk.load();
+  return -1;
+}
+
+}  // extern "C"

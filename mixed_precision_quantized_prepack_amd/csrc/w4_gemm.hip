@@ -1,0 +1,579 @@
+// W4A8 / W4A16 GEMM kernels for gfx950.
+//
+//   out[m,n] = RNE( s_a[m] * sum_g s[n,g] * sum_{k in g} a[m,k] * w[n,k] + bias[n] )
+//
+// (Machete README, "Overview"; "support W4A8 Marlin kernel" for the
+// per-channel / per-group W4A8 variants; the rdna_hybrid_w4a16 API page for
+// the W4A16 zero-point form (c - z) * s.)
+//
+// Two kernels share the operand expansion and the MFMA step:
+//   * w4_gemm_skinny: M <= 16.  The weight stream is the whole cost, so one
+//     wave walks a 16-column strip of W over a contiguous K range with wide
+//     (16-byte) loads; the waves of a workgroup split K and are summed through
+//     LDS in a fixed order.
+//   * w4_gemm_tiled: larger M.  A BM x BN output tile per workgroup; the
+//     activation tile of each 128-deep K step is staged in LDS (double
+//     buffered) and shared by the four waves, each of which streams its own
+//     weight blocks from memory.  Few tiles -> K is split across workgroups
+//     and a second kernel sums the partial tiles in a fixed order.
+//
+// Matrix-core mapping (one PB-v1 block = 16 n x 128 k):
+//   MFMA operand A = weights, lane l supplies row n = l%16 and the 32 k of
+//   lane group l/16; operand B = activations, lane l supplies row m = l%16
+//   with the same k set.  D element i of lane l is (n = 4*(l/16)+i, m = l%16).
+//   int8 : 2 x v_mfma_i32_16x16x64_i8   per block (weights as 16*w)
+//   fp8  : 1 x v_mfma_scale_f32_16x16x128_f8f6f4 (e4m3 x e4m3, unit scales)
+//   fp16 / bf16 : 4 x v_mfma_f32_16x16x32_{f16,bf16}
+// Group-128 problems restart the block accumulator every block (one block is
+// one group) and fold it into an fp32 total with the group scale.
+#include "w4_device.h"
+#include "w4_internal.h"
+
+namespace w4 {
+
+template <int OP>
+struct OpTraits;
+template <>
+struct OpTraits<OP_I8> {
+  using Acc = i32x4;
+  static constexpr int kElemBytes = 1;
+};
+template <>
+struct OpTraits<OP_FP8> {
+  using Acc = f32x4;
+  static constexpr int kElemBytes = 1;
+};
+template <>
+struct OpTraits<OP_F16> {
+  using Acc = f32x4;
+  static constexpr int kElemBytes = 2;
+};
+template <>
+struct OpTraits<OP_BF16> {
+  using Acc = f32x4;
+  static constexpr int kElemBytes = 2;
+};
+
+// 16-byte words of one lane's activation fragment for one 128-deep block.
+template <int OP>
+constexpr int act_vecs() {
+  return OpTraits<OP>::kElemBytes * 2;  // 32 bytes (8-bit) or 64 bytes (16-bit)
+}
+
+// Expand one lane's four packed words into MFMA operand words.
+template <int OP, bool FLIP>
+__device__ __forceinline__ void expand_weights(const u32x4 w, const f16x2 nz, uint32_t e[16]) {
+  const uint32_t q[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if constexpr (OP == OP_I8) {
+      expand_i8x16(FLIP ? (q[j] ^ 0x88888888u) : q[j], e[2 * j], e[2 * j + 1]);
+    } else if constexpr (OP == OP_FP8) {
+      expand_fp8(FLIP ? (q[j] ^ 0x88888888u) : q[j], e[2 * j], e[2 * j + 1]);
+    } else {
+      expand_f16class<OP>(q[j], &e[4 * j]);
+      if constexpr (OP == OP_F16) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) e[4 * j + t] = f16x2_add(e[4 * j + t], nz);
+      }
+    }
+  }
+}
+
+template <int OP>
+__device__ __forceinline__ void block_mma(const uint32_t e[16], const u32x4* a,
+                                          typename OpTraits<OP>::Acc& acc) {
+  if constexpr (OP == OP_I8) {
+    acc = mma_i8(u32x4{e[0], e[1], e[2], e[3]}, a[0], acc);
+    acc = mma_i8(u32x4{e[4], e[5], e[6], e[7]}, a[1], acc);
+  } else if constexpr (OP == OP_FP8) {
+    acc = mma_fp8(u32x8{e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]},
+                  u32x8{a[0].x, a[0].y, a[0].z, a[0].w, a[1].x, a[1].y, a[1].z, a[1].w}, acc);
+  } else {
+#pragma unroll
+    for (int kw = 0; kw < 4; ++kw) {
+      const u32x4 wv{e[4 * kw], e[4 * kw + 1], e[4 * kw + 2], e[4 * kw + 3]};
+      if constexpr (OP == OP_F16)
+        acc = mma_f16(wv, a[kw], acc);
+      else
+        acc = mma_bf16(wv, a[kw], acc);
+    }
+  }
+}
+
+// bf16 W4A16: the operand holds 128 + c, so each group also needs the sum of
+// its activations (times 128 + z).  A weight operand of ones gives that sum in
+// every D row.
+__device__ __forceinline__ void ones_mma(const u32x4* a, f32x4& ones) {
+  const u32x4 one{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+#pragma unroll
+  for (int kw = 0; kw < 4; ++kw) ones = mma_bf16(one, a[kw], ones);
+}
+
+// The group (or whole-K) dot product of one D element.
+template <int OP>
+__device__ __forceinline__ float partial_value(typename OpTraits<OP>::Acc acc, f32x4 ones, float zc,
+                                               int i) {
+  if constexpr (OP == OP_I8) return (float)acc[i] * 0.0625f;  // acc = 16 * sum
+  if constexpr (OP == OP_BF16) return fmaf(-zc, ones[i], acc[i]);
+  return acc[i];
+}
+
+// Integer group partial of the int8 path (acc holds 16 * sum); 0 otherwise.
+template <int OP>
+__device__ __forceinline__ int32_t int_partial(typename OpTraits<OP>::Acc acc, int i) {
+  if constexpr (OP == OP_I8) return acc[i] >> 4;
+  return 0;
+}
+
+__device__ __forceinline__ float zero_point(const GemmArgs& p, int64_t n, int g) {
+  return p.z ? load_as_f32(p.z, p.out_dtype, n * p.G + g) : 8.0f;
+}
+
+__device__ __forceinline__ void store_out(const GemmArgs& p, int64_t m, int64_t n, float v) {
+  if (p.out_dtype == W4_F16)
+    static_cast<uint16_t*>(p.out)[m * p.N + n] = f32_to_f16_bits(v);
+  else
+    static_cast<uint16_t*>(p.out)[m * p.N + n] = f32_to_bf16_bits(v);
+}
+
+// Final epilogue of one element: v is the group-scaled total (grouped) or the
+// raw whole-K dot product (per channel; int32 for the int8 path).
+template <int OP, bool GROUPED>
+__device__ __forceinline__ float finalize(const GemmArgs& p, int64_t m, int64_t n, float fv,
+                                          int32_t iv) {
+  float v;
+  if constexpr (GROUPED) {
+    v = fv;
+  } else {
+    const float s = load_as_f32(p.s, p.s_dtype, n);
+    v = (OP == OP_I8) ? (float)iv * (s * 0.0625f) : fv * s;
+  }
+  if (p.a_scales) v *= p.a_scales[m];
+  if (p.bias) v += load_as_f32(p.bias, p.out_dtype, n);
+  return v;
+}
+
+__device__ __forceinline__ bool in_window(const GemmArgs& p, int64_t m, int64_t n) {
+  return m >= p.m0 && m < p.m1 && n >= p.n0 && n < p.n1;
+}
+
+template <int OP>
+__device__ __forceinline__ void store_partial(const GemmArgs& p, int g, int64_t m, int64_t n, float fv,
+                                              int32_t iv) {
+  const int64_t wm = p.m1 - p.m0, wn = p.n1 - p.n0;
+  const int64_t idx = ((int64_t)g * wm + (m - p.m0)) * wn + (n - p.n0);
+  if constexpr (OP == OP_I8)
+    static_cast<int32_t*>(p.partials)[idx] = iv;
+  else
+    static_cast<float*>(p.partials)[idx] = fv;
+}
+
+// ===========================================================================
+// Small-M kernel.
+// ===========================================================================
+constexpr int kSkinnyMaxWaves = 16;
+
+template <int OP, bool GROUPED, bool FLIP>
+__global__ __launch_bounds__(1024) void w4_gemm_skinny(GemmArgs p) {
+  using Acc = typename OpTraits<OP>::Acc;
+  constexpr int EB = OpTraits<OP>::kElemBytes;
+  constexpr int AV = act_vecs<OP>();
+  constexpr int U = (EB == 1) ? 4 : 2;  // blocks loaded per batch
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int S = blockDim.x >> 6;
+  const int64_t nb = blockIdx.x;
+  const int KB = (int)(p.K >> 7);
+  const int kb0 = (int)((int64_t)KB * wave / S);
+  const int kb1 = (int)((int64_t)KB * (wave + 1) / S);
+  const int r = lane & 15;
+  const int kq = lane >> 4;
+  const bool mvalid = r < p.M;
+  const u32x4* __restrict__ bp = reinterpret_cast<const u32x4*>(p.b) + nb * KB * 64 + lane;
+  const uint8_t* __restrict__ ap =
+      static_cast<const uint8_t*>(p.a) + ((int64_t)r * p.K + kq * 32) * EB;
+  const int64_t n_op = nb * 16 + r;    // weight row this lane feeds to the MFMA
+  const int64_t n_d = nb * 16 + 4 * kq;  // first output row this lane holds
+  const bool partials = p.mode == MODE_PARTIALS;
+
+  Acc acc = {};
+  f32x4 ones = {};
+  f32x4 tot = {};
+
+  for (int kb = kb0; kb < kb1; kb += U) {
+    u32x4 wv[U];
+    u32x4 av[U][AV];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (kb + u < kb1) {
+        wv[u] = __builtin_nontemporal_load(bp + (int64_t)(kb + u) * 64);
+#pragma unroll
+        for (int j = 0; j < AV; ++j)
+          av[u][j] = mvalid ? *reinterpret_cast<const u32x4*>(ap + (int64_t)(kb + u) * 128 * EB + 16 * j)
+                            : u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (kb + u < kb1) {
+        const int g = GROUPED ? kb + u : 0;
+        f16x2 nz = {};
+        if constexpr (OP == OP_F16) {
+          const _Float16 h = (_Float16)(-(1024.0f + zero_point(p, n_op, g)));
+          nz = f16x2{h, h};
+        }
+        uint32_t e[16];
+        expand_weights<OP, FLIP>(wv[u], nz, e);
+        block_mma<OP>(e, av[u], acc);
+        if constexpr (OP == OP_BF16) ones_mma(av[u], ones);
+        if constexpr (GROUPED) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float zc = (OP == OP_BF16) ? 128.0f + zero_point(p, n_d + i, g) : 0.0f;
+            const float pv = partial_value<OP>(acc, ones, zc, i);
+            if (partials) {
+              if (in_window(p, r, n_d + i)) store_partial<OP>(p, g, r, n_d + i, pv, int_partial<OP>(acc, i));
+            } else {
+              tot[i] = fmaf(pv, load_as_f32(p.s, p.s_dtype, (n_d + i) * p.G + g), tot[i]);
+            }
+          }
+          acc = Acc{};
+          ones = f32x4{};
+        }
+      }
+    }
+  }
+
+  // Sum the waves' results in wave order through LDS.
+  __shared__ uint32_t red[kSkinnyMaxWaves][64][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t bits;
+    if constexpr (GROUPED) {
+      bits = __float_as_uint(tot[i]);
+    } else if constexpr (OP == OP_I8) {
+      bits = (uint32_t)acc[i];
+    } else {
+      const float zc = (OP == OP_BF16) ? 128.0f + zero_point(p, n_d + i, 0) : 0.0f;
+      bits = __float_as_uint(partial_value<OP>(acc, ones, zc, i));
+    }
+    red[wave][lane][i] = bits;
+  }
+  __syncthreads();
+  if (GROUPED && partials) return;
+  for (int t = threadIdx.x; t < 256; t += blockDim.x) {
+    const int l = t >> 2, i = t & 3;
+    const int64_t m = l & 15;
+    const int64_t n = nb * 16 + 4 * (l >> 4) + i;
+    if (m >= p.M) continue;
+    float fv = 0.0f;
+    int32_t iv = 0;
+    for (int w = 0; w < S; ++w) {
+      if (!GROUPED && OP == OP_I8)
+        iv += (int32_t)red[w][l][i];
+      else
+        fv += __uint_as_float(red[w][l][i]);
+    }
+    if (partials) {
+      if (in_window(p, m, n)) store_partial<OP>(p, 0, m, n, fv, iv >> 4);
+    } else {
+      store_out(p, m, n, finalize<OP, GROUPED>(p, m, n, fv, iv));
+    }
+  }
+}
+
+// ===========================================================================
+// Tiled kernel.
+// ===========================================================================
+template <int OP, bool GROUPED, bool FLIP, int NT, int MT, bool SPLIT>
+__global__ __launch_bounds__(256) void w4_gemm_tiled(GemmArgs p, int splitk) {
+  using Acc = typename OpTraits<OP>::Acc;
+  constexpr int EB = OpTraits<OP>::kElemBytes;
+  constexpr int AV = act_vecs<OP>();
+  constexpr int BM = MT * 16;
+  constexpr int ROWB = 128 * EB;          // bytes of one activation row per K step
+  constexpr int LDSROW = ROWB + 16;       // +16 B pad: the 16 rows one MFMA reads hit distinct banks
+  constexpr int CH_PER_ROW = ROWB / 16;
+  constexpr int CPT = BM * CH_PER_ROW / 256;  // 16-byte chunks per thread per tile
+  static_assert(BM * CH_PER_ROW % 256 == 0, "tile must split evenly over 256 threads");
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2][BM * LDSROW];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int r = lane & 15;
+  const int kq = lane >> 4;
+  const int64_t m_base = (int64_t)blockIdx.x * BM;
+  const int64_t NB = p.N >> 4;
+  const int64_t nb_base = (int64_t)blockIdx.y * (4 * NT) + wave * NT;
+  const int KB = (int)(p.K >> 7);
+  const int kb0 = (int)((int64_t)KB * blockIdx.z / splitk);
+  const int kb1 = (int)((int64_t)KB * (blockIdx.z + 1) / splitk);
+  const bool partials = p.mode == MODE_PARTIALS;
+  const uint8_t* __restrict__ abase = static_cast<const uint8_t*>(p.a);
+  const u32x4* __restrict__ bbase = reinterpret_cast<const u32x4*>(p.b);
+
+  u32x4 areg[CPT];
+  auto load_a = [&](int kb) {
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+      const int c = tid + 256 * j;
+      const int row = c / CH_PER_ROW, col = c % CH_PER_ROW;
+      const int64_t m = m_base + row;
+      areg[j] = (m < p.M) ? *reinterpret_cast<const u32x4*>(abase + (m * p.K + (int64_t)kb * 128) * EB + col * 16)
+                          : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  auto store_a = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+      const int c = tid + 256 * j;
+      const int row = c / CH_PER_ROW, col = c % CH_PER_ROW;
+      *reinterpret_cast<u32x4*>(&lds[buf][row * LDSROW + col * 16]) = areg[j];
+    }
+  };
+  u32x4 wcur[NT], wnxt[NT];
+  auto load_w = [&](int kb, u32x4* w) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int64_t nb = nb_base + nt;
+      w[nt] = (nb < NB) ? bbase[(nb * KB + kb) * 64 + lane] : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+
+  Acc acc[NT][MT];
+  f32x4 tot[NT][MT];
+  f32x4 ones[MT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      acc[nt][mt] = Acc{};
+      tot[nt][mt] = f32x4{};
+    }
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) ones[mt] = f32x4{};
+
+  if (kb0 < kb1) {
+    load_a(kb0);
+    store_a(0);
+    load_w(kb0, wcur);
+  }
+  __syncthreads();
+  int buf = 0;
+  for (int kb = kb0; kb < kb1; ++kb) {
+    const bool has_next = kb + 1 < kb1;
+    if (has_next) {
+      load_a(kb + 1);
+      load_w(kb + 1, wnxt);
+    }
+    const int g = GROUPED ? kb : 0;
+    uint32_t e[NT][16];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      f16x2 nz = {};
+      if constexpr (OP == OP_F16) {
+        const int64_t n_op = (nb_base + nt) * 16 + r;
+        const _Float16 h = (_Float16)(-(1024.0f + (n_op < p.N ? zero_point(p, n_op, g) : 0.0f)));
+        nz = f16x2{h, h};
+      }
+      expand_weights<OP, FLIP>(wcur[nt], nz, e[nt]);
+    }
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      u32x4 af[AV];
+      const uint8_t* src = &lds[buf][(mt * 16 + r) * LDSROW + kq * 32 * EB];
+#pragma unroll
+      for (int j = 0; j < AV; ++j) af[j] = *reinterpret_cast<const u32x4*>(src + 16 * j);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) block_mma<OP>(e[nt], af, acc[nt][mt]);
+      if constexpr (OP == OP_BF16) ones_mma(af, ones[mt]);
+    }
+    if constexpr (GROUPED) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const int64_t n_d = (nb_base + nt) * 16 + 4 * kq;
+        if (n_d >= p.N) continue;
+        float sc[4], zc[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          sc[i] = partials ? 0.0f : load_as_f32(p.s, p.s_dtype, (n_d + i) * p.G + g);
+          zc[i] = (OP == OP_BF16) ? 128.0f + zero_point(p, n_d + i, g) : 0.0f;
+        }
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float pv = partial_value<OP>(acc[nt][mt], ones[mt], zc[i], i);
+            if (partials) {
+              const int64_t m = m_base + mt * 16 + r;
+              if (m < p.M && in_window(p, m, n_d + i))
+                store_partial<OP>(p, g, m, n_d + i, pv, int_partial<OP>(acc[nt][mt], i));
+            } else {
+              tot[nt][mt][i] = fmaf(pv, sc[i], tot[nt][mt][i]);
+            }
+          }
+          acc[nt][mt] = Acc{};
+        }
+      }
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) ones[mt] = f32x4{};
+    }
+    if (has_next) {
+      store_a(buf ^ 1);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) wcur[nt] = wnxt[nt];
+    }
+    __syncthreads();
+    buf ^= 1;
+  }
+
+  if (GROUPED && partials) return;
+  // Epilogue: lane holds rows n_d..n_d+3 of column m for every (nt, mt).
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int64_t n_d = (nb_base + nt) * 16 + 4 * kq;
+    if (n_d >= p.N) continue;
+    float zc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if constexpr (OP == OP_BF16 && !GROUPED) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) zc[i] = 128.0f + zero_point(p, n_d + i, 0);
+    }
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int64_t m = m_base + mt * 16 + r;
+      if (m >= p.M) continue;
+      uint32_t bits[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if constexpr (GROUPED)
+          bits[i] = __float_as_uint(tot[nt][mt][i]);
+        else if constexpr (OP == OP_I8)
+          bits[i] = (uint32_t)acc[nt][mt][i];
+        else
+          bits[i] = __float_as_uint(partial_value<OP>(acc[nt][mt], ones[mt], zc[i], i));
+      }
+      if constexpr (SPLIT) {
+        uint32_t* slot = static_cast<uint32_t*>(p.ws) + ((int64_t)blockIdx.z * p.M + m) * p.N + n_d;
+        *reinterpret_cast<u32x4*>(slot) = u32x4{bits[0], bits[1], bits[2], bits[3]};
+      } else if (partials) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (in_window(p, m, n_d + i))
+            store_partial<OP>(p, 0, m, n_d + i, __uint_as_float(bits[i]), (int32_t)bits[i] >> 4);
+      } else {
+        uint16_t o[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float v = finalize<OP, GROUPED>(p, m, n_d + i, __uint_as_float(bits[i]), (int32_t)bits[i]);
+          o[i] = p.out_dtype == W4_F16 ? f32_to_f16_bits(v) : f32_to_bf16_bits(v);
+        }
+        uint2 packed = make_uint2((uint32_t)o[0] | ((uint32_t)o[1] << 16), (uint32_t)o[2] | ((uint32_t)o[3] << 16));
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + m * p.N + n_d) = packed;
+      }
+    }
+  }
+}
+
+// Sum the split-K slots of the tiled kernel in split order, then the epilogue.
+template <int OP, bool GROUPED>
+__global__ __launch_bounds__(256) void w4_splitk_reduce(GemmArgs p, int splitk) {
+  const int64_t quads = p.N >> 2;
+  const int64_t total = p.M * quads;
+  const bool partials = p.mode == MODE_PARTIALS;
+  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total;
+       t += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t m = t / quads;
+    const int64_t n = (t - m * quads) * 4;
+    const uint32_t* src = static_cast<const uint32_t*>(p.ws) + m * p.N + n;
+    float fv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    int32_t iv[4] = {0, 0, 0, 0};
+    for (int s = 0; s < splitk; ++s) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(src + (int64_t)s * p.M * p.N);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (!GROUPED && OP == OP_I8)
+          iv[i] += (int32_t)v[i];
+        else
+          fv[i] += __uint_as_float(v[i]);
+      }
+    }
+    if (partials) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (in_window(p, m, n + i)) store_partial<OP>(p, 0, m, n + i, fv[i], iv[i] >> 4);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) store_out(p, m, n + i, finalize<OP, GROUPED>(p, m, n + i, fv[i], iv[i]));
+    }
+  }
+}
+
+// ===========================================================================
+// Host-side launchers.
+// ===========================================================================
+void tiled_tile(int op, bool grouped, int* bm, int* bn) {
+  if (op == OP_I8 || op == OP_FP8) {
+    *bm = grouped ? 64 : 128;
+    *bn = 256;
+  } else {
+    *bm = 64;
+    *bn = 128;
+  }
+}
+
+template <int OP, bool GROUPED, bool FLIP>
+static hipError_t launch_typed(const GemmArgs& args, const GemmPlan& plan, hipStream_t stream) {
+  if (plan.path == PATH_SKINNY) {
+    const unsigned waves = (unsigned)plan.splitk;
+    hipLaunchKernelGGL((w4_gemm_skinny<OP, GROUPED, FLIP>), dim3((unsigned)(args.N / 16)),
+                       dim3(64 * waves), 0, stream, args);
+    return hipGetLastError();
+  }
+  constexpr bool kByte = (OP == OP_I8 || OP == OP_FP8);
+  constexpr int NT = kByte ? 4 : 2;
+  constexpr int MT = kByte ? (GROUPED ? 4 : 8) : 4;
+  const int64_t BM = MT * 16, BN = NT * 64;
+  const dim3 grid((unsigned)((args.M + BM - 1) / BM), (unsigned)((args.N + BN - 1) / BN),
+                  (unsigned)plan.splitk);
+  if (plan.splitk > 1)
+    hipLaunchKernelGGL((w4_gemm_tiled<OP, GROUPED, FLIP, NT, MT, true>), grid, dim3(256), 0, stream, args,
+                       plan.splitk);
+  else
+    hipLaunchKernelGGL((w4_gemm_tiled<OP, GROUPED, FLIP, NT, MT, false>), grid, dim3(256), 0, stream, args,
+                       1);
+  hipError_t e = hipGetLastError();
+  // grouped partials are stored by the tiled kernel itself
+  if (e != hipSuccess || plan.splitk == 1 || (GROUPED && args.mode == MODE_PARTIALS)) return e;
+  const int64_t total = args.M * (args.N / 4);
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL((w4_splitk_reduce<OP, GROUPED>), dim3((unsigned)blocks), dim3(256), 0, stream,
+                     args, plan.splitk);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm(const GemmArgs& args, int op, bool grouped, bool flip, const GemmPlan& plan,
+                       hipStream_t stream) {
+#define W4_DISPATCH(OPV)                                                          \
+  if (grouped)                                                                    \
+    return flip ? launch_typed<OPV, true, true>(args, plan, stream)               \
+                : launch_typed<OPV, true, false>(args, plan, stream);             \
+  return flip ? launch_typed<OPV, false, true>(args, plan, stream)                \
+              : launch_typed<OPV, false, false>(args, plan, stream);
+  switch (op) {
+    case OP_I8: W4_DISPATCH(OP_I8)
+    case OP_FP8: W4_DISPATCH(OP_FP8)
+    case OP_F16:
+      return grouped ? launch_typed<OP_F16, true, false>(args, plan, stream)
+                     : launch_typed<OP_F16, false, false>(args, plan, stream);
+    default:
+      return grouped ? launch_typed<OP_BF16, true, false>(args, plan, stream)
+                     : launch_typed<OP_BF16, false, false>(args, plan, stream);
+  }
+#undef W4_DISPATCH
+}
+
+}  // namespace w4

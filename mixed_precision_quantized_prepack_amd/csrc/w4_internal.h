@@ -1,0 +1,50 @@
+// Internal interface between the C ABI (w4_api.cpp) and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace w4 {
+
+// Matrix-core operand class of a GEMM (the activation type it multiplies).
+enum Op : int { OP_I8 = 0, OP_FP8 = 1, OP_F16 = 2, OP_BF16 = 3 };
+
+enum Path : int { PATH_AUTO = 0, PATH_SKINNY = 1, PATH_TILED = 2 };
+enum Mode : int { MODE_OUTPUT = 0, MODE_PARTIALS = 1 };
+
+// Everything a GEMM kernel reads, in element units unless noted.
+struct GemmArgs {
+  const void* a;           // [M][K] activations: int8 / e4m3 bytes, or fp16 / bf16
+  const float* a_scales;   // [M] per-token scales (W4A8) or nullptr (W4A16)
+  const uint32_t* b;       // PB-v1 words
+  const void* s;           // weight scales: [N] (per channel) or [N][G]
+  const void* z;           // W4A16 zero-points [N][G] or nullptr (z = 8)
+  const void* bias;        // [N] in out dtype, or nullptr
+  void* out;               // [M][N]
+  void* ws;                // split-K slots [splitk][M][N] of 4-byte values
+  void* partials;          // MODE_PARTIALS: [G][m1-m0][n1-n0]
+  int64_t M, N, K;
+  int G;                   // K / group_size
+  int s_dtype;             // W4_F32 / W4_F16 / W4_BF16
+  int out_dtype;           // W4_F16 / W4_BF16
+  int mode;                // Mode
+  int64_t m0, m1, n0, n1;  // partials window
+};
+
+struct GemmPlan {
+  int path;    // PATH_SKINNY or PATH_TILED
+  int splitk;  // skinny: waves per workgroup splitting K; tiled: K splits across workgroups
+  int bm, bn;  // tiled block tile (rows of A, columns of W)
+};
+
+// Block tile of the tiled kernel for an operand class / grouping.
+void tiled_tile(int op, bool grouped, int* bm, int* bn);
+
+hipError_t launch_prepack(const void* w_logical, void* w_packed, int64_t N, int64_t K, int operand,
+                          hipStream_t stream);
+hipError_t launch_quant(const void* x, int x_dtype, void* xq, int q_dtype, float* scales, int64_t M,
+                        int64_t K, hipStream_t stream);
+hipError_t launch_gemm(const GemmArgs& args, int op, bool grouped, bool flip, const GemmPlan& plan,
+                       hipStream_t stream);
+
+}  // namespace w4

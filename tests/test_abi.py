@@ -1,0 +1,156 @@
+"""Host-side tests of the C ABI (CPU only: no kernel is launched).
+
+The library must load, export every function that include/w4.h declares,
+and reject invalid arguments on the host with the documented status before
+enqueueing anything.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mixed_precision_quantized_prepack_amd as w4
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "w4.h")
+
+W4_OK, E_NULL, E_SHAPE, E_DTYPE, E_ALIGN, E_GROUP, E_WS, E_UNSUP = 0, 1, 2, 3, 4, 5, 6, 7
+FAKE = ctypes.c_void_p(0x10000)      # aligned, never dereferenced by validation
+MISALIGNED = ctypes.c_void_p(0x10008)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(w4.LIB_PATH):
+        pytest.skip("libw4.so not built")
+    return w4.lib()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    return re.findall(r"^W4_API\s+[\w\s\*]+?\b(w4\w*)\s*\(", text, flags=re.M)
+
+
+def test_header_declares_the_documented_entry_points():
+    names = header_functions()
+    for n in ("w4_prepack_B", "w4_quant_act_per_token", "w4a8_gemm", "w4a16_gemm"):
+        assert n in names
+    assert sorted(names) == sorted(w4.EXPORTED_SYMBOLS)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in header_functions():
+        assert hasattr(lib, name), name
+
+
+def test_only_the_abi_is_exported(lib):
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", w4.LIB_PATH], capture_output=True, text=True).stdout
+    text_syms = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    assert text_syms == set(header_functions())
+
+
+def test_versions_and_status_strings(lib):
+    assert lib.w4_abi_version() == 1
+    assert lib.w4_layout_version() == 1
+    for s in range(9):
+        assert lib.w4_status_string(s).decode().startswith("W4_")
+    assert lib.w4_prepack_B_bytes(256, 512) == 256 * 512 // 2
+
+
+def test_prepack_validation(lib):
+    assert lib.w4_prepack_B(None, FAKE, 16, 128, 0, None) == E_NULL
+    assert lib.w4_prepack_B(FAKE, ctypes.c_void_p(0x90000), 24, 128, 0, None) == E_SHAPE
+    assert lib.w4_prepack_B(FAKE, ctypes.c_void_p(0x90000), 16, 100, 0, None) == E_SHAPE
+    assert lib.w4_prepack_B(FAKE, ctypes.c_void_p(0x90000), 16, 128, 7, None) == E_DTYPE
+    assert lib.w4_prepack_B(MISALIGNED, ctypes.c_void_p(0x90000), 16, 128, 0, None) == E_ALIGN
+    # overlapping input and output
+    assert lib.w4_prepack_B(FAKE, ctypes.c_void_p(0x10010), 16, 128, 0, None) == E_SHAPE
+    assert "overlap" in lib.w4_last_error().decode()
+
+
+def test_quant_validation(lib):
+    q = lib.w4_quant_act_per_token
+    assert q(FAKE, 7, FAKE, 3, FAKE, 4, 64, None) == E_DTYPE
+    assert q(FAKE, 0, FAKE, 5, FAKE, 4, 64, None) == E_DTYPE
+    assert q(FAKE, 0, FAKE, 3, FAKE, 4, 60, None) == E_SHAPE
+    assert q(FAKE, 0, FAKE, 3, FAKE, -1, 64, None) == E_SHAPE
+    assert q(None, 0, FAKE, 3, FAKE, 4, 64, None) == E_NULL
+    assert q(MISALIGNED, 0, FAKE, 3, FAKE, 4, 64, None) == E_ALIGN
+    assert q(None, 0, None, 3, None, 0, 64, None) == W4_OK        # M = 0: nothing to do
+
+
+def _w4a8(lib, aq=FAKE, a_dtype=3, a_scales=FAKE, b=FAKE, wtype=0, bs=FAKE, s_dtype=2, gs=128,
+          bias=None, out=FAKE, out_dtype=0, M=4, N=32, K=256, ws=None, wsb=0):
+    return lib.w4a8_gemm(aq, a_dtype, a_scales, b, wtype, bs, s_dtype, gs, bias, out, out_dtype,
+                         M, N, K, ws, wsb, None)
+
+
+def test_w4a8_validation(lib):
+    assert _w4a8(lib, a_dtype=0) == E_DTYPE
+    assert _w4a8(lib, wtype=1) == E_DTYPE              # unsigned without zero-points
+    assert _w4a8(lib, s_dtype=3) == E_DTYPE
+    assert _w4a8(lib, out_dtype=2) == E_DTYPE
+    assert _w4a8(lib, N=40) == E_SHAPE
+    assert _w4a8(lib, K=200) == E_SHAPE
+    assert _w4a8(lib, M=-2) == E_SHAPE
+    assert _w4a8(lib, gs=64) == E_GROUP
+    assert _w4a8(lib, K=384, gs=256) == E_GROUP
+    assert _w4a8(lib, aq=None) == E_NULL
+    assert _w4a8(lib, b=None) == E_NULL
+    assert _w4a8(lib, out=None) == E_NULL
+    assert _w4a8(lib, a_scales=None) == E_NULL
+    assert _w4a8(lib, aq=MISALIGNED) == E_ALIGN
+    assert _w4a8(lib, out=MISALIGNED) == E_ALIGN
+    assert _w4a8(lib, K=131072 + 128, gs=-1) == E_SHAPE  # int32 range of per-channel int8
+    assert _w4a8(lib, M=0) == W4_OK
+
+
+def test_w4a16_validation(lib):
+    def call(a=FAKE, a_dtype=1, b=FAKE, wtype=1, s=FAKE, z=FAKE, gs=128, out=FAKE, M=2, N=32, K=256):
+        return lib.w4a16_gemm(a, a_dtype, b, wtype, s, z, gs, None, out, M, N, K, None, 0, None)
+    assert call(a_dtype=3) == E_DTYPE
+    assert call(wtype=0) == E_DTYPE
+    assert call(wtype=2) == E_DTYPE                      # uint4b8 takes no zero-points
+    assert call(s=None) == E_NULL
+    assert call(gs=32) == E_GROUP
+    assert call(N=8) == E_SHAPE
+    assert call(z=ctypes.c_void_p(0x10001)) == E_ALIGN
+    assert call(M=0) == W4_OK
+
+
+def test_partials_window_validation(lib):
+    f = lib.w4a8_gemm_partials
+    assert f(FAKE, 3, FAKE, 0, 128, 4, 32, 256, 0, 5, 0, 32, FAKE, None, 0, None) == E_SHAPE
+    assert f(FAKE, 3, FAKE, 0, 128, 4, 32, 256, 2, 1, 0, 32, FAKE, None, 0, None) == E_SHAPE
+    assert f(FAKE, 3, FAKE, 0, 128, 4, 32, 256, 0, 4, 0, 32, None, None, 0, None) == E_NULL
+
+
+def test_options_and_plans(lib):
+    try:
+        assert lib.w4_set_option(b"nonsense", 1) == E_UNSUP
+        assert lib.w4_set_option(b"force_path", 5) == E_SHAPE
+        assert w4.gemm_plan(1, 8192, 21760, -1, w4.I8)[0] == 1     # small M -> skinny
+        assert w4.gemm_plan(4096, 8192, 21760, -1, w4.I8)[0] == 2  # large M -> tiled
+        w4.set_option("force_path", 1)
+        with pytest.raises(w4.W4Error):
+            w4.gemm_plan(64, 8192, 21760, -1, w4.I8)               # skinny handles M <= 16
+        w4.set_option("force_path", 2)
+        assert w4.gemm_plan(1, 8192, 21760, -1, w4.I8)[0] == 2
+        w4.set_option("splitk", 4)
+        assert w4.gemm_plan(1, 8192, 21760, -1, w4.I8) == (2, 4)
+        assert w4.gemm_workspace_bytes(1, 8192, 21760, -1, w4.I8) == 4 * 1 * 8192 * 4
+        # a split-K tiled plan needs its workspace
+        assert _w4a8(lib, M=1, N=8192, K=21760, gs=-1, s_dtype=2) == E_WS
+    finally:
+        w4.set_option("force_path", 0)
+        w4.set_option("splitk", 0)
+    assert w4.get_option("force_path") == 0
+
+
+def test_binding_refuses_cpu_tensors(lib):
+    import torch
+    x = torch.zeros((4, 64), dtype=torch.float16)
+    with pytest.raises(ValueError):
+        w4.quant_act_per_token(x)

@@ -1,0 +1,82 @@
+"""GPU parity: weight prepack and per-token quantisation, bit-exact against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import mixed_precision_quantized_prepack_amd as w4
+import workloads
+from oracle import w4_oracle as O
+from tests.parity import DEV, bits16
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("operand", ["i8", "f16"])
+@pytest.mark.parametrize("N,K", [(16, 128), (48, 384), (272, 640), (1024, 4096)])
+def test_prepack_bit_exact(operand, N, K):
+    w = workloads.store_nibbles(workloads.int4_codes(N, K, "uint4", seed=N + K))
+    got = w4.prepack_B(w.to(DEV), operand).cpu().numpy()
+    assert np.array_equal(got, O.prepack_B(w.numpy(), N, K, operand))
+
+
+@pytest.mark.parametrize("N,K,operand", [(4096, 4096, "f16"), (8192, 21760, "i8"),
+                                         (28672, 8192, "i8"), (22016, 4096, "i8")])
+def test_prepack_bit_exact_full_size(N, K, operand):
+    w = workloads.store_nibbles(workloads.int4_codes(N, K, "uint4", seed=7))
+    got = w4.prepack_B(w.to(DEV), operand).cpu().numpy()
+    assert np.array_equal(got, O.prepack_B(w.numpy(), N, K, operand))
+
+
+@pytest.mark.parametrize("x_dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("q_dtype", ["i8", "fp8"])
+@pytest.mark.parametrize("M,K,dist", [(1, 128, "normal"), (3, 4096, "normal"), (16, 512, "wide"),
+                                      (5, 8, "normal"), (7, 40000, "normal"), (33, 21760, "wide"),
+                                      (64, 8192, "normal")])
+def test_quant_bit_exact(x_dtype, q_dtype, M, K, dist):
+    x = workloads.activations(M, K, x_dtype, seed=M * 31 + K, dist=dist)
+    if M >= 3:
+        x[1] = 0                     # a zero row
+        x[2, :K // 2] = 0
+    q, s = w4.quant_act_per_token(x.to(DEV), q_dtype)
+    qo, so = O.quant_act_per_token(bits16(x), x_dtype, q_dtype)
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), so.view(np.uint32))
+    qg = q.cpu().numpy()
+    if q_dtype == "i8":
+        assert np.array_equal(qg, qo)
+    else:
+        assert np.array_equal(qg.view(np.uint8), qo.view(np.uint8))
+
+
+@pytest.mark.parametrize("M,K,x_dtype,q_dtype", [(4096, 21760, "f16", "i8"), (8192, 8192, "bf16", "fp8"),
+                                                 (1024, 11008, "f16", "i8")])
+def test_quant_bit_exact_full_size(M, K, x_dtype, q_dtype):
+    x = workloads.activations(M, K, x_dtype, seed=99)
+    q, s = w4.quant_act_per_token(x.to(DEV), q_dtype)
+    qo, so = O.quant_act_per_token(bits16(x), x_dtype, q_dtype)
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), so.view(np.uint32))
+    assert np.array_equal(q.cpu().numpy().view(np.uint8), qo.view(np.uint8))
+
+
+def test_quant_empty_rows_is_a_no_op():
+    x = torch.zeros((0, 256), dtype=torch.float16, device=DEV)
+    q, s = w4.quant_act_per_token(x)
+    assert q.shape == (0, 256) and s.shape == (0,)
+
+
+def test_quant_exhaustive_fp16_codes():
+    """Every finite fp16 bit pattern goes through the quantiser once, in rows
+    whose absolute maxima span the whole range."""
+    b = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    fin = np.isfinite(b.view(np.float16))
+    vals = b[fin]
+    K = 512
+    pad = (-vals.size) % K
+    vals = np.concatenate([vals, np.zeros(pad, np.uint16)]).reshape(-1, K)
+    rng = np.random.default_rng(5)
+    vals = vals[rng.permutation(vals.shape[0])]
+    x = torch.from_numpy(vals.view(np.int16)).view(torch.float16)
+    for q_dtype in ("i8", "fp8"):
+        q, s = w4.quant_act_per_token(x.to(DEV), q_dtype)
+        qo, so = O.quant_act_per_token(vals, "f16", q_dtype)
+        assert np.array_equal(s.cpu().numpy().view(np.uint32), so.view(np.uint32))
+        assert np.array_equal(q.cpu().numpy().view(np.uint8), qo.view(np.uint8))

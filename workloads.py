@@ -203,3 +203,13 @@ def make_case(wl: Workload, M: int, with_bias: bool = False, seed_base: Optional
     zp = zero_points((N, K // gs), wl.a_dtype, sd(3)) if wl.has_zeros else None
     b = bias(N, wl.out_dtype, sd(4)) if with_bias else None
     return Case(wl, M, a, wv, wlog, ws, zp, b)
+
+
+def weight_copy(w_logical: torch.Tensor, i: int) -> torch.Tensor:
+    """A distinct weight with the same distribution: every stored byte XOR-ed
+    with a per-copy constant (a bijection on each 4-bit code).  Used to rotate
+    several resident weight copies through a benchmark so that no launch finds
+    its weight in a cache.  Works on CPU or device tensors."""
+    if i == 0:
+        return w_logical
+    return w_logical ^ ((i * 0x37 + 0x5A) & 0xFF)
