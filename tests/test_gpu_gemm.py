@@ -87,8 +87,9 @@ def test_fp8_partials_within_bound(path, M, split):
     A = np.abs(O.activation_integers(codes, "fp8")).astype(np.float64) * 2.0 ** -9
     W = np.abs(O.weight_values(dc.case.w_logical.numpy(), dc.K, "int4")).astype(np.float64)
     bound = np.stack([A[:, g * 128:(g + 1) * 128] @ W[:, g * 128:(g + 1) * 128].T for g in range(dc.G)])
+    # the MFMA sums 128 exact products in fp32 in an order of its own: the
+    # result may round, within gamma_128 * sum|a w|
     assert np.all(np.abs(part - exact) <= 128 * 2.0 ** -24 * bound)
-    assert np.mean(part == exact) > 0.99
 
 
 @pytest.mark.parametrize("a_dtype", ["bf16", "f16"])
