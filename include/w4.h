@@ -238,6 +238,8 @@ W4_API int w4a16_gemm_partials(const void* a, int a_dtype, const void* b_packed,
  *   "force_path" : 0 = automatic, 1 = small-M kernel, 2 = tiled kernel
  *   "splitk"     : 0 = automatic, else the number of K splits (tiled kernel)
  *                  or waves splitting K (small-M kernel)
+ *   "skinny_strips": 0 = automatic, 1 or 2 16-column strips per wave of the
+ *                  small-M kernel (2 needs N % 32 == 0)
  * Returns W4_OK, or W4_E_UNSUPPORTED for an unknown key / W4_E_SHAPE for an
  * out-of-range value.
  * ------------------------------------------------------------------------- */

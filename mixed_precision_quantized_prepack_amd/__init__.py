@@ -77,14 +77,16 @@ class W4Error(RuntimeError):
         self.detail = detail
 
 
-def lib() -> ctypes.CDLL:
-    """Load libw4.so (once).  Raises if it has not been built."""
+def lib(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load libw4.so (once).  Raises if it has not been built.  ``path``
+    binds another build of the same ABI instead (tuning experiments)."""
     global _LIB
-    if _LIB is None:
-        if not os.path.exists(LIB_PATH):
-            raise ImportError(f"{LIB_PATH} is missing: build it with "
+    if _LIB is None or path is not None:
+        path = path or LIB_PATH
+        if not os.path.exists(path):
+            raise ImportError(f"{path} is missing: build it with "
                               "`python -m mixed_precision_quantized_prepack_amd.build`")
-        h = ctypes.CDLL(LIB_PATH)
+        h = ctypes.CDLL(path)
         for name, res, args in _SIGNATURES:
             f = getattr(h, name)
             f.restype = res

@@ -34,9 +34,9 @@ COMMON_FLAGS = [
 SOURCES = ["w4_api.cpp", "w4_prepack_quant.hip", "w4_gemm.hip"]
 
 
-def _compile(src: str, verbose: bool) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *COMMON_FLAGS]
+def _compile(src: str, verbose: bool, build_dir: str, extra) -> str:
+    obj = os.path.join(build_dir, os.path.basename(src) + ".o")
+    cmd = [HIPCC, *COMMON_FLAGS, *extra]
     if src.endswith(".cpp"):
         cmd += ["-x", "hip"]
     cmd += ["-c", os.path.join(CSRC, src), "-o", obj]
@@ -52,19 +52,23 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(jobs: int = 4, verbose: bool = False) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
+def build(jobs: int = 4, verbose: bool = False, extra_flags=(), out_path: str = LIB_PATH) -> str:
+    """Compile and link.  ``extra_flags`` (e.g. tuning -D defines) and
+    ``out_path`` allow side builds for experiments; the defaults build the
+    library the package loads."""
+    build_dir = BUILD_DIR if out_path == LIB_PATH else out_path + ".objs"
+    os.makedirs(build_dir, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB_PATH + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, verbose, build_dir, list(extra_flags)), SOURCES))
+    tmp = out_path + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"linking libw4.so failed:\n{r.stdout}{r.stderr}")
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, out_path)
+    return out_path
 
 
 def main(argv=None) -> int:

@@ -20,6 +20,7 @@ thread_local std::string g_last_error;
 
 std::atomic<int64_t> g_force_path{0};
 std::atomic<int64_t> g_splitk{0};
+std::atomic<int64_t> g_skinny_strips{0};
 
 int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 int fail(int status, const char* fmt, ...) {
@@ -106,18 +107,25 @@ int make_plan(int64_t M, int64_t N, int64_t K, bool grouped, int op, GemmPlan* p
   tiled_tile(op, grouped, &plan->bm, &plan->bn);
   if (plan->path == PATH_SKINNY) {
     if (M > 16) return fail(W4_E_UNSUPPORTED, "the small-M kernel handles M <= 16 (M=%lld)", (long long)M);
+    // strips of 16 columns per wave: two strips share one activation fragment
+    const int64_t fns = g_skinny_strips.load();
+    const int64_t ns = fns ? fns : ((!grouped && N % 32 == 0 && M > 1) ? 2 : 1);
+    if (N % (16 * ns))
+      return fail(W4_E_SHAPE, "small-M kernel with %lld strips per wave needs N %% %lld == 0", (long long)ns,
+                  (long long)(16 * ns));
+    plan->bn = (int)(16 * ns);
     int64_t s;
     if (fs) {
       s = fs;
     } else {
-      const int64_t strips = N / 16;
-      const int64_t want = (16LL * cu + strips - 1) / strips;
+      const int64_t groups = N / (16 * ns);
+      const int64_t want = (16LL * cu + groups - 1) / groups;
       s = 1;
-      while (s < want && s < 16) s *= 2;
+      while (s < want && s < 8) s *= 2;
       while (s > 1 && KB / s < 2) s /= 2;
     }
-    if (s < 1 || s > 16 || s > KB)
-      return fail(W4_E_SHAPE, "small-M kernel: %lld K-splitting waves not in [1, min(16, K/128)]", (long long)s);
+    if (s < 1 || s > 8 || s > KB)
+      return fail(W4_E_SHAPE, "small-M kernel: %lld K-splitting waves not in [1, min(8, K/128)]", (long long)s);
     plan->splitk = (int)s;
   } else {
     int64_t s;
@@ -400,6 +408,11 @@ int w4_set_option(const char* key, int64_t value) {
     g_splitk.store(value);
     return ok();
   }
+  if (!strcmp(key, "skinny_strips")) {
+    if (value < 0 || value > 2) return fail(W4_E_SHAPE, "skinny_strips must be 0, 1 or 2");
+    g_skinny_strips.store(value);
+    return ok();
+  }
   return fail(W4_E_UNSUPPORTED, "unknown option '%s'", key);
 }
 
@@ -407,6 +420,7 @@ int64_t w4_get_option(const char* key) {
   if (!key) return -1;
   if (!strcmp(key, "force_path")) return g_force_path.load();
   if (!strcmp(key, "splitk")) return g_splitk.load();
+  if (!strcmp(key, "skinny_strips")) return g_skinny_strips.load();
   return -1;
 }
 

@@ -169,112 +169,216 @@ __device__ __forceinline__ void store_partial(const GemmArgs& p, int g, int64_t 
     static_cast<float*>(p.partials)[idx] = fv;
 }
 
+// Buffer loads: a descriptor bounds every load, and an out-of-range offset
+// returns zero without touching memory.
+constexpr uint32_t kBufferDword3 = 0x00020000u;  // raw buffer, 32-bit data format (gfx9)
+constexpr uint32_t kOutOfRange = 0x80000000u;    // offset beyond every descriptor's size
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int64_t n = bytes < 0 ? 0 : (bytes > 0x7FFFFFF0LL ? 0x7FFFFFF0LL : bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n, kBufferDword3);
+}
+__device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+}
+
 // ===========================================================================
 // Small-M kernel.
 // ===========================================================================
-constexpr int kSkinnyMaxWaves = 16;
+constexpr int kSkinnyMaxWaves = 8;
 
-template <int OP, bool GROUPED, bool FLIP>
-__global__ __launch_bounds__(1024) void w4_gemm_skinny(GemmArgs p) {
+// Blocks per batch of the small-M kernel (8-bit / 16-bit operands) and the
+// cache-policy bits of its weight loads (2 = non-temporal: the weight stream
+// is read once).
+#ifndef W4_SKINNY_U8
+#define W4_SKINNY_U8 4
+#endif
+#ifndef W4_SKINNY_U16
+#define W4_SKINNY_U16 2
+#endif
+#ifndef W4_SKINNY_UG
+#define W4_SKINNY_UG 2   // grouped problems also prefetch per-block scales
+#endif
+#ifndef W4_SKINNY_WPOLICY
+#define W4_SKINNY_WPOLICY 2
+#endif
+
+// Raw 32-bit word of element i of a scale / zero-point array (fp32, or a
+// 16-bit float in the low half); out-of-range offsets read as zero.
+__device__ __forceinline__ uint32_t load_raw(__amdgpu_buffer_rsrc_t r, int dtype, uint32_t i, bool in) {
+  if (dtype == W4_F32) return __builtin_amdgcn_raw_buffer_load_b32(r, (int)(in ? i * 4u : kOutOfRange), 0, 0);
+  return __builtin_amdgcn_raw_buffer_load_b16(r, (int)(in ? i * 2u : kOutOfRange), 0, 0);
+}
+__device__ __forceinline__ float raw_to_f32(uint32_t b, int dtype) {
+  return dtype == W4_F32 ? __uint_as_float(b) : dtype == W4_F16 ? f16_bits_to_f32(b) : bf16_bits_to_f32(b);
+}
+
+// Small-M kernel (M <= 16).
+//
+// Workgroup = S waves over the same NS 16-column strips of W; the K blocks are
+// dealt to the waves round-robin (wave w takes blocks w, w+S, ...), so at any
+// time a workgroup reads S contiguous KiB of each strip.  A wave multiplies
+// each activation fragment with its NS weight blocks (NS strips share the
+// fragment, which divides the activation traffic by NS).  Batches of U
+// K-blocks are double buffered: the loads of batch i+1 (weights, activations
+// and, for groups, the group scales / zero-points) are issued before the
+// MFMAs of batch i.  Rows past M and blocks past K are buffer loads with
+// out-of-range offsets: they read as zero without memory traffic.  The
+// waves' results are summed through LDS in wave order.
+template <int OP, bool GROUPED, bool FLIP, int NS>
+__global__ __launch_bounds__(64 * kSkinnyMaxWaves) void w4_gemm_skinny(GemmArgs p) {
   using Acc = typename OpTraits<OP>::Acc;
   constexpr int EB = OpTraits<OP>::kElemBytes;
   constexpr int AV = act_vecs<OP>();
-  constexpr int U = (EB == 1) ? 4 : 2;  // blocks loaded per batch
+  constexpr int U = GROUPED ? W4_SKINNY_UG : (EB == 1) ? W4_SKINNY_U8 : W4_SKINNY_U16;  // K blocks per batch
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int S = blockDim.x >> 6;
-  const int64_t nb = blockIdx.x;
+  const int64_t nb0 = (int64_t)blockIdx.x * NS;   // first strip of the workgroup
   const int KB = (int)(p.K >> 7);
-  const int kb0 = (int)((int64_t)KB * wave / S);
-  const int kb1 = (int)((int64_t)KB * (wave + 1) / S);
   const int r = lane & 15;
   const int kq = lane >> 4;
-  const bool mvalid = r < p.M;
-  const u32x4* __restrict__ bp = reinterpret_cast<const u32x4*>(p.b) + nb * KB * 64 + lane;
-  const uint8_t* __restrict__ ap =
-      static_cast<const uint8_t*>(p.a) + ((int64_t)r * p.K + kq * 32) * EB;
-  const int64_t n_op = nb * 16 + r;    // weight row this lane feeds to the MFMA
-  const int64_t n_d = nb * 16 + 4 * kq;  // first output row this lane holds
   const bool partials = p.mode == MODE_PARTIALS;
+  const int zdt = p.out_dtype;                    // W4A16: zero-points in the activation dtype
 
-  Acc acc = {};
+  const __amdgpu_buffer_rsrc_t rw =
+      make_rsrc(reinterpret_cast<const uint8_t*>(p.b) + nb0 * KB * 1024, (int64_t)NS * KB * 1024);
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a, p.M * p.K * EB);
+  const int sbytes = p.s_dtype == W4_F32 ? 4 : 2;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.s, p.N * p.G * sbytes);
+  const __amdgpu_buffer_rsrc_t rz = make_rsrc(p.z, p.z ? p.N * p.G * 2 : 0);
+  const uint32_t w_lane = (uint32_t)lane * 16;
+  const uint32_t a_lane = (uint32_t)((r * p.K + kq * 32) * EB);
+
+  Acc acc[NS];
   f32x4 ones = {};
-  f32x4 tot = {};
+  f32x4 tot[NS];
+#pragma unroll
+  for (int j = 0; j < NS; ++j) {
+    acc[j] = Acc{};
+    tot[j] = f32x4{};
+  }
+  u32x4 wv[2][U][NS];
+  u32x4 av[2][U][AV];
+  uint32_t sc[2][U][NS][4];   // group scales (grouped) for rows n_d + i
+  uint32_t zd[2][U][NS][4];   // zero-points for rows n_d + i (bf16 W4A16)
+  uint32_t zo[2][U][NS];      // zero-point for row n_op (fp16 W4A16)
 
-  for (int kb = kb0; kb < kb1; kb += U) {
-    u32x4 wv[U];
-    u32x4 av[U][AV];
+  auto load_batch = [&](int buf, int kb) {   // kb: this wave's batch index in blocks of S
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      if (kb + u < kb1) {
-        wv[u] = __builtin_nontemporal_load(bp + (int64_t)(kb + u) * 64);
+      const int k = wave + (kb + u) * S;     // K block
+      const bool in = k < KB;
 #pragma unroll
-        for (int j = 0; j < AV; ++j)
-          av[u][j] = mvalid ? *reinterpret_cast<const u32x4*>(ap + (int64_t)(kb + u) * 128 * EB + 16 * j)
-                            : u32x4{0u, 0u, 0u, 0u};
+      for (int j = 0; j < NS; ++j)
+        wv[buf][u][j] = __builtin_amdgcn_raw_buffer_load_b128(
+            rw, (int)(in ? (uint32_t)((j * KB + k) * 1024) + w_lane : kOutOfRange), 0, W4_SKINNY_WPOLICY);
+#pragma unroll
+      for (int a = 0; a < AV; ++a)
+        av[buf][u][a] = buffer_load16(ra, in ? a_lane + (uint32_t)(k * 128 * EB + 16 * a) : kOutOfRange);
+      const int g = GROUPED ? k : 0;
+#pragma unroll
+      for (int j = 0; j < NS; ++j) {
+        const uint32_t nd = (uint32_t)((nb0 + j) * 16 + 4 * kq);
+        if constexpr (GROUPED) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sc[buf][u][j][i] = load_raw(rs, p.s_dtype, (nd + i) * p.G + g, in && !partials);
+        }
+        if constexpr (OP == OP_BF16) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) zd[buf][u][j][i] = load_raw(rz, zdt, (nd + i) * p.G + g, in && p.z);
+        }
+        if constexpr (OP == OP_F16)
+          zo[buf][u][j] = load_raw(rz, zdt, (uint32_t)((nb0 + j) * 16 + r) * p.G + g, in && p.z);
       }
     }
+  };
+  auto compute_batch = [&](int buf, int kb) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      if (kb + u < kb1) {
-        const int g = GROUPED ? kb + u : 0;
+      const int k = wave + (kb + u) * S;
+      const int g = GROUPED ? k : 0;
+      if constexpr (OP == OP_BF16) ones_mma(av[buf][u], ones);
+#pragma unroll
+      for (int j = 0; j < NS; ++j) {
         f16x2 nz = {};
         if constexpr (OP == OP_F16) {
-          const _Float16 h = (_Float16)(-(1024.0f + zero_point(p, n_op, g)));
+          const float z = p.z ? raw_to_f32(zo[buf][u][j], zdt) : 8.0f;
+          const _Float16 h = (_Float16)(-(1024.0f + z));
           nz = f16x2{h, h};
         }
         uint32_t e[16];
-        expand_weights<OP, FLIP>(wv[u], nz, e);
-        block_mma<OP>(e, av[u], acc);
-        if constexpr (OP == OP_BF16) ones_mma(av[u], ones);
-        if constexpr (GROUPED) {
+        expand_weights<OP, FLIP>(wv[buf][u][j], nz, e);
+        block_mma<OP>(e, av[buf][u], acc[j]);
+      }
+      if constexpr (GROUPED) {
+        if (k < KB) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float zc = (OP == OP_BF16) ? 128.0f + zero_point(p, n_d + i, g) : 0.0f;
-            const float pv = partial_value<OP>(acc, ones, zc, i);
-            if (partials) {
-              if (in_window(p, r, n_d + i)) store_partial<OP>(p, g, r, n_d + i, pv, int_partial<OP>(acc, i));
-            } else {
-              tot[i] = fmaf(pv, load_as_f32(p.s, p.s_dtype, (n_d + i) * p.G + g), tot[i]);
+          for (int j = 0; j < NS; ++j) {
+            const int64_t n_d = (nb0 + j) * 16 + 4 * kq;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float zc = (OP == OP_BF16) ? 128.0f + (p.z ? raw_to_f32(zd[buf][u][j][i], zdt) : 8.0f) : 0.0f;
+              const float pv = partial_value<OP>(acc[j], ones, zc, i);
+              if (partials) {
+                if (in_window(p, r, n_d + i)) store_partial<OP>(p, g, r, n_d + i, pv, int_partial<OP>(acc[j], i));
+              } else {
+                tot[j][i] = fmaf(pv, raw_to_f32(sc[buf][u][j][i], p.s_dtype), tot[j][i]);
+              }
             }
           }
-          acc = Acc{};
-          ones = f32x4{};
         }
+#pragma unroll
+        for (int j = 0; j < NS; ++j) acc[j] = Acc{};
+        ones = f32x4{};
       }
     }
+  };
+
+  const int nbatch = (KB - wave + S - 1) / S;   // K blocks of this wave
+  load_batch(0, 0);
+  for (int kb = 0; kb < nbatch; kb += 2 * U) {
+    load_batch(1, kb + U);
+    compute_batch(0, kb);
+    if (kb + U >= nbatch) break;
+    load_batch(0, kb + 2 * U);
+    compute_batch(1, kb + U);
   }
 
   // Sum the waves' results in wave order through LDS.
-  __shared__ uint32_t red[kSkinnyMaxWaves][64][4];
+  __shared__ uint32_t red[kSkinnyMaxWaves][NS][64][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    uint32_t bits;
-    if constexpr (GROUPED) {
-      bits = __float_as_uint(tot[i]);
-    } else if constexpr (OP == OP_I8) {
-      bits = (uint32_t)acc[i];
-    } else {
-      const float zc = (OP == OP_BF16) ? 128.0f + zero_point(p, n_d + i, 0) : 0.0f;
-      bits = __float_as_uint(partial_value<OP>(acc, ones, zc, i));
+  for (int j = 0; j < NS; ++j) {
+    const int64_t n_d = (nb0 + j) * 16 + 4 * kq;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t bits;
+      if constexpr (GROUPED) {
+        bits = __float_as_uint(tot[j][i]);
+      } else if constexpr (OP == OP_I8) {
+        bits = (uint32_t)acc[j][i];
+      } else {
+        const float zc = (OP == OP_BF16) ? 128.0f + zero_point(p, n_d + i, 0) : 0.0f;
+        bits = __float_as_uint(partial_value<OP>(acc[j], ones, zc, i));
+      }
+      red[wave][j][lane][i] = bits;
     }
-    red[wave][lane][i] = bits;
   }
   __syncthreads();
   if (GROUPED && partials) return;
-  for (int t = threadIdx.x; t < 256; t += blockDim.x) {
-    const int l = t >> 2, i = t & 3;
+  for (int t = threadIdx.x; t < 256 * NS; t += blockDim.x) {
+    const int j = t >> 8, l = (t >> 2) & 63, i = t & 3;
     const int64_t m = l & 15;
-    const int64_t n = nb * 16 + 4 * (l >> 4) + i;
-    if (m >= p.M) continue;
+    const int64_t n = (nb0 + j) * 16 + 4 * (l >> 4) + i;
+    if (m >= p.M || n >= p.N) continue;
     float fv = 0.0f;
     int32_t iv = 0;
     for (int w = 0; w < S; ++w) {
       if (!GROUPED && OP == OP_I8)
-        iv += (int32_t)red[w][l][i];
+        iv += (int32_t)red[w][j][l][i];
       else
-        fv += __uint_as_float(red[w][l][i]);
+        fv += __uint_as_float(red[w][j][l][i]);
     }
     if (partials) {
       if (in_window(p, m, n)) store_partial<OP>(p, 0, m, n, fv, iv >> 4);
@@ -286,6 +390,20 @@ __global__ __launch_bounds__(1024) void w4_gemm_skinny(GemmArgs p) {
 
 // ===========================================================================
 // Tiled kernel.
+//
+// Workgroup = 4 waves; tile BM (rows of A) x BN = 4*NT*16 (columns of W);
+// K steps of 128 (one PB-v1 block, one group).  Per step each wave expands
+// its NT weight blocks once and multiplies them with the MT activation
+// fragments of the step, read from LDS one m-tile ahead of use.
+//
+// Software pipeline (2 phases, ping-pong):
+//   phase p computes step kb from LDS buffer p with weight registers wp, while
+//   the global loads of step kb+1 (activation tile -> registers, weights ->
+//   w(1-p)) are in flight; then the activation tile goes to LDS buffer 1-p and
+//   one barrier separates the phases.  All global loads are buffer loads:
+//   rows past M and blocks past N read as zero, and loads past the K range use
+//   an out-of-range offset, so the loop has no divergent branches and the
+//   compiler can count the outstanding loads exactly.
 // ===========================================================================
 template <int OP, bool GROUPED, bool FLIP, int NT, int MT, bool SPLIT>
 __global__ __launch_bounds__(256) void w4_gemm_tiled(GemmArgs p, int splitk) {
@@ -302,7 +420,7 @@ __global__ __launch_bounds__(256) void w4_gemm_tiled(GemmArgs p, int splitk) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave: scalar registers
   const int r = lane & 15;
   const int kq = lane >> 4;
   const int64_t m_base = (int64_t)blockIdx.x * BM;
@@ -312,34 +430,38 @@ __global__ __launch_bounds__(256) void w4_gemm_tiled(GemmArgs p, int splitk) {
   const int kb0 = (int)((int64_t)KB * blockIdx.z / splitk);
   const int kb1 = (int)((int64_t)KB * (blockIdx.z + 1) / splitk);
   const bool partials = p.mode == MODE_PARTIALS;
-  const uint8_t* __restrict__ abase = static_cast<const uint8_t*>(p.a);
-  const u32x4* __restrict__ bbase = reinterpret_cast<const u32x4*>(p.b);
+
+  // Activation tile rows [m_base, m_base + BM): rows past M are out of range.
+  const int64_t rows_valid = p.M - m_base < BM ? p.M - m_base : BM;
+  const __amdgpu_buffer_rsrc_t ra =
+      make_rsrc(static_cast<const uint8_t*>(p.a) + m_base * p.K * EB, rows_valid * p.K * EB);
+  // This wave's weight strips: NT n-blocks from nb_base, all K blocks.
+  const __amdgpu_buffer_rsrc_t rw =
+      make_rsrc(reinterpret_cast<const uint8_t*>(p.b) + nb_base * KB * 1024, (NB - nb_base) * KB * 1024);
+  uint32_t a_off[CPT], a_lds[CPT];
+#pragma unroll
+  for (int j = 0; j < CPT; ++j) {
+    const int c = tid + 256 * j;
+    const int row = c / CH_PER_ROW, col = c % CH_PER_ROW;
+    a_off[j] = (uint32_t)(row * p.K * EB + col * 16);
+    a_lds[j] = (uint32_t)(row * LDSROW + col * 16);
+  }
 
   u32x4 areg[CPT];
   auto load_a = [&](int kb) {
+    const uint32_t base = kb < kb1 ? (uint32_t)(kb * ROWB) : kOutOfRange;
 #pragma unroll
-    for (int j = 0; j < CPT; ++j) {
-      const int c = tid + 256 * j;
-      const int row = c / CH_PER_ROW, col = c % CH_PER_ROW;
-      const int64_t m = m_base + row;
-      areg[j] = (m < p.M) ? *reinterpret_cast<const u32x4*>(abase + (m * p.K + (int64_t)kb * 128) * EB + col * 16)
-                          : u32x4{0u, 0u, 0u, 0u};
-    }
+    for (int j = 0; j < CPT; ++j) areg[j] = buffer_load16(ra, base + a_off[j]);
   };
   auto store_a = [&](int buf) {
 #pragma unroll
-    for (int j = 0; j < CPT; ++j) {
-      const int c = tid + 256 * j;
-      const int row = c / CH_PER_ROW, col = c % CH_PER_ROW;
-      *reinterpret_cast<u32x4*>(&lds[buf][row * LDSROW + col * 16]) = areg[j];
-    }
+    for (int j = 0; j < CPT; ++j) *reinterpret_cast<u32x4*>(&lds[buf][a_lds[j]]) = areg[j];
   };
-  u32x4 wcur[NT], wnxt[NT];
   auto load_w = [&](int kb, u32x4* w) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      const int64_t nb = nb_base + nt;
-      w[nt] = (nb < NB) ? bbase[(nb * KB + kb) * 64 + lane] : u32x4{0u, 0u, 0u, 0u};
+      const uint32_t off = kb < kb1 ? (uint32_t)(((nt * KB) + kb) * 1024 + lane * 16) : kOutOfRange;
+      w[nt] = buffer_load16(rw, off);
     }
   };
 
@@ -356,19 +478,8 @@ __global__ __launch_bounds__(256) void w4_gemm_tiled(GemmArgs p, int splitk) {
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) ones[mt] = f32x4{};
 
-  if (kb0 < kb1) {
-    load_a(kb0);
-    store_a(0);
-    load_w(kb0, wcur);
-  }
-  __syncthreads();
-  int buf = 0;
-  for (int kb = kb0; kb < kb1; ++kb) {
-    const bool has_next = kb + 1 < kb1;
-    if (has_next) {
-      load_a(kb + 1);
-      load_w(kb + 1, wnxt);
-    }
+  // One K step on LDS buffer `buf` with weight registers `w`.
+  auto compute = [&](int buf, const u32x4* w, int kb) {
     const int g = GROUPED ? kb : 0;
     uint32_t e[NT][16];
 #pragma unroll
@@ -379,17 +490,22 @@ __global__ __launch_bounds__(256) void w4_gemm_tiled(GemmArgs p, int splitk) {
         const _Float16 h = (_Float16)(-(1024.0f + (n_op < p.N ? zero_point(p, n_op, g) : 0.0f)));
         nz = f16x2{h, h};
       }
-      expand_weights<OP, FLIP>(wcur[nt], nz, e[nt]);
+      expand_weights<OP, FLIP>(w[nt], nz, e[nt]);
     }
+    const uint8_t* src = &lds[buf][r * LDSROW + kq * 32 * EB];
+    u32x4 af[2][AV];
+#pragma unroll
+    for (int j = 0; j < AV; ++j) af[0][j] = *reinterpret_cast<const u32x4*>(src + 16 * j);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      u32x4 af[AV];
-      const uint8_t* src = &lds[buf][(mt * 16 + r) * LDSROW + kq * 32 * EB];
+      if (mt + 1 < MT) {
 #pragma unroll
-      for (int j = 0; j < AV; ++j) af[j] = *reinterpret_cast<const u32x4*>(src + 16 * j);
+        for (int j = 0; j < AV; ++j)
+          af[(mt + 1) & 1][j] = *reinterpret_cast<const u32x4*>(src + (mt + 1) * 16 * LDSROW + 16 * j);
+      }
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) block_mma<OP>(e[nt], af, acc[nt][mt]);
-      if constexpr (OP == OP_BF16) ones_mma(af, ones[mt]);
+      for (int nt = 0; nt < NT; ++nt) block_mma<OP>(e[nt], af[mt & 1], acc[nt][mt]);
+      if constexpr (OP == OP_BF16) ones_mma(af[mt & 1], ones[mt]);
     }
     if constexpr (GROUPED) {
 #pragma unroll
@@ -421,13 +537,28 @@ __global__ __launch_bounds__(256) void w4_gemm_tiled(GemmArgs p, int splitk) {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) ones[mt] = f32x4{};
     }
-    if (has_next) {
-      store_a(buf ^ 1);
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) wcur[nt] = wnxt[nt];
-    }
+  };
+
+  u32x4 w0[NT], w1[NT];
+  load_a(kb0);
+  load_w(kb0, w0);
+  store_a(0);
+  __syncthreads();
+  load_a(kb0 + 1);
+  load_w(kb0 + 1, w1);
+  for (int kb = kb0;; kb += 2) {
+    compute(0, w0, kb);
+    if (kb + 1 >= kb1) break;
+    store_a(1);
     __syncthreads();
-    buf ^= 1;
+    load_a(kb + 2);
+    load_w(kb + 2, w0);
+    compute(1, w1, kb + 1);
+    if (kb + 2 >= kb1) break;
+    store_a(0);
+    __syncthreads();
+    load_a(kb + 3);
+    load_w(kb + 3, w1);
   }
 
   if (GROUPED && partials) return;
@@ -528,8 +659,12 @@ template <int OP, bool GROUPED, bool FLIP>
 static hipError_t launch_typed(const GemmArgs& args, const GemmPlan& plan, hipStream_t stream) {
   if (plan.path == PATH_SKINNY) {
     const unsigned waves = (unsigned)plan.splitk;
-    hipLaunchKernelGGL((w4_gemm_skinny<OP, GROUPED, FLIP>), dim3((unsigned)(args.N / 16)),
-                       dim3(64 * waves), 0, stream, args);
+    if (plan.bn == 32)
+      hipLaunchKernelGGL((w4_gemm_skinny<OP, GROUPED, FLIP, 2>), dim3((unsigned)(args.N / 32)),
+                         dim3(64 * waves), 0, stream, args);
+    else
+      hipLaunchKernelGGL((w4_gemm_skinny<OP, GROUPED, FLIP, 1>), dim3((unsigned)(args.N / 16)),
+                         dim3(64 * waves), 0, stream, args);
     return hipGetLastError();
   }
   constexpr bool kByte = (OP == OP_I8 || OP == OP_FP8);
