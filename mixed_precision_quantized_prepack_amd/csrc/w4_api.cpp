@@ -21,6 +21,7 @@ thread_local std::string g_last_error;
 std::atomic<int64_t> g_force_path{0};
 std::atomic<int64_t> g_splitk{0};
 std::atomic<int64_t> g_skinny_strips{0};
+std::atomic<int64_t> g_tiled_bm{0};
 
 int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 int fail(int status, const char* fmt, ...) {
@@ -109,7 +110,7 @@ int make_plan(int64_t M, int64_t N, int64_t K, bool grouped, int op, GemmPlan* p
     if (M > 16) return fail(W4_E_UNSUPPORTED, "the small-M kernel handles M <= 16 (M=%lld)", (long long)M);
     // strips of 16 columns per wave: two strips share one activation fragment
     const int64_t fns = g_skinny_strips.load();
-    const int64_t ns = fns ? fns : ((!grouped && N % 32 == 0 && M > 1) ? 2 : 1);
+    const int64_t ns = fns ? fns : ((!grouped && N % 32 == 0) ? 2 : 1);
     if (N % (16 * ns))
       return fail(W4_E_SHAPE, "small-M kernel with %lld strips per wave needs N %% %lld == 0", (long long)ns,
                   (long long)(16 * ns));
@@ -118,8 +119,11 @@ int make_plan(int64_t M, int64_t N, int64_t K, bool grouped, int op, GemmPlan* p
     if (fs) {
       s = fs;
     } else {
+      // ~16 resident waves per CU; grouped problems hold more registers per
+      // wave (prefetched scales), so fewer fit and fewer are asked for
       const int64_t groups = N / (16 * ns);
-      const int64_t want = (16LL * cu + groups - 1) / groups;
+      const int64_t per_cu = grouped ? 8 : 16;
+      const int64_t want = (per_cu * cu + groups - 1) / groups;
       s = 1;
       while (s < want && s < 8) s *= 2;
       while (s > 1 && KB / s < 2) s /= 2;
@@ -128,13 +132,24 @@ int make_plan(int64_t M, int64_t N, int64_t K, bool grouped, int op, GemmPlan* p
       return fail(W4_E_SHAPE, "small-M kernel: %lld K-splitting waves not in [1, min(8, K/128)]", (long long)s);
     plan->splitk = (int)s;
   } else {
+    // 8-bit per-channel problems: 128-row tiles when they give at least two
+    // workgroups per CU, 64-row tiles otherwise
+    const bool tall_ok = (op == OP_I8 || op == OP_FP8) && !grouped;
+    const int64_t fbm = g_tiled_bm.load();
+    if (tall_ok) {
+      const int64_t tiles128 = ((M + 127) / 128) * ((N + plan->bn - 1) / plan->bn);
+      plan->bm = fbm ? (int)fbm : (tiles128 >= 2LL * cu ? 128 : 64);
+    } else if (fbm && fbm != plan->bm) {
+      return fail(W4_E_SHAPE, "tiled_bm=%lld is not available for this problem", (long long)fbm);
+    }
     int64_t s;
     if (fs) {
       s = fs;
     } else {
       const int64_t tiles = ((M + plan->bm - 1) / plan->bm) * ((N + plan->bn - 1) / plan->bn);
+      const int64_t slots = (tall_ok ? 2LL : 1LL) * cu;   // resident workgroups
       s = 1;
-      while (tiles * s < cu && s * 2 <= 16 && KB / (s * 2) >= 4) s *= 2;
+      while (tiles * s < slots && s * 2 <= 8 && KB / (s * 2) >= 4) s *= 2;
     }
     if (s < 1 || s > 64 || s > KB)
       return fail(W4_E_SHAPE, "tiled kernel: K split %lld not in [1, min(64, K/128)]", (long long)s);
@@ -413,6 +428,11 @@ int w4_set_option(const char* key, int64_t value) {
     g_skinny_strips.store(value);
     return ok();
   }
+  if (!strcmp(key, "tiled_bm")) {
+    if (value != 0 && value != 64 && value != 128) return fail(W4_E_SHAPE, "tiled_bm must be 0, 64 or 128");
+    g_tiled_bm.store(value);
+    return ok();
+  }
   return fail(W4_E_UNSUPPORTED, "unknown option '%s'", key);
 }
 
@@ -421,6 +441,7 @@ int64_t w4_get_option(const char* key) {
   if (!strcmp(key, "force_path")) return g_force_path.load();
   if (!strcmp(key, "splitk")) return g_splitk.load();
   if (!strcmp(key, "skinny_strips")) return g_skinny_strips.load();
+  if (!strcmp(key, "tiled_bm")) return g_tiled_bm.load();
   return -1;
 }
 

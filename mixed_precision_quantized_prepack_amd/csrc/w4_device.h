@@ -39,8 +39,8 @@ __device__ __forceinline__ void expand_i8x16(uint32_t w, uint32_t& k0123, uint32
 // The sixteen int4 values have no arithmetic relation to their e4m3 codes, so
 // this is a 16-entry table lookup done with the byte-permute instruction: the
 // low three bits of each nibble index two 8-byte tables (values 0..7 and
-// -8..-1) and bit 3 selects between the two results byte by byte.  The same
-// routine with other tables would give any other 8-bit target.
+// -8..-1) and a third permute picks, byte by byte, one of the two results by
+// bit 3.  The same routine with other tables gives any other 8-bit target.
 //   e4m3fn codes:   0:00 1:38 2:40 3:44 4:48 5:4A 6:4C 7:4E
 //                  -8:D0 -7:CE -6:CC -5:CA -4:C8 -3:C4 -2:C0 -1:B8
 // v_perm_b32(hi, lo, sel): selector byte 0..3 picks a byte of lo, 4..7 of hi.
@@ -50,23 +50,20 @@ constexpr uint32_t kFp8PosHi = 0x4E4C4A48u;
 constexpr uint32_t kFp8NegLo = 0xCACCCED0u;
 constexpr uint32_t kFp8NegHi = 0xB8C0C4C8u;
 
-__device__ __forceinline__ uint32_t byte_mask_from_bit0(uint32_t t) {
-  // t has 0 or 1 in each byte; returns 0x00 / 0xFF per byte:
-  // (t << 8) - t = sum_i t_i * 0xFF * 2^(8i) with no carries between bytes.
-  return (t << 8) - t;
-}
-
 __device__ __forceinline__ void expand_fp8(uint32_t w, uint32_t& k0123, uint32_t& k4567) {
+  // table lookups on the low three bits of each nibble
   const uint32_t sel_lo = w & 0x07070707u;
   const uint32_t sel_hi = (w >> 4) & 0x07070707u;
-  const uint32_t neg_lo = byte_mask_from_bit0((w >> 3) & 0x01010101u);
-  const uint32_t neg_hi = byte_mask_from_bit0((w >> 7) & 0x01010101u);
   const uint32_t p_lo = __builtin_amdgcn_perm(kFp8PosHi, kFp8PosLo, sel_lo);
   const uint32_t n_lo = __builtin_amdgcn_perm(kFp8NegHi, kFp8NegLo, sel_lo);
   const uint32_t p_hi = __builtin_amdgcn_perm(kFp8PosHi, kFp8PosLo, sel_hi);
   const uint32_t n_hi = __builtin_amdgcn_perm(kFp8NegHi, kFp8NegLo, sel_hi);
-  k0123 = (n_lo & neg_lo) | (p_lo & ~neg_lo);
-  k4567 = (n_hi & neg_hi) | (p_hi & ~neg_hi);
+  // per byte, keep byte i of the positive result (selector i) or of the
+  // negative one (selector i + 4): bit 3 of the nibble moved to bit 2
+  const uint32_t pick_lo = ((w >> 1) & 0x04040404u) | 0x03020100u;
+  const uint32_t pick_hi = ((w >> 5) & 0x04040404u) | 0x03020100u;
+  k0123 = __builtin_amdgcn_perm(n_lo, p_lo, pick_lo);
+  k4567 = __builtin_amdgcn_perm(n_hi, p_hi, pick_hi);
 }
 
 // ---------------------------------------------------------------------------

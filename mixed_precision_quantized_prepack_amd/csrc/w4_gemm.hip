@@ -26,6 +26,8 @@
 //   fp16 / bf16 : 4 x v_mfma_f32_16x16x32_{f16,bf16}
 // Group-128 problems restart the block accumulator every block (one block is
 // one group) and fold it into an fp32 total with the group scale.
+#include <type_traits>
+
 #include "w4_device.h"
 #include "w4_internal.h"
 
@@ -203,14 +205,19 @@ constexpr int kSkinnyMaxWaves = 8;
 #define W4_SKINNY_WPOLICY 2
 #endif
 
-// Raw 32-bit word of element i of a scale / zero-point array (fp32, or a
-// 16-bit float in the low half); out-of-range offsets read as zero.
-__device__ __forceinline__ uint32_t load_raw(__amdgpu_buffer_rsrc_t r, int dtype, uint32_t i, bool in) {
-  if (dtype == W4_F32) return __builtin_amdgcn_raw_buffer_load_b32(r, (int)(in ? i * 4u : kOutOfRange), 0, 0);
-  return __builtin_amdgcn_raw_buffer_load_b16(r, (int)(in ? i * 2u : kOutOfRange), 0, 0);
+// Scale and zero-point loads without branches (a branch around a load makes
+// the compiler wait for every outstanding load where the paths join): the
+// 32-bit word holding element i is always loaded; the 16-bit half and the
+// conversion are chosen by selects when the value is used.
+__device__ __forceinline__ uint32_t elem_byte(int dtype, uint32_t i) { return dtype == W4_F32 ? i * 4u : i * 2u; }
+__device__ __forceinline__ uint32_t load_word(__amdgpu_buffer_rsrc_t r, int dtype, uint32_t i, bool in) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, (int)(in ? (elem_byte(dtype, i) & ~3u) : kOutOfRange), 0, 0);
 }
-__device__ __forceinline__ float raw_to_f32(uint32_t b, int dtype) {
-  return dtype == W4_F32 ? __uint_as_float(b) : dtype == W4_F16 ? f16_bits_to_f32(b) : bf16_bits_to_f32(b);
+__device__ __forceinline__ float word_to_f32(uint32_t w, int dtype, uint32_t i) {
+  const uint32_t h = (elem_byte(dtype, i) & 2u) ? (w >> 16) : (w & 0xFFFFu);
+  const float f16 = f16_bits_to_f32(h);
+  const float bf = __uint_as_float(h << 16);
+  return dtype == W4_F32 ? __uint_as_float(w) : (dtype == W4_F16 ? f16 : bf);
 }
 
 // Small-M kernel (M <= 16).
@@ -225,7 +232,7 @@ __device__ __forceinline__ float raw_to_f32(uint32_t b, int dtype) {
 // MFMAs of batch i.  Rows past M and blocks past K are buffer loads with
 // out-of-range offsets: they read as zero without memory traffic.  The
 // waves' results are summed through LDS in wave order.
-template <int OP, bool GROUPED, bool FLIP, int NS>
+template <int OP, bool GROUPED, bool FLIP, int NS, bool PARTIALS>
 __global__ __launch_bounds__(64 * kSkinnyMaxWaves) void w4_gemm_skinny(GemmArgs p) {
   using Acc = typename OpTraits<OP>::Acc;
   constexpr int EB = OpTraits<OP>::kElemBytes;
@@ -239,7 +246,7 @@ __global__ __launch_bounds__(64 * kSkinnyMaxWaves) void w4_gemm_skinny(GemmArgs 
   const int KB = (int)(p.K >> 7);
   const int r = lane & 15;
   const int kq = lane >> 4;
-  const bool partials = p.mode == MODE_PARTIALS;
+  constexpr bool partials = PARTIALS;  // verification mode: store group partials
   const int zdt = p.out_dtype;                    // W4A16: zero-points in the activation dtype
 
   const __amdgpu_buffer_rsrc_t rw =
@@ -283,14 +290,14 @@ __global__ __launch_bounds__(64 * kSkinnyMaxWaves) void w4_gemm_skinny(GemmArgs 
         const uint32_t nd = (uint32_t)((nb0 + j) * 16 + 4 * kq);
         if constexpr (GROUPED) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) sc[buf][u][j][i] = load_raw(rs, p.s_dtype, (nd + i) * p.G + g, in && !partials);
+          for (int i = 0; i < 4; ++i) sc[buf][u][j][i] = load_word(rs, p.s_dtype, (nd + i) * p.G + g, in && !partials);
         }
         if constexpr (OP == OP_BF16) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) zd[buf][u][j][i] = load_raw(rz, zdt, (nd + i) * p.G + g, in && p.z);
+          for (int i = 0; i < 4; ++i) zd[buf][u][j][i] = load_word(rz, zdt, (nd + i) * p.G + g, in && p.z);
         }
         if constexpr (OP == OP_F16)
-          zo[buf][u][j] = load_raw(rz, zdt, (uint32_t)((nb0 + j) * 16 + r) * p.G + g, in && p.z);
+          zo[buf][u][j] = load_word(rz, zdt, (uint32_t)((nb0 + j) * 16 + r) * p.G + g, in && p.z);
       }
     }
   };
@@ -304,7 +311,7 @@ __global__ __launch_bounds__(64 * kSkinnyMaxWaves) void w4_gemm_skinny(GemmArgs 
       for (int j = 0; j < NS; ++j) {
         f16x2 nz = {};
         if constexpr (OP == OP_F16) {
-          const float z = p.z ? raw_to_f32(zo[buf][u][j], zdt) : 8.0f;
+          const float z = p.z ? word_to_f32(zo[buf][u][j], zdt, (uint32_t)((nb0 + j) * 16 + r) * p.G + g) : 8.0f;
           const _Float16 h = (_Float16)(-(1024.0f + z));
           nz = f16x2{h, h};
         }
@@ -319,12 +326,13 @@ __global__ __launch_bounds__(64 * kSkinnyMaxWaves) void w4_gemm_skinny(GemmArgs 
             const int64_t n_d = (nb0 + j) * 16 + 4 * kq;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              const float zc = (OP == OP_BF16) ? 128.0f + (p.z ? raw_to_f32(zd[buf][u][j][i], zdt) : 8.0f) : 0.0f;
+              const uint32_t idx = (uint32_t)(n_d + i) * p.G + g;
+              const float zc = (OP == OP_BF16) ? 128.0f + (p.z ? word_to_f32(zd[buf][u][j][i], zdt, idx) : 8.0f) : 0.0f;
               const float pv = partial_value<OP>(acc[j], ones, zc, i);
               if (partials) {
                 if (in_window(p, r, n_d + i)) store_partial<OP>(p, g, r, n_d + i, pv, int_partial<OP>(acc[j], i));
               } else {
-                tot[j][i] = fmaf(pv, raw_to_f32(sc[buf][u][j][i], p.s_dtype), tot[j][i]);
+                tot[j][i] = fmaf(pv, word_to_f32(sc[buf][u][j][i], p.s_dtype, idx), tot[j][i]);
               }
             }
           }
@@ -405,8 +413,26 @@ __global__ __launch_bounds__(64 * kSkinnyMaxWaves) void w4_gemm_skinny(GemmArgs 
 //   an out-of-range offset, so the loop has no divergent branches and the
 //   compiler can count the outstanding loads exactly.
 // ===========================================================================
-template <int OP, bool GROUPED, bool FLIP, int NT, int MT, bool SPLIT>
-__global__ __launch_bounds__(256) void w4_gemm_tiled(GemmArgs p, int splitk) {
+// Workgroups are dealt round-robin to the 8 XCDs (each with its own L2) in
+// launch order.  Renumber them so that each XCD receives a contiguous range of
+// tiles, with the m-tile index fastest: the workgroups of one XCD that run
+// together share their weight strips (and neighbouring activation tiles) in
+// that XCD's L2.  Any permutation is correct; this one only changes locality.
+constexpr int kXcds = 8;
+__device__ __forceinline__ void tile_of_block(int& bx, int& by, int& bz) {
+  const int gx = gridDim.x, gy = gridDim.y;
+  const int total = gx * gy * gridDim.z;
+  const int b = blockIdx.x + gx * (blockIdx.y + gy * blockIdx.z);
+  const int xcd = b % kXcds, idx = b / kXcds;
+  const int per = total / kXcds, rem = total % kXcds;
+  const int t = xcd < rem ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
+  bx = t % gx;
+  by = (t / gx) % gy;
+  bz = t / (gx * gy);
+}
+
+template <int OP, bool GROUPED, bool FLIP, int NT, int MT, bool SPLIT, bool PARTIALS>
+__global__ __launch_bounds__(256, GROUPED ? 1 : 2) void w4_gemm_tiled(GemmArgs p, int splitk) {
   using Acc = typename OpTraits<OP>::Acc;
   constexpr int EB = OpTraits<OP>::kElemBytes;
   constexpr int AV = act_vecs<OP>();
@@ -423,13 +449,15 @@ __global__ __launch_bounds__(256) void w4_gemm_tiled(GemmArgs p, int splitk) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave: scalar registers
   const int r = lane & 15;
   const int kq = lane >> 4;
-  const int64_t m_base = (int64_t)blockIdx.x * BM;
+  int bx, by, bz;
+  tile_of_block(bx, by, bz);
+  const int64_t m_base = (int64_t)bx * BM;
   const int64_t NB = p.N >> 4;
-  const int64_t nb_base = (int64_t)blockIdx.y * (4 * NT) + wave * NT;
+  const int64_t nb_base = (int64_t)by * (4 * NT) + wave * NT;
   const int KB = (int)(p.K >> 7);
-  const int kb0 = (int)((int64_t)KB * blockIdx.z / splitk);
-  const int kb1 = (int)((int64_t)KB * (blockIdx.z + 1) / splitk);
-  const bool partials = p.mode == MODE_PARTIALS;
+  const int kb0 = (int)((int64_t)KB * bz / splitk);
+  const int kb1 = (int)((int64_t)KB * (bz + 1) / splitk);
+  constexpr bool partials = PARTIALS;  // verification mode: store group partials
 
   // Activation tile rows [m_base, m_base + BM): rows past M are out of range.
   const int64_t rows_valid = p.M - m_base < BM ? p.M - m_base : BM;
@@ -438,6 +466,10 @@ __global__ __launch_bounds__(256) void w4_gemm_tiled(GemmArgs p, int splitk) {
   // This wave's weight strips: NT n-blocks from nb_base, all K blocks.
   const __amdgpu_buffer_rsrc_t rw =
       make_rsrc(reinterpret_cast<const uint8_t*>(p.b) + nb_base * KB * 1024, (NB - nb_base) * KB * 1024);
+  const int sbytes = p.s_dtype == W4_F32 ? 4 : 2;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.s, p.N * p.G * sbytes);
+  const __amdgpu_buffer_rsrc_t rz = make_rsrc(p.z, p.z ? p.N * p.G * 2 : 0);
+  const int zdt = p.out_dtype;  // W4A16: zero-points in the activation dtype
   uint32_t a_off[CPT], a_lds[CPT];
 #pragma unroll
   for (int j = 0; j < CPT; ++j) {
@@ -457,11 +489,16 @@ __global__ __launch_bounds__(256) void w4_gemm_tiled(GemmArgs p, int splitk) {
 #pragma unroll
     for (int j = 0; j < CPT; ++j) *reinterpret_cast<u32x4*>(&lds[buf][a_lds[j]]) = areg[j];
   };
-  auto load_w = [&](int kb, u32x4* w) {
+  // weights of step kb (and, for fp16 W4A16, the zero-point of the row each
+  // lane feeds: it is needed before the MFMAs)
+  auto load_w = [&](int kb, u32x4* w, uint32_t* wz) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       const uint32_t off = kb < kb1 ? (uint32_t)(((nt * KB) + kb) * 1024 + lane * 16) : kOutOfRange;
       w[nt] = buffer_load16(rw, off);
+      if constexpr (OP == OP_F16)
+        wz[nt] = load_word(rz, zdt, (uint32_t)(((nb_base + nt) * 16 + r) * p.G + (GROUPED ? kb : 0)),
+                           kb < kb1 && p.z);
     }
   };
 
@@ -479,15 +516,28 @@ __global__ __launch_bounds__(256) void w4_gemm_tiled(GemmArgs p, int splitk) {
   for (int mt = 0; mt < MT; ++mt) ones[mt] = f32x4{};
 
   // One K step on LDS buffer `buf` with weight registers `w`.
-  auto compute = [&](int buf, const u32x4* w, int kb) {
+  auto compute = [&](int buf, const u32x4* w, const uint32_t* wz, int kb) {
     const int g = GROUPED ? kb : 0;
+    // group scales (and bf16 zero-points) of this step: issued first, used
+    // after the MFMAs
+    uint32_t sc[NT][4], zd[NT][4];
+    if constexpr (GROUPED) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t n = (uint32_t)((nb_base + nt) * 16 + 4 * kq + i);
+          sc[nt][i] = load_word(rs, p.s_dtype, n * p.G + g, !partials);
+          if constexpr (OP == OP_BF16) zd[nt][i] = load_word(rz, zdt, n * p.G + g, p.z != nullptr);
+        }
+    }
     uint32_t e[NT][16];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       f16x2 nz = {};
       if constexpr (OP == OP_F16) {
-        const int64_t n_op = (nb_base + nt) * 16 + r;
-        const _Float16 h = (_Float16)(-(1024.0f + (n_op < p.N ? zero_point(p, n_op, g) : 0.0f)));
+        const uint32_t zi = (uint32_t)(((nb_base + nt) * 16 + r) * p.G + g);
+        const _Float16 h = (_Float16)(-(1024.0f + (p.z ? word_to_f32(wz[nt], zdt, zi) : 8.0f)));
         nz = f16x2{h, h};
       }
       expand_weights<OP, FLIP>(w[nt], nz, e[nt]);
@@ -511,12 +561,12 @@ __global__ __launch_bounds__(256) void w4_gemm_tiled(GemmArgs p, int splitk) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         const int64_t n_d = (nb_base + nt) * 16 + 4 * kq;
-        if (n_d >= p.N) continue;
-        float sc[4], zc[4];
+        float scf[4], zc[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          sc[i] = partials ? 0.0f : load_as_f32(p.s, p.s_dtype, (n_d + i) * p.G + g);
-          zc[i] = (OP == OP_BF16) ? 128.0f + zero_point(p, n_d + i, g) : 0.0f;
+          const uint32_t idx = (uint32_t)(n_d + i) * p.G + g;
+          scf[i] = word_to_f32(sc[nt][i], p.s_dtype, idx);
+          zc[i] = (OP == OP_BF16) ? 128.0f + (p.z ? word_to_f32(zd[nt][i], zdt, idx) : 8.0f) : 0.0f;
         }
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
@@ -525,10 +575,10 @@ __global__ __launch_bounds__(256) void w4_gemm_tiled(GemmArgs p, int splitk) {
             const float pv = partial_value<OP>(acc[nt][mt], ones[mt], zc[i], i);
             if (partials) {
               const int64_t m = m_base + mt * 16 + r;
-              if (m < p.M && in_window(p, m, n_d + i))
+              if (m < p.M && n_d < p.N && in_window(p, m, n_d + i))
                 store_partial<OP>(p, g, m, n_d + i, pv, int_partial<OP>(acc[nt][mt], i));
             } else {
-              tot[nt][mt][i] = fmaf(pv, sc[i], tot[nt][mt][i]);
+              tot[nt][mt][i] = fmaf(pv, scf[i], tot[nt][mt][i]);
             }
           }
           acc[nt][mt] = Acc{};
@@ -540,25 +590,26 @@ __global__ __launch_bounds__(256) void w4_gemm_tiled(GemmArgs p, int splitk) {
   };
 
   u32x4 w0[NT], w1[NT];
+  uint32_t z0[NT], z1[NT];
   load_a(kb0);
-  load_w(kb0, w0);
+  load_w(kb0, w0, z0);
   store_a(0);
   __syncthreads();
   load_a(kb0 + 1);
-  load_w(kb0 + 1, w1);
+  load_w(kb0 + 1, w1, z1);
   for (int kb = kb0;; kb += 2) {
-    compute(0, w0, kb);
+    compute(0, w0, z0, kb);
     if (kb + 1 >= kb1) break;
     store_a(1);
     __syncthreads();
     load_a(kb + 2);
-    load_w(kb + 2, w0);
-    compute(1, w1, kb + 1);
+    load_w(kb + 2, w0, z0);
+    compute(1, w1, z1, kb + 1);
     if (kb + 2 >= kb1) break;
     store_a(0);
     __syncthreads();
     load_a(kb + 3);
-    load_w(kb + 3, w1);
+    load_w(kb + 3, w1, z1);
   }
 
   if (GROUPED && partials) return;
@@ -587,7 +638,7 @@ __global__ __launch_bounds__(256) void w4_gemm_tiled(GemmArgs p, int splitk) {
           bits[i] = __float_as_uint(partial_value<OP>(acc[nt][mt], ones[mt], zc[i], i));
       }
       if constexpr (SPLIT) {
-        uint32_t* slot = static_cast<uint32_t*>(p.ws) + ((int64_t)blockIdx.z * p.M + m) * p.N + n_d;
+        uint32_t* slot = static_cast<uint32_t*>(p.ws) + ((int64_t)bz * p.M + m) * p.N + n_d;
         *reinterpret_cast<u32x4*>(slot) = u32x4{bits[0], bits[1], bits[2], bits[3]};
       } else if (partials) {
 #pragma unroll
@@ -646,6 +697,7 @@ __global__ __launch_bounds__(256) void w4_splitk_reduce(GemmArgs p, int splitk) 
 // Host-side launchers.
 // ===========================================================================
 void tiled_tile(int op, bool grouped, int* bm, int* bn) {
+  // default (tallest) tile; 8-bit per-channel problems may also use bm = 64
   if (op == OP_I8 || op == OP_FP8) {
     *bm = grouped ? 64 : 128;
     *bn = 256;
@@ -659,35 +711,68 @@ template <int OP, bool GROUPED, bool FLIP>
 static hipError_t launch_typed(const GemmArgs& args, const GemmPlan& plan, hipStream_t stream) {
   if (plan.path == PATH_SKINNY) {
     const unsigned waves = (unsigned)plan.splitk;
-    if (plan.bn == 32)
-      hipLaunchKernelGGL((w4_gemm_skinny<OP, GROUPED, FLIP, 2>), dim3((unsigned)(args.N / 32)),
-                         dim3(64 * waves), 0, stream, args);
-    else
-      hipLaunchKernelGGL((w4_gemm_skinny<OP, GROUPED, FLIP, 1>), dim3((unsigned)(args.N / 16)),
-                         dim3(64 * waves), 0, stream, args);
+    const bool part = args.mode == MODE_PARTIALS;
+    if (plan.bn == 32) {
+      if (part)
+        hipLaunchKernelGGL((w4_gemm_skinny<OP, GROUPED, FLIP, 2, true>), dim3((unsigned)(args.N / 32)),
+                           dim3(64 * waves), 0, stream, args);
+      else
+        hipLaunchKernelGGL((w4_gemm_skinny<OP, GROUPED, FLIP, 2, false>), dim3((unsigned)(args.N / 32)),
+                           dim3(64 * waves), 0, stream, args);
+    } else {
+      if (part)
+        hipLaunchKernelGGL((w4_gemm_skinny<OP, GROUPED, FLIP, 1, true>), dim3((unsigned)(args.N / 16)),
+                           dim3(64 * waves), 0, stream, args);
+      else
+        hipLaunchKernelGGL((w4_gemm_skinny<OP, GROUPED, FLIP, 1, false>), dim3((unsigned)(args.N / 16)),
+                           dim3(64 * waves), 0, stream, args);
+    }
     return hipGetLastError();
   }
   constexpr bool kByte = (OP == OP_I8 || OP == OP_FP8);
   constexpr int NT = kByte ? 4 : 2;
-  constexpr int MT = kByte ? (GROUPED ? 4 : 8) : 4;
-  const int64_t BM = MT * 16, BN = NT * 64;
-  const dim3 grid((unsigned)((args.M + BM - 1) / BM), (unsigned)((args.N + BN - 1) / BN),
-                  (unsigned)plan.splitk);
-  if (plan.splitk > 1)
-    hipLaunchKernelGGL((w4_gemm_tiled<OP, GROUPED, FLIP, NT, MT, true>), grid, dim3(256), 0, stream, args,
+  const int64_t BN = NT * 64;
+  auto finish = [&]() -> hipError_t {
+    hipError_t e = hipGetLastError();
+    // grouped partials are stored by the tiled kernel itself
+    if (e != hipSuccess || plan.splitk == 1 || (GROUPED && args.mode == MODE_PARTIALS)) return e;
+    const int64_t total = args.M * (args.N / 4);
+    int64_t blocks = (total + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    hipLaunchKernelGGL((w4_splitk_reduce<OP, GROUPED>), dim3((unsigned)blocks), dim3(256), 0, stream, args,
                        plan.splitk);
-  else
-    hipLaunchKernelGGL((w4_gemm_tiled<OP, GROUPED, FLIP, NT, MT, false>), grid, dim3(256), 0, stream, args,
-                       1);
-  hipError_t e = hipGetLastError();
-  // grouped partials are stored by the tiled kernel itself
-  if (e != hipSuccess || plan.splitk == 1 || (GROUPED && args.mode == MODE_PARTIALS)) return e;
-  const int64_t total = args.M * (args.N / 4);
-  int64_t blocks = (total + 255) / 256;
-  if (blocks > 65536) blocks = 65536;
-  hipLaunchKernelGGL((w4_splitk_reduce<OP, GROUPED>), dim3((unsigned)blocks), dim3(256), 0, stream,
-                     args, plan.splitk);
-  return hipGetLastError();
+    return hipGetLastError();
+  };
+  auto launch = [&](auto mt_tag) {
+    constexpr int MT = decltype(mt_tag)::value;
+    const int64_t BM = MT * 16;
+    const dim3 grid((unsigned)((args.M + BM - 1) / BM), (unsigned)((args.N + BN - 1) / BN),
+                    (unsigned)plan.splitk);
+    const bool part = args.mode == MODE_PARTIALS;
+    if (plan.splitk > 1) {
+      if (part)
+        hipLaunchKernelGGL((w4_gemm_tiled<OP, GROUPED, FLIP, NT, MT, true, true>), grid, dim3(256), 0, stream,
+                           args, plan.splitk);
+      else
+        hipLaunchKernelGGL((w4_gemm_tiled<OP, GROUPED, FLIP, NT, MT, true, false>), grid, dim3(256), 0, stream,
+                           args, plan.splitk);
+    } else {
+      if (part)
+        hipLaunchKernelGGL((w4_gemm_tiled<OP, GROUPED, FLIP, NT, MT, false, true>), grid, dim3(256), 0, stream,
+                           args, 1);
+      else
+        hipLaunchKernelGGL((w4_gemm_tiled<OP, GROUPED, FLIP, NT, MT, false, false>), grid, dim3(256), 0, stream,
+                           args, 1);
+    }
+  };
+  if constexpr (kByte && !GROUPED) {
+    if (plan.bm == 128) {
+      launch(std::integral_constant<int, 8>{});
+      return finish();
+    }
+  }
+  launch(std::integral_constant<int, 4>{});
+  return finish();
 }
 
 hipError_t launch_gemm(const GemmArgs& args, int op, bool grouped, bool flip, const GemmPlan& plan,

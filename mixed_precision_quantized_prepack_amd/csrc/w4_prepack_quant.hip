@@ -79,15 +79,22 @@ hipError_t launch_prepack(const void* w_logical, void* w_packed, int64_t N, int6
 // summary and review discussion: one scale per row computed at run time from
 // the row's absolute maximum.
 //
-// One workgroup (256 threads) per row.  Each thread keeps up to kChunks
+// One workgroup per row (256 threads, or 1024 when there are few rows so that
+// a single row is not latency bound).  Each thread keeps up to kChunks
 // 16-byte chunks (8 elements) of the row in registers, so the row is read from
 // HBM once: pass 1 takes the absolute maximum, a wave reduction plus an LDS
-// exchange gives the row maximum, pass 2 divides (correctly rounded fp32
-// division), rounds half to even and stores the codes.  Rows longer than
-// 256 * 8 * kChunks elements re-read the tail from memory in pass 2.
+// exchange gives the row maximum, pass 2 forms the quotients and stores the
+// codes.  Longer rows re-read their tail in pass 2.
+//
+// Quotients x / s must be the correctly rounded fp32 division.  They are
+// formed from one correctly rounded reciprocal per row, y = RN(1/s):
+// q = RN(x * y), the exact residual r = fma(-q, s, x), and RN(q + r * y), which
+// equals RN(x / s) by Markstein's theorem (y within half an ulp of 1/s, q
+// within one ulp of x/s, r exact; no overflow or underflow).  Rows whose scale
+// is too small for that (bf16 inputs near the bottom of the exponent range)
+// use the plain division.
 // ---------------------------------------------------------------------------
-constexpr int kQuantThreads = 256;
-constexpr int kChunks = 12;  // K <= 24576 stays register resident
+constexpr int kChunks = 12;
 
 template <int XT>
 __device__ __forceinline__ float elem(const uint4& v, int j) {
@@ -96,20 +103,24 @@ __device__ __forceinline__ float elem(const uint4& v, int j) {
   return XT == W4_F16 ? f16_bits_to_f32(b) : bf16_bits_to_f32(b);
 }
 
-__device__ __forceinline__ float chunk_absmax(float m, const uint4& v, bool bf16) {
-  // |x| via the sign bit, max via fmaxf on the widened values
-  if (bf16) {
+template <int XT>
+__device__ __forceinline__ float chunk_absmax(float m, const uint4& v) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(elem<W4_BF16>(v, j)));
-  } else {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(elem<W4_F16>(v, j)));
-  }
+  for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(elem<XT>(v, j)));
   return m;
 }
 
-template <int XT, int QT>
-__device__ __forceinline__ uint2 quant_chunk(const uint4& v, float s) {
+// correctly rounded x / s given y = RN(1 / s) (see above).  The sum q + r*y
+// of a zero quotient is +0 even for x = -0, so the sign is taken from x (with
+// s > 0 the quotient always has the sign of x).
+__device__ __forceinline__ float div_rn(float x, float s, float y) {
+  const float q = x * y;
+  const float r = fmaf(-q, s, x);
+  return copysignf(fmaf(r, y, q), x);
+}
+
+template <int XT, int QT, bool FAST>
+__device__ __forceinline__ uint2 quant_chunk(const uint4& v, float s, float y) {
   uint32_t out[2];
   if (QT == W4_I8) {
 #pragma unroll
@@ -117,7 +128,8 @@ __device__ __forceinline__ uint2 quant_chunk(const uint4& v, float s) {
       uint32_t word = 0;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        float q = rintf(elem<XT>(v, 4 * h + j) / s);
+        const float x = elem<XT>(v, 4 * h + j);
+        float q = rintf(FAST ? div_rn(x, s, y) : x / s);
         q = fminf(fmaxf(q, -127.0f), 127.0f);
         word |= ((uint32_t)(int)q & 0xFFu) << (8 * j);
       }
@@ -128,8 +140,10 @@ __device__ __forceinline__ uint2 quant_chunk(const uint4& v, float s) {
     for (int h = 0; h < 2; ++h) {
       float q[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        q[j] = fminf(fmaxf(elem<XT>(v, 4 * h + j) / s, -448.0f), 448.0f);
+      for (int j = 0; j < 4; ++j) {
+        const float x = elem<XT>(v, 4 * h + j);
+        q[j] = fminf(fmaxf(FAST ? div_rn(x, s, y) : x / s, -448.0f), 448.0f);
+      }
       int word = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
       word = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], word, true);
       out[h] = (uint32_t)word;
@@ -138,11 +152,10 @@ __device__ __forceinline__ uint2 quant_chunk(const uint4& v, float s) {
   return make_uint2(out[0], out[1]);
 }
 
-template <int XT, int QT>
-__global__ __launch_bounds__(kQuantThreads) void w4_quant_kernel(const uint16_t* __restrict__ x,
-                                                                 uint8_t* __restrict__ xq,
-                                                                 float* __restrict__ scales,
-                                                                 int64_t K) {
+template <int XT, int QT, int THREADS>
+__global__ __launch_bounds__(THREADS) void w4_quant_kernel(const uint16_t* __restrict__ x,
+                                                           uint8_t* __restrict__ xq,
+                                                           float* __restrict__ scales, int64_t K) {
   const int64_t row = blockIdx.x;
   const int tid = threadIdx.x;
   const uint4* xr = reinterpret_cast<const uint4*>(x + row * K);
@@ -153,54 +166,76 @@ __global__ __launch_bounds__(kQuantThreads) void w4_quant_kernel(const uint16_t*
   float amax = 0.0f;
 #pragma unroll
   for (int c = 0; c < kChunks; ++c) {
-    const int idx = c * kQuantThreads + tid;
+    const int idx = c * THREADS + tid;
     if (idx < nchunks) {
       v[c] = xr[idx];
-      amax = chunk_absmax(amax, v[c], XT == W4_BF16);
+      amax = chunk_absmax<XT>(amax, v[c]);
     }
   }
-  for (int idx = kChunks * kQuantThreads + tid; idx < nchunks; idx += kQuantThreads)
-    amax = chunk_absmax(amax, xr[idx], XT == W4_BF16);
+  for (int idx = kChunks * THREADS + tid; idx < nchunks; idx += THREADS)
+    amax = chunk_absmax<XT>(amax, xr[idx]);
 
   // row maximum: wave butterfly, then one value per wave through LDS
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
-  __shared__ float wave_max[kQuantThreads / 64];
+  __shared__ float wave_max[THREADS / 64];
   if ((tid & 63) == 0) wave_max[tid >> 6] = amax;
   __syncthreads();
   amax = wave_max[0];
 #pragma unroll
-  for (int w = 1; w < kQuantThreads / 64; ++w) amax = fmaxf(amax, wave_max[w]);
+  for (int w = 1; w < THREADS / 64; ++w) amax = fmaxf(amax, wave_max[w]);
 
   const float qmax = (QT == W4_I8) ? 127.0f : 448.0f;
   const float s = amax / qmax;
   if (tid == 0) scales[row] = s;
   if (s == 0.0f) {
-    for (int idx = tid; idx < nchunks; idx += kQuantThreads) qr[idx] = make_uint2(0u, 0u);
+    for (int idx = tid; idx < nchunks; idx += THREADS) qr[idx] = make_uint2(0u, 0u);
     return;
   }
+  const float y = 1.0f / s;
+  if (s >= 0x1p-100f) {
 #pragma unroll
-  for (int c = 0; c < kChunks; ++c) {
-    const int idx = c * kQuantThreads + tid;
-    if (idx < nchunks) qr[idx] = quant_chunk<XT, QT>(v[c], s);
+    for (int c = 0; c < kChunks; ++c) {
+      const int idx = c * THREADS + tid;
+      if (idx < nchunks) qr[idx] = quant_chunk<XT, QT, true>(v[c], s, y);
+    }
+    for (int idx = kChunks * THREADS + tid; idx < nchunks; idx += THREADS)
+      qr[idx] = quant_chunk<XT, QT, true>(xr[idx], s, y);
+  } else {
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) {
+      const int idx = c * THREADS + tid;
+      if (idx < nchunks) qr[idx] = quant_chunk<XT, QT, false>(v[c], s, y);
+    }
+    for (int idx = kChunks * THREADS + tid; idx < nchunks; idx += THREADS)
+      qr[idx] = quant_chunk<XT, QT, false>(xr[idx], s, y);
   }
-  for (int idx = kChunks * kQuantThreads + tid; idx < nchunks; idx += kQuantThreads)
-    qr[idx] = quant_chunk<XT, QT>(xr[idx], s);
+}
+
+template <int THREADS>
+static void launch_quant_t(const void* x, int x_dtype, void* xq, int q_dtype, float* scales, int64_t M,
+                           int64_t K, hipStream_t stream) {
+  const dim3 grid((unsigned)M), block(THREADS);
+  const uint16_t* xp = (const uint16_t*)x;
+  uint8_t* qp = (uint8_t*)xq;
+  if (x_dtype == W4_F16 && q_dtype == W4_I8)
+    hipLaunchKernelGGL((w4_quant_kernel<W4_F16, W4_I8, THREADS>), grid, block, 0, stream, xp, qp, scales, K);
+  else if (x_dtype == W4_F16)
+    hipLaunchKernelGGL((w4_quant_kernel<W4_F16, W4_FP8_E4M3, THREADS>), grid, block, 0, stream, xp, qp, scales, K);
+  else if (q_dtype == W4_I8)
+    hipLaunchKernelGGL((w4_quant_kernel<W4_BF16, W4_I8, THREADS>), grid, block, 0, stream, xp, qp, scales, K);
+  else
+    hipLaunchKernelGGL((w4_quant_kernel<W4_BF16, W4_FP8_E4M3, THREADS>), grid, block, 0, stream, xp, qp, scales,
+                       K);
 }
 
 hipError_t launch_quant(const void* x, int x_dtype, void* xq, int q_dtype, float* scales, int64_t M,
                         int64_t K, hipStream_t stream) {
-  const dim3 grid((unsigned)M), block(kQuantThreads);
-  const uint16_t* xp = (const uint16_t*)x;
-  uint8_t* qp = (uint8_t*)xq;
-  if (x_dtype == W4_F16 && q_dtype == W4_I8)
-    hipLaunchKernelGGL((w4_quant_kernel<W4_F16, W4_I8>), grid, block, 0, stream, xp, qp, scales, K);
-  else if (x_dtype == W4_F16)
-    hipLaunchKernelGGL((w4_quant_kernel<W4_F16, W4_FP8_E4M3>), grid, block, 0, stream, xp, qp, scales, K);
-  else if (q_dtype == W4_I8)
-    hipLaunchKernelGGL((w4_quant_kernel<W4_BF16, W4_I8>), grid, block, 0, stream, xp, qp, scales, K);
+  // few rows: a whole CU per row
+  if (M <= 512 && K >= 8 * 1024)
+    launch_quant_t<1024>(x, x_dtype, xq, q_dtype, scales, M, K, stream);
   else
-    hipLaunchKernelGGL((w4_quant_kernel<W4_BF16, W4_FP8_E4M3>), grid, block, 0, stream, xp, qp, scales, K);
+    launch_quant_t<256>(x, x_dtype, xq, q_dtype, scales, M, K, stream);
   return hipGetLastError();
 }
 
