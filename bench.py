@@ -20,8 +20,12 @@ and the CPU oracle timed on a bounded sample as a baseline.
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -33,6 +37,25 @@ MS = (1, 16, 64, 256, 1024, 4096)
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 INT8_PEAK_TOPS = 5000.0         # MI355X dense int8 MFMA
 METRIC = "W4A8 GEMM TOPS + weight GB/s (% roofline), N=8192 K=21760, M=1..4096"
+CALIB_BYTES = 256 << 20          # plain copy of known size: reads and writes this many bytes
+TRAFFIC_MD = os.path.join(ROOT, "profiles", "w4a8_i8_pc_8192x21760_hbm_traffic.md")
+GEMM_SOURCES = ["mixed_precision_quantized_prepack_amd/csrc/w4_gemm.hip",
+                "mixed_precision_quantized_prepack_amd/csrc/w4_device.h",
+                "mixed_precision_quantized_prepack_amd/csrc/w4_api.cpp"]
+
+
+def sources_sha256() -> str:
+    h = hashlib.sha256()
+    for f in GEMM_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def kernel_label(path: int, split: int, tm: int, tn: int) -> str:
+    if path == 1:
+        return f"w4_gemm_skinny<int8, per-channel, {tn // 16} strip(s)>"
+    return f"w4_gemm_tiled<int8, per-channel, {tm}x{tn} tile, {'K split' if split > 1 else 'no K split'}>"
 
 
 def gemm_alg_bytes(M: int) -> int:
@@ -75,6 +98,121 @@ def cpu_baseline(seconds: float) -> dict:
                       f"fp64 epilogue), {iters} runs in {el:.1f} s; host has {os.cpu_count()} CPUs"}
 
 
+# ---------------------------------------------------------------------------
+# HBM traffic from rocprofv3 counters.
+# ---------------------------------------------------------------------------
+def _read_csv(d: str, suffix: str):
+    files = glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True)
+    rows = []
+    for f in files:
+        with open(f) as fh:
+            rows += list(csv.DictReader(fh))
+    return rows
+
+
+def _short(name: str) -> str:
+    return re.sub(r"\s+", " ", name.split("(")[0].replace("void ", ""))
+
+
+def _dispatch_counters(d: str, counter: str):
+    """{(kernel, grid): [value per dispatch]} for one counter (KiB per dispatch)."""
+    out = {}
+    for r in _read_csv(d, "counter_collection.csv"):
+        if r.get("Counter_Name") != counter:
+            continue
+        key = (_short(r["Kernel_Name"]), int(float(r.get("Grid_Size", 0) or 0)))
+        out.setdefault(key, []).append(float(r["Counter_Value"]))
+    return out
+
+
+def summarize(trace_dir: str, fetch_dir: str, write_dir: str) -> int:
+    fetch = _dispatch_counters(fetch_dir, "FETCH_SIZE")
+    write = _dispatch_counters(write_dir, "WRITE_SIZE")
+    calib_f = [v for (k, g), vs in fetch.items() if "BitwiseNot" in k or "bitwise_not" in k for v in vs]
+    calib_w = [v for (k, g), vs in write.items() if "BitwiseNot" in k or "bitwise_not" in k for v in vs]
+    f_factor = CALIB_BYTES / (1024 * (sum(calib_f) / len(calib_f))) if calib_f else None
+    w_factor = CALIB_BYTES / (1024 * (sum(calib_w) / len(calib_w))) if calib_w else None
+    stats = {_short(r["Name"]): r for r in _read_csv(trace_dir, "kernel_stats.csv")}
+    kernels = {}
+    for (k, g), vs in fetch.items():
+        if not k.startswith("w4::"):
+            continue
+        wv = write.get((k, g), [])
+        kernels[f"{k} grid={g}"] = {
+            "dispatches": len(vs), "fetch_KiB_avg": sum(vs) / len(vs),
+            "write_KiB_avg": (sum(wv) / len(wv)) if wv else None,
+            "hbm_bytes_per_launch": (sum(vs) / len(vs) * 1024 * f_factor +
+                                     ((sum(wv) / len(wv)) * 1024 * w_factor if wv else 0.0))
+            if f_factor and w_factor else None}
+    data = {"source_sha256": sources_sha256(), "fetch_factor": f_factor, "write_factor": w_factor,
+            "kernels": kernels}
+    lines = ["# HBM traffic: W4A8 int8 per-channel, N=8192 K=21760, M sweep {1,16,64,256,1024,4096}", "",
+             "Commands (repository root, one MI355X; each counter in its own run):", "", "```",
+             f"rocprofv3 --kernel-trace --stats --output-format csv -d {trace_dir} -o trace -- "
+             "python -u bench.py --steps 2 --warmup 1 --no-cpu-baseline --calibrate-copy",
+             f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {fetch_dir} -o fetch -- "
+             "python -u bench.py --steps 2 --warmup 1 --no-cpu-baseline --calibrate-copy",
+             f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {write_dir} -o write -- "
+             "python -u bench.py --steps 2 --warmup 1 --no-cpu-baseline --calibrate-copy",
+             f"python bench.py --summarize {trace_dir} {fetch_dir} {write_dir}", "```", "",
+             "FETCH_SIZE / WRITE_SIZE are KiB per dispatch.  They are scaled by what the same counters read "
+             f"for a plain copy kernel that reads and writes {CALIB_BYTES >> 20} MiB "
+             f"(fetch factor {f_factor if f_factor is None else round(f_factor, 4)}, "
+             f"write factor {w_factor if w_factor is None else round(w_factor, 4)}).", "",
+             "| kernel | grid | dispatches | FETCH KiB | WRITE KiB | HBM bytes / launch |", "|---|---|---|---|---|---|"]
+    for name, v in sorted(kernels.items()):
+        k, g = name.rsplit(" grid=", 1)
+        lines.append(f"| `{k[:90]}` | {g} | {v['dispatches']} | {v['fetch_KiB_avg']:.0f} | "
+                     f"{v['write_KiB_avg'] if v['write_KiB_avg'] is None else round(v['write_KiB_avg'])} | "
+                     f"{v['hbm_bytes_per_launch'] if v['hbm_bytes_per_launch'] is None else int(v['hbm_bytes_per_launch'])} |")
+    lines += ["", "Kernel time from the trace run:", "", "| kernel | calls | avg us |", "|---|---|---|"]
+    for k, r in stats.items():
+        lines.append(f"| `{k[:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} |")
+    lines += ["", "Machine-readable (read by bench.py while the GEMM sources hash the same):", "", "```json",
+              json.dumps(data, indent=1), "```", ""]
+    os.makedirs(os.path.dirname(TRAFFIC_MD), exist_ok=True)
+    with open(TRAFFIC_MD, "w") as fh:
+        fh.write("\n".join(lines))
+    print(TRAFFIC_MD)
+    return 0
+
+
+def traffic_for(label: str, Ms) -> "float | None":
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    summary, or None if there is none or the GEMM sources changed since."""
+    try:
+        with open(TRAFFIC_MD) as fh:
+            text = fh.read()
+        data = json.loads(text.split("```json", 1)[1].split("```", 1)[0])
+    except (OSError, IndexError, ValueError):
+        return None
+    if data.get("source_sha256") != sources_sha256():
+        return None
+    grids = {M: grid_of(label, M) for M in Ms}
+    vals = [v["hbm_bytes_per_launch"] for k, v in data["kernels"].items()
+            if v.get("hbm_bytes_per_launch") and any(k.endswith(f"grid={g}") and kernel_matches(k, label)
+                                                      for g in grids.values())]
+    return round(sum(vals) / len(vals)) if vals else None
+
+
+def grid_of(label: str, M: int) -> int:
+    """Total threads of the GEMM launch for M (the trace's Grid_Size)."""
+    m = re.search(r"(\d+)x(\d+) tile", label)
+    if not m:
+        return -1
+    tm, tn = int(m.group(1)), int(m.group(2))
+    return ((M + tm - 1) // tm) * ((N + tn - 1) // tn) * 256
+
+
+def kernel_matches(key: str, label: str) -> bool:
+    if "tiled" in label:
+        m = re.search(r"(\d+)x(\d+) tile", label)
+        mt = int(m.group(1)) // 16 if m else 0
+        return "w4_gemm_tiled" in key and f", 4, {mt}, " in key and key.rstrip().endswith(
+            "grid=" + key.rsplit("grid=", 1)[1])
+    return "w4_gemm_skinny" in key
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -83,7 +221,13 @@ def main(argv=None) -> int:
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--ms", default=",".join(str(m) for m in MS))
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 256 MiB device copy (read + write) to scale HBM counters")
+    ap.add_argument("--summarize", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
+                    help="write the HBM-traffic summary from rocprofv3 outputs and exit")
     args = ap.parse_args(argv)
+    if args.summarize:
+        return summarize(*args.summarize)
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the kernels run on a single MI355X and this build has no "
               f"multi-GPU path (asked for --gpus {args.gpus}).", file=sys.stderr)
@@ -117,6 +261,21 @@ def main(argv=None) -> int:
     ws_bytes = max(w4.gemm_workspace_bytes(M, N, K, -1, w4.I8) for M in Ms)
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     plans = {M: w4.gemm_plan(M, N, K, -1, w4.I8) for M in Ms}
+
+    calib = None
+    if args.calibrate_copy:
+        src = torch.zeros(CALIB_BYTES // 4, dtype=torch.int32, device=dev)
+        dst = torch.empty_like(src)
+        ce = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+        torch.bitwise_not(src, out=dst)                  # warm-up
+        ce[0].record()
+        torch.bitwise_not(src, out=dst)                  # plain copy kernel: reads and writes 256 MiB
+        ce[1].record()
+        torch.cuda.synchronize()
+        us = ce[0].elapsed_time(ce[1]) * 1e3
+        calib = {"bytes_read": CALIB_BYTES, "bytes_written": CALIB_BYTES, "us": round(us, 2),
+                 "GBps_read_plus_write": round(2 * CALIB_BYTES / (us * 1e-6) / 1e9, 1)}
+        del src, dst
 
     # prepack (load-time): one launch per weight copy, timed with events
     pev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(copies)]
@@ -165,39 +324,39 @@ def main(argv=None) -> int:
         g_us = sum(all_evs[s][i][1].elapsed_time(all_evs[s][i][2]) for s in range(args.steps)) * 1e3 / args.steps
         ops = 2.0 * M * N * K
         total_ops += ops
-        path, split = plans[M]
+        path, split, tm, tn = plans[M]
         tops = ops / (g_us * 1e-6) / 1e12
         wgbps = (N * K / 2) / (g_us * 1e-6) / 1e9
         agbps = gemm_alg_bytes(M) / (g_us * 1e-6) / 1e9
-        per_m.append({"M": M, "kernel": "small_m" if path == 1 else "tiled", "k_split": split,
+        per_m.append({"M": M, "kernel": kernel_label(path, split, tm, tn), "k_split": split,
                       "gemm_us": round(g_us, 2), "quant_us": round(q_us, 2), "gemm_tops": round(tops, 2),
                       "weight_GBps": round(wgbps, 1), "alg_GBps": round(agbps, 1),
                       "hbm_frac": round(agbps / HBM_PEAK_GBPS, 4),
                       "mfma_frac": round(tops / INT8_PEAK_TOPS, 4)})
     value = total_ops / (ms_per_step * 1e-3) / 1e12
 
-    # dominant kernel: the tiled kernel without K split (the large-M launches)
-    dom = [(pm["M"], pm["gemm_us"]) for pm in per_m if pm["kernel"] == "tiled" and pm["k_split"] == 1]
-    if dom:
-        flops = sum(2.0 * M * N * K for M, _ in dom) / len(dom)
-        dur = sum(us for _, us in dom) / len(dom)
-        ach = flops / (dur * 1e-6) / 1e12
-        roofline = {"bound": "mfma", "achieved": round(ach, 2), "peak": INT8_PEAK_TOPS, "unit": "TFLOP/s",
-                    "frac": round(ach / INT8_PEAK_TOPS, 4), "traffic": None,
-                    "kernel": "w4_gemm_tiled<int8, per-channel, no K split>",
-                    "launches": [M for M, _ in dom], "avg_launch_us": round(dur, 2),
-                    "note": "int8 ops (2 per multiply-add) per second"}
-    else:
-        roofline = None
-    small = [pm for pm in per_m if pm["kernel"] == "small_m"]
+    # dominant kernel: the kernel (template instance) with the most time in a step
+    by_kernel = {}
+    for pm in per_m:
+        by_kernel.setdefault(pm["kernel"], []).append(pm)
+    dom_name, dom = max(by_kernel.items(), key=lambda kv: sum(pm["gemm_us"] for pm in kv[1]))
+    flops = sum(2.0 * pm["M"] * N * K for pm in dom) / len(dom)
+    dur = sum(pm["gemm_us"] for pm in dom) / len(dom)
+    ach = flops / (dur * 1e-6) / 1e12
+    roofline = {"bound": "mfma", "achieved": round(ach, 2), "peak": INT8_PEAK_TOPS, "unit": "TFLOP/s",
+                "frac": round(ach / INT8_PEAK_TOPS, 4), "traffic": traffic_for(dom_name, [pm["M"] for pm in dom]),
+                "kernel": dom_name, "launches": [pm["M"] for pm in dom], "avg_launch_us": round(dur, 2),
+                "note": "int8 ops (2 per multiply-add) per second"}
+    small = [pm for pm in per_m if pm["kernel"].startswith("w4_gemm_skinny")]
     roofline_small = None
     if small:
         b = sum(gemm_alg_bytes(pm["M"]) for pm in small) / len(small)
         dur = sum(pm["gemm_us"] for pm in small) / len(small)
         gb = b / (dur * 1e-6) / 1e9
         roofline_small = {"bound": "hbm", "achieved": round(gb, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                          "frac": round(gb / HBM_PEAK_GBPS, 4), "traffic": None,
-                          "kernel": "w4_gemm_skinny<int8, per-channel>", "launches": [pm["M"] for pm in small],
+                          "frac": round(gb / HBM_PEAK_GBPS, 4),
+                          "traffic": traffic_for(small[0]["kernel"], [pm["M"] for pm in small]),
+                          "kernel": small[0]["kernel"], "launches": [pm["M"] for pm in small],
                           "avg_launch_us": round(dur, 2)}
 
     line = {
@@ -215,6 +374,8 @@ def main(argv=None) -> int:
                     "GBps_read_plus_write": round(N * K / (prepack_us[len(prepack_us) // 2] * 1e-6) / 1e9, 1)},
         "wall_s_timed": round(wall, 3),
     }
+    if calib:
+        line["copy_calibration"] = calib
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(line), flush=True)

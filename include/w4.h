@@ -249,10 +249,12 @@ W4_API int w4_set_option(const char* key, int64_t value);
 W4_API int64_t w4_get_option(const char* key);
 
 /* The kernel the GEMM entry points would choose for this problem under the
- * current options (*path: 1 = small-M, 2 = tiled) and its K split; for
- * logging and tests.  Errors as for the GEMM's shape checks. */
+ * current options, for logging and tests: *path (1 = small-M, 2 = tiled), its
+ * K split (*splitk), and the output tile one workgroup computes (*tile_m rows
+ * x *tile_n columns; for the small-M kernel tile_m is 16).  Any out pointer
+ * may be NULL.  Errors as for the GEMM's shape checks. */
 W4_API int w4_gemm_plan(int64_t M, int64_t N, int64_t K, int64_t group_size, int a_dtype, int* path,
-                 int* splitk);
+                        int* splitk, int* tile_m, int* tile_n);
 
 #ifdef __cplusplus
 }

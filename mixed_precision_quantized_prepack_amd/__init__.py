@@ -63,7 +63,7 @@ _SIGNATURES = [
     ("w4_set_option", _int, [ctypes.c_char_p, _i64]),
     ("w4_get_option", _i64, [ctypes.c_char_p]),
     ("w4_gemm_plan", _int, [_i64, _i64, _i64, _i64, _int, ctypes.POINTER(_int),
-                            ctypes.POINTER(_int)]),
+                            ctypes.POINTER(_int), ctypes.POINTER(_int), ctypes.POINTER(_int)]),
 ]
 EXPORTED_SYMBOLS = tuple(n for n, _, _ in _SIGNATURES)
 
@@ -182,9 +182,11 @@ def gemm_workspace_bytes(M: int, N: int, K: int, group_size: int, a_dtype: int) 
 
 
 def gemm_plan(M: int, N: int, K: int, group_size: int, a_dtype: int):
-    p, s = _int(0), _int(0)
-    _check("w4_gemm_plan", lib().w4_gemm_plan(M, N, K, group_size, a_dtype, ctypes.byref(p), ctypes.byref(s)))
-    return p.value, s.value
+    """(path, k_split, tile_m, tile_n) the GEMM would use; path 1 = small-M, 2 = tiled."""
+    p, s, tm, tn = _int(0), _int(0), _int(0), _int(0)
+    _check("w4_gemm_plan", lib().w4_gemm_plan(M, N, K, group_size, a_dtype, ctypes.byref(p), ctypes.byref(s),
+                                              ctypes.byref(tm), ctypes.byref(tn)))
+    return p.value, s.value, tm.value, tn.value
 
 
 def set_option(key: str, value: int):

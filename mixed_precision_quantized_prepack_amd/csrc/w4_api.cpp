@@ -254,7 +254,8 @@ size_t w4_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t group_si
   return workspace_for(plan, M, N);
 }
 
-int w4_gemm_plan(int64_t M, int64_t N, int64_t K, int64_t group_size, int a_dtype, int* path, int* splitk) {
+int w4_gemm_plan(int64_t M, int64_t N, int64_t K, int64_t group_size, int a_dtype, int* path, int* splitk,
+                 int* tile_m, int* tile_n) {
   const int op = op_of(a_dtype);
   if (op < 0) return fail(W4_E_DTYPE, "unknown a_dtype");
   if (int st = check_shape(M, N, K)) return st;
@@ -263,6 +264,8 @@ int w4_gemm_plan(int64_t M, int64_t N, int64_t K, int64_t group_size, int a_dtyp
   if (int st = make_plan(M, N, K, resolve_group(group_size, K) != K, op, &plan)) return st;
   if (path) *path = plan.path;
   if (splitk) *splitk = plan.splitk;
+  if (tile_m) *tile_m = plan.path == PATH_SKINNY ? 16 : plan.bm;
+  if (tile_n) *tile_n = plan.bn;
   return ok();
 }
 

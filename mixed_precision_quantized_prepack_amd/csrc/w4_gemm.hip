@@ -413,12 +413,16 @@ __global__ __launch_bounds__(64 * kSkinnyMaxWaves) void w4_gemm_skinny(GemmArgs 
 //   an out-of-range offset, so the loop has no divergent branches and the
 //   compiler can count the outstanding loads exactly.
 // ===========================================================================
-// Workgroups are dealt round-robin to the 8 XCDs (each with its own L2) in
-// launch order.  Renumber them so that each XCD receives a contiguous range of
-// tiles, with the m-tile index fastest: the workgroups of one XCD that run
-// together share their weight strips (and neighbouring activation tiles) in
-// that XCD's L2.  Any permutation is correct; this one only changes locality.
+// Tile order.  Workgroups are dealt round-robin to the 8 XCDs (each with its
+// own L2) in launch order.  They are renumbered so that each XCD receives a
+// contiguous range of tile numbers t, and t runs through the (m, n) tiles in
+// groups of kGroupM m-tiles: the workgroups one XCD runs together cover a
+// near-square patch of kGroupM m-tiles x (their number / kGroupM) n-tiles, so
+// each activation and weight strip they read is shared through that L2 by
+// several of them.  The K split index is outermost.  Any permutation is
+// correct; this one only changes locality.
 constexpr int kXcds = 8;
+constexpr int kGroupM = 8;
 __device__ __forceinline__ void tile_of_block(int& bx, int& by, int& bz) {
   const int gx = gridDim.x, gy = gridDim.y;
   const int total = gx * gy * gridDim.z;
@@ -426,9 +430,65 @@ __device__ __forceinline__ void tile_of_block(int& bx, int& by, int& bz) {
   const int xcd = b % kXcds, idx = b / kXcds;
   const int per = total / kXcds, rem = total % kXcds;
   const int t = xcd < rem ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
-  bx = t % gx;
-  by = (t / gx) % gy;
   bz = t / (gx * gy);
+  const int mn = t - bz * gx * gy;
+  const int in_group = kGroupM * gy;              // tiles per group of kGroupM m-tiles
+  const int group = mn / in_group;
+  const int first_m = group * kGroupM;
+  const int size_m = gx - first_m < kGroupM ? gx - first_m : kGroupM;
+  const int r = mn - group * in_group;
+  bx = first_m + r % size_m;
+  by = r / size_m;
+}
+
+// LDS layout of an activation tile: rows of 128 k (ROWB bytes), unpadded;
+// 16-byte chunk c of row R is stored in slot c ^ swz(R), where swz depends on
+// R mod 16 only.  A wave's fragment read takes one chunk of 16 consecutive
+// rows; the swizzle makes those 16 chunks cover 64 distinct 4-byte banks, and
+// every 8 of them 32 distinct banks.
+template <int EB>
+__device__ __forceinline__ int lds_swizzle(int row) {
+  return EB == 1 ? ((row & 7) ^ ((row >> 3) & 1)) : (row & 15);
+}
+
+// 16 bytes per lane from a buffer straight into LDS (lane l writes bytes
+// [16 l, 16 l + 16) from the wave-uniform base `lds`).  Kept out of kernel
+// bodies: the host-side pass of a kernel template that calls the builtin
+// directly emits no launch stub.
+__device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t r, uint8_t* lds, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, (int)off, 0, 0, 0);
+}
+
+// Operand words expand_weights produces per block (8-bit: 8, 16-bit: 16).
+template <int OP>
+constexpr int kExpandedWords = OpTraits<OP>::kElemBytes * 8;
+
+// Ties N words to an empty asm statement with a memory clobber: everything
+// that computes them is scheduled before it, every memory access after it.
+template <int N>
+__device__ __forceinline__ void pin_words(uint32_t* e) {
+  static_assert(N % 8 == 0, "pinned in groups of 8");
+#pragma unroll
+  for (int i = 0; i < N; i += 8)
+    asm volatile("" : "+v"(e[i]), "+v"(e[i + 1]), "+v"(e[i + 2]), "+v"(e[i + 3]), "+v"(e[i + 4]),
+                 "+v"(e[i + 5]), "+v"(e[i + 6]), "+v"(e[i + 7])::"memory");
+}
+
+// s_waitcnt immediate (gfx9 encoding): at most `vm` vector-memory operations
+// outstanding, every LDS operation done, export count left free.
+constexpr int waitcnt_vm_lgkm0(int vm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4); }
+
+// Block-wide barrier that first waits until at most VM of this wave's vector
+// memory operations are outstanding.  The direct-to-LDS loads that fill a
+// tile stage are vector memory operations the compiler does not order against
+// LDS reads, so the wait is explicit; the empty asm statements keep every
+// memory access on its side of the barrier.
+template <int VM>
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(VM));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 template <int OP, bool GROUPED, bool FLIP, int NT, int MT, bool SPLIT, bool PARTIALS>
@@ -437,12 +497,14 @@ __global__ __launch_bounds__(256, GROUPED ? 1 : 2) void w4_gemm_tiled(GemmArgs p
   constexpr int EB = OpTraits<OP>::kElemBytes;
   constexpr int AV = act_vecs<OP>();
   constexpr int BM = MT * 16;
-  constexpr int ROWB = 128 * EB;          // bytes of one activation row per K step
-  constexpr int LDSROW = ROWB + 16;       // +16 B pad: the 16 rows one MFMA reads hit distinct banks
-  constexpr int CH_PER_ROW = ROWB / 16;
-  constexpr int CPT = BM * CH_PER_ROW / 256;  // 16-byte chunks per thread per tile
-  static_assert(BM * CH_PER_ROW % 256 == 0, "tile must split evenly over 256 threads");
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2][BM * LDSROW];
+  constexpr int ROWB = 128 * EB;            // bytes of one activation row per K step
+  constexpr int CPR = ROWB / 16;            // 16-byte chunks per row
+  constexpr int RPL = 1024 / ROWB;          // rows filled by one wave-wide 16-byte load
+  constexpr int LPT = BM / (4 * RPL);       // such loads per wave per tile
+  constexpr int STAGE = BM * ROWB;          // bytes of one tile
+  static_assert(BM % (4 * RPL) == 0, "tile rows must split evenly over the 4 waves");
+  static_assert(3 * STAGE <= 65536, "fragment offsets must fit the LDS immediate");
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[3 * STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -470,37 +532,63 @@ __global__ __launch_bounds__(256, GROUPED ? 1 : 2) void w4_gemm_tiled(GemmArgs p
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.s, p.N * p.G * sbytes);
   const __amdgpu_buffer_rsrc_t rz = make_rsrc(p.z, p.z ? p.N * p.G * 2 : 0);
   const int zdt = p.out_dtype;  // W4A16: zero-points in the activation dtype
-  uint32_t a_off[CPT], a_lds[CPT];
-#pragma unroll
-  for (int j = 0; j < CPT; ++j) {
-    const int c = tid + 256 * j;
-    const int row = c / CH_PER_ROW, col = c % CH_PER_ROW;
-    a_off[j] = (uint32_t)(row * p.K * EB + col * 16);
-    a_lds[j] = (uint32_t)(row * LDSROW + col * 16);
-  }
 
-  u32x4 areg[CPT];
-  auto load_a = [&](int kb) {
+  // Load j of this wave fills tile rows [(4 j + wave) RPL, +RPL); lane l
+  // writes LDS bytes [16 l, 16 l + 16) of that range, i.e. row l / CPR, slot
+  // l % CPR, which holds global chunk (l % CPR) ^ swz(row).
+  uint32_t a_off[LPT];
+#pragma unroll
+  for (int j = 0; j < LPT; ++j) {
+    const int row = (4 * j + wave) * RPL + lane / CPR;
+    const int chunk = (lane % CPR) ^ lds_swizzle<EB>(row);
+    a_off[j] = (uint32_t)(row * p.K * EB + chunk * 16);
+  }
+  // Tile of step kb into LDS stage st.  Steps past the range read zeros.
+  auto load_a = [&](int kb, int st) {
     const uint32_t base = kb < kb1 ? (uint32_t)(kb * ROWB) : kOutOfRange;
 #pragma unroll
-    for (int j = 0; j < CPT; ++j) areg[j] = buffer_load16(ra, base + a_off[j]);
+    for (int j = 0; j < LPT; ++j)
+      buffer_load_lds16(ra, lds + st * STAGE + (4 * j + wave) * RPL * ROWB, base + a_off[j]);
   };
-  auto store_a = [&](int buf) {
-#pragma unroll
-    for (int j = 0; j < CPT; ++j) *reinterpret_cast<u32x4*>(&lds[buf][a_lds[j]]) = areg[j];
-  };
-  // weights of step kb (and, for fp16 W4A16, the zero-point of the row each
-  // lane feeds: it is needed before the MFMAs)
-  auto load_w = [&](int kb, u32x4* w, uint32_t* wz) {
+  auto load_w = [&](int kb, u32x4* w) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       const uint32_t off = kb < kb1 ? (uint32_t)(((nt * KB) + kb) * 1024 + lane * 16) : kOutOfRange;
       w[nt] = buffer_load16(rw, off);
-      if constexpr (OP == OP_F16)
-        wz[nt] = load_word(rz, zdt, (uint32_t)(((nb_base + nt) * 16 + r) * p.G + (GROUPED ? kb : 0)),
-                           kb < kb1 && p.z);
     }
   };
+  // Per-step side inputs, loaded one step ahead: group scales and (bf16)
+  // zero-points of the D rows this lane owns, and (fp16 W4A16) the
+  // zero-point of the operand row it feeds.
+  struct Aux {
+    uint32_t sc[NT][4];
+    uint32_t zd[NT][4];
+    uint32_t wz[NT];
+  };
+  auto load_aux = [&](int kb, Aux& x) {
+    if constexpr (GROUPED) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t n = (uint32_t)((nb_base + nt) * 16 + 4 * kq + i);
+          x.sc[nt][i] = load_word(rs, p.s_dtype, n * p.G + kb, !partials && kb < kb1);
+          if constexpr (OP == OP_BF16) x.zd[nt][i] = load_word(rz, zdt, n * p.G + kb, kb < kb1 && p.z);
+        }
+        if constexpr (OP == OP_F16)
+          x.wz[nt] = load_word(rz, zdt, (uint32_t)(((nb_base + nt) * 16 + r) * p.G + kb), kb < kb1 && p.z);
+      }
+    }
+  };
+  // fp16 W4A16 per channel: one zero-point per operand row for all of K.
+  f16x2 nz_fixed[NT];
+  if constexpr (OP == OP_F16 && !GROUPED) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const _Float16 h = (_Float16)(-(1024.0f + zero_point(p, (nb_base + nt) * 16 + r, 0)));
+      nz_fixed[nt] = f16x2{h, h};
+    }
+  }
 
   Acc acc[NT][MT];
   f32x4 tot[NT][MT];
@@ -515,43 +603,46 @@ __global__ __launch_bounds__(256, GROUPED ? 1 : 2) void w4_gemm_tiled(GemmArgs p
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) ones[mt] = f32x4{};
 
-  // One K step on LDS buffer `buf` with weight registers `w`.
-  auto compute = [&](int buf, const u32x4* w, const uint32_t* wz, int kb) {
-    const int g = GROUPED ? kb : 0;
-    // group scales (and bf16 zero-points) of this step: issued first, used
-    // after the MFMAs
-    uint32_t sc[NT][4], zd[NT][4];
-    if constexpr (GROUPED) {
+  // LDS offset of this lane's fragment chunk j in rows r (+ 16 mt).
+  int frag_off[AV];
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint32_t n = (uint32_t)((nb_base + nt) * 16 + 4 * kq + i);
-          sc[nt][i] = load_word(rs, p.s_dtype, n * p.G + g, !partials);
-          if constexpr (OP == OP_BF16) zd[nt][i] = load_word(rz, zdt, n * p.G + g, p.z != nullptr);
-        }
-    }
+  for (int j = 0; j < AV; ++j) frag_off[j] = r * ROWB + (((kq * AV + j) ^ lds_swizzle<EB>(r)) * 16);
+
+  // One K step: expand this step's weights, refill their registers with the
+  // weights of step kb + 2, then run the MFMAs on LDS stage st.
+  auto step = [&](int kb, int st, u32x4* w, const Aux& x) {
     uint32_t e[NT][16];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       f16x2 nz = {};
       if constexpr (OP == OP_F16) {
-        const uint32_t zi = (uint32_t)(((nb_base + nt) * 16 + r) * p.G + g);
-        const _Float16 h = (_Float16)(-(1024.0f + (p.z ? word_to_f32(wz[nt], zdt, zi) : 8.0f)));
-        nz = f16x2{h, h};
+        if constexpr (GROUPED) {
+          const uint32_t zi = (uint32_t)(((nb_base + nt) * 16 + r) * p.G + kb);
+          const _Float16 h = (_Float16)(-(1024.0f + (p.z ? word_to_f32(x.wz[nt], zdt, zi) : 8.0f)));
+          nz = f16x2{h, h};
+        } else {
+          nz = nz_fixed[nt];
+        }
       }
       expand_weights<OP, FLIP>(w[nt], nz, e[nt]);
     }
-    const uint8_t* src = &lds[buf][r * LDSROW + kq * 32 * EB];
+    // Every expanded word exists before the weight registers are refilled:
+    // the old words die here, so the refill reuses their registers and no
+    // copy (and no wait for the refill) is needed at the loop's back edge.
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) pin_words<kExpandedWords<OP>>(e[nt]);
+    load_w(kb + 2, w);
+    asm volatile("" ::: "memory");  // issue the refill before the LDS reads
+    const uint8_t* src = lds + st * STAGE;
     u32x4 af[2][AV];
 #pragma unroll
-    for (int j = 0; j < AV; ++j) af[0][j] = *reinterpret_cast<const u32x4*>(src + 16 * j);
+    for (int j = 0; j < AV; ++j) af[0][j] = *reinterpret_cast<const u32x4*>(src + frag_off[j]);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       if (mt + 1 < MT) {
 #pragma unroll
         for (int j = 0; j < AV; ++j)
-          af[(mt + 1) & 1][j] = *reinterpret_cast<const u32x4*>(src + (mt + 1) * 16 * LDSROW + 16 * j);
+          af[(mt + 1) & 1][j] = *reinterpret_cast<const u32x4*>(src + (mt + 1) * 16 * ROWB + frag_off[j]);
       }
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) block_mma<OP>(e[nt], af[mt & 1], acc[nt][mt]);
@@ -564,9 +655,9 @@ __global__ __launch_bounds__(256, GROUPED ? 1 : 2) void w4_gemm_tiled(GemmArgs p
         float scf[4], zc[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const uint32_t idx = (uint32_t)(n_d + i) * p.G + g;
-          scf[i] = word_to_f32(sc[nt][i], p.s_dtype, idx);
-          zc[i] = (OP == OP_BF16) ? 128.0f + (p.z ? word_to_f32(zd[nt][i], zdt, idx) : 8.0f) : 0.0f;
+          const uint32_t idx = (uint32_t)(n_d + i) * p.G + kb;
+          scf[i] = word_to_f32(x.sc[nt][i], p.s_dtype, idx);
+          zc[i] = (OP == OP_BF16) ? 128.0f + (p.z ? word_to_f32(x.zd[nt][i], zdt, idx) : 8.0f) : 0.0f;
         }
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
@@ -576,7 +667,7 @@ __global__ __launch_bounds__(256, GROUPED ? 1 : 2) void w4_gemm_tiled(GemmArgs p
             if (partials) {
               const int64_t m = m_base + mt * 16 + r;
               if (m < p.M && n_d < p.N && in_window(p, m, n_d + i))
-                store_partial<OP>(p, g, m, n_d + i, pv, int_partial<OP>(acc[nt][mt], i));
+                store_partial<OP>(p, kb, m, n_d + i, pv, int_partial<OP>(acc[nt][mt], i));
             } else {
               tot[nt][mt][i] = fmaf(pv, scf[i], tot[nt][mt][i]);
             }
@@ -589,28 +680,45 @@ __global__ __launch_bounds__(256, GROUPED ? 1 : 2) void w4_gemm_tiled(GemmArgs p
     }
   };
 
+  // Pipeline: step kb computes from LDS stage kb mod 3 while the tiles of
+  // steps kb + 1 and kb + 2 are in flight, and from weight registers that are
+  // refilled with step kb + 2 as soon as they are expanded.  Each step issues
+  // its side inputs, then LPT tile loads, then NT weight loads, so at a
+  // barrier at most LPT + NT operations issued after the tile the next step
+  // reads (those of the previous step) may still be outstanding.
+  constexpr int kAfterTile = LPT + NT;
   u32x4 w0[NT], w1[NT];
-  uint32_t z0[NT], z1[NT];
-  load_a(kb0);
-  load_w(kb0, w0, z0);
-  store_a(0);
-  __syncthreads();
-  load_a(kb0 + 1);
-  load_w(kb0 + 1, w1, z1);
-  for (int kb = kb0;; kb += 2) {
-    compute(0, w0, z0, kb);
-    if (kb + 1 >= kb1) break;
-    store_a(1);
-    __syncthreads();
-    load_a(kb + 2);
-    load_w(kb + 2, w0, z0);
-    compute(1, w1, z1, kb + 1);
-    if (kb + 2 >= kb1) break;
-    store_a(0);
-    __syncthreads();
-    load_a(kb + 3);
-    load_w(kb + 3, w1, z1);
+  Aux x0, x1;
+  // The prologue issues in the loop's order (the compiler's waits at the
+  // loop head must hold for the first entry as well).
+  load_aux(kb0, x0);
+  asm volatile("" ::: "memory");
+  load_a(kb0, 0);
+  load_w(kb0, w0);
+  asm volatile("" ::: "memory");
+  load_a(kb0 + 1, 1);
+  load_w(kb0 + 1, w1);
+  asm volatile("" ::: "memory");
+  // Whole pairs of steps, then an odd last step: a loop without an exit in
+  // its middle, so the compiler's wait analysis sees only the real order.
+  auto phase = [&](int kb, int st, u32x4* w, Aux& cur, Aux& next) {
+    stage_barrier<kAfterTile>();
+    load_aux(kb + 1, next);
+    load_a(kb + 2, st == 0 ? 2 : st - 1);
+    step(kb, st, w, cur);
+  };
+  int st = 0;
+  int kb = kb0;
+  for (int pairs = (kb1 - kb0) >> 1; pairs > 0; --pairs, kb += 2) {
+    phase(kb, st, w0, x0, x1);
+    st = st == 2 ? 0 : st + 1;
+    phase(kb + 1, st, w1, x1, x0);
+    st = st == 2 ? 0 : st + 1;
   }
+  if ((kb1 - kb0) & 1) phase(kb, st, w0, x0, x1);
+  // Drain the loads issued past the last step before the workgroup's LDS is
+  // released.
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
 
   if (GROUPED && partials) return;
   // Epilogue: lane holds rows n_d..n_d+3 of column m for every (nt, mt).
