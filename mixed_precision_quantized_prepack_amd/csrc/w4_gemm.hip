@@ -459,6 +459,10 @@ __device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t r, uint
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, (int)off, 0, 0, 0);
 }
 
+// MFMAs per 16 x 128 weight block (int8: 2, fp8: 1, fp16 / bf16: 4).
+template <int OP>
+constexpr int kMfmaPerBlock = OP == OP_I8 ? 2 : (OP == OP_FP8 ? 1 : 4);
+
 // Operand words expand_weights produces per block (8-bit: 8, 16-bit: 16).
 template <int OP>
 constexpr int kExpandedWords = OpTraits<OP>::kElemBytes * 8;
@@ -611,6 +615,11 @@ __global__ __launch_bounds__(256, GROUPED ? 1 : 2) void w4_gemm_tiled(GemmArgs p
   // One K step: expand this step's weights, refill their registers with the
   // weights of step kb + 2, then run the MFMAs on LDS stage st.
   auto step = [&](int kb, int st, u32x4* w, const Aux& x) {
+    // The weight words enter an asm statement that follows the barrier, so
+    // their expansion (and the wait for their loads) stays in this step
+    // instead of being hoisted into the previous one.
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) asm volatile("" : "+v"(w[nt]));
     uint32_t e[NT][16];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
@@ -634,19 +643,26 @@ __global__ __launch_bounds__(256, GROUPED ? 1 : 2) void w4_gemm_tiled(GemmArgs p
     load_w(kb + 2, w);
     asm volatile("" ::: "memory");  // issue the refill before the LDS reads
     const uint8_t* src = lds + st * STAGE;
-    u32x4 af[2][AV];
+    u32x4 af[MT][AV];
 #pragma unroll
-    for (int j = 0; j < AV; ++j) af[0][j] = *reinterpret_cast<const u32x4*>(src + frag_off[j]);
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int j = 0; j < AV; ++j)
+        af[mt][j] = *reinterpret_cast<const u32x4*>(src + mt * 16 * ROWB + frag_off[j]);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      if (mt + 1 < MT) {
 #pragma unroll
-        for (int j = 0; j < AV; ++j)
-          af[(mt + 1) & 1][j] = *reinterpret_cast<const u32x4*>(src + (mt + 1) * 16 * ROWB + frag_off[j]);
-      }
+      for (int nt = 0; nt < NT; ++nt) block_mma<OP>(e[nt], af[mt], acc[nt][mt]);
+      if constexpr (OP == OP_BF16) ones_mma(af[mt], ones[mt]);
+    }
+    // Issue order: the fragment reads of tile row mt + 2 go out with the
+    // MFMAs of row mt, so each read has two rows of MFMAs to land.
+    constexpr int kMfmaPerRow = NT * kMfmaPerBlock<OP> + (OP == OP_BF16 ? 4 : 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * AV, 0);
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) block_mma<OP>(e[nt], af[mt & 1], acc[nt][mt]);
-      if constexpr (OP == OP_BF16) ones_mma(af[mt & 1], ones[mt]);
+    for (int mt = 0; mt < MT; ++mt) {
+      __builtin_amdgcn_sched_group_barrier(0x008, kMfmaPerRow, 0);
+      if (mt + 2 < MT) __builtin_amdgcn_sched_group_barrier(0x100, AV, 0);
     }
     if constexpr (GROUPED) {
 #pragma unroll
