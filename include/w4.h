@@ -236,8 +236,9 @@ W4_API int w4a16_gemm_partials(const void* a, int a_dtype, const void* b_packed,
  * Tuning / test overrides (process-wide, not synchronised with running
  * calls; set them before issuing work).
  *   "force_path" : 0 = automatic, 1 = small-M kernel, 2 = tiled kernel
- *   "splitk"     : 0 = automatic, else the number of K splits (tiled kernel)
- *                  or waves splitting K (small-M kernel)
+ *   "splitk"     : 0 = automatic, else the number of K splits (tiled kernel,
+ *                  1..64) or waves splitting K (small-M kernel: 1..16 for
+ *                  ungrouped int8 / fp8, 1..8 otherwise)
  *   "skinny_strips": 0 = automatic, 1 or 2 16-column strips per wave of the
  *                  small-M kernel (2 needs N % 32 == 0)
  *   "tiled_bm"   : 0 = automatic, 64 or 128 rows per tile of the tiled kernel

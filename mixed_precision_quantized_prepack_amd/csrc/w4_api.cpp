@@ -128,8 +128,10 @@ int make_plan(int64_t M, int64_t N, int64_t K, bool grouped, int op, GemmPlan* p
       while (s < want && s < 8) s *= 2;
       while (s > 1 && KB / s < 2) s /= 2;
     }
-    if (s < 1 || s > 8 || s > KB)
-      return fail(W4_E_SHAPE, "small-M kernel: %lld K-splitting waves not in [1, min(8, K/128)]", (long long)s);
+    const int smax = skinny_max_waves(op, grouped);
+    if (s < 1 || s > smax || s > KB)
+      return fail(W4_E_SHAPE, "small-M kernel: %lld K-splitting waves not in [1, min(%d, K/128)]", (long long)s,
+                  smax);
     plan->splitk = (int)s;
   } else {
     // 8-bit per-channel problems: 128-row tiles when they give at least two

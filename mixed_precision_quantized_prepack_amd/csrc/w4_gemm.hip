@@ -187,13 +187,12 @@ __device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_
 // ===========================================================================
 // Small-M kernel.
 // ===========================================================================
-constexpr int kSkinnyMaxWaves = 8;
 
 // Blocks per batch of the small-M kernel (8-bit / 16-bit operands) and the
 // cache-policy bits of its weight loads (2 = non-temporal: the weight stream
 // is read once).
 #ifndef W4_SKINNY_U8
-#define W4_SKINNY_U8 4
+#define W4_SKINNY_U8 2
 #endif
 #ifndef W4_SKINNY_U16
 #define W4_SKINNY_U16 2
@@ -233,7 +232,7 @@ __device__ __forceinline__ float word_to_f32(uint32_t w, int dtype, uint32_t i) 
 // out-of-range offsets: they read as zero without memory traffic.  The
 // waves' results are summed through LDS in wave order.
 template <int OP, bool GROUPED, bool FLIP, int NS, bool PARTIALS>
-__global__ __launch_bounds__(64 * kSkinnyMaxWaves) void w4_gemm_skinny(GemmArgs p) {
+__global__ __launch_bounds__(64 * skinny_max_waves(OP, GROUPED)) void w4_gemm_skinny(GemmArgs p, int S) {
   using Acc = typename OpTraits<OP>::Acc;
   constexpr int EB = OpTraits<OP>::kElemBytes;
   constexpr int AV = act_vecs<OP>();
@@ -241,7 +240,6 @@ __global__ __launch_bounds__(64 * kSkinnyMaxWaves) void w4_gemm_skinny(GemmArgs 
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int S = blockDim.x >> 6;
   const int64_t nb0 = (int64_t)blockIdx.x * NS;   // first strip of the workgroup
   const int KB = (int)(p.K >> 7);
   const int r = lane & 15;
@@ -266,6 +264,28 @@ __global__ __launch_bounds__(64 * kSkinnyMaxWaves) void w4_gemm_skinny(GemmArgs 
     acc[j] = Acc{};
     tot[j] = f32x4{};
   }
+  // Epilogue inputs, fetched now so the kernel's tail does not wait on memory:
+  // the element this thread finalises after the reduction (threads below
+  // 256 NS; element t = (strip j, lane l, row i)) and, for bf16 W4A16 per
+  // channel, the zero-points of this lane's D rows.
+  const int ep_j = threadIdx.x >> 8, ep_l = (threadIdx.x >> 2) & 63, ep_i = threadIdx.x & 3;
+  const int64_t ep_m = ep_l & 15;
+  const int64_t ep_n = (nb0 + ep_j) * 16 + 4 * (ep_l >> 4) + ep_i;
+  const bool ep_in = (int)threadIdx.x < 256 * NS && ep_m < p.M && ep_n < p.N;
+  const __amdgpu_buffer_rsrc_t rsa = make_rsrc(p.a_scales, p.a_scales ? p.M * 4 : 0);
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.bias, p.bias ? p.N * 2 : 0);
+  const uint32_t ep_s = load_word(rs, p.s_dtype, (uint32_t)ep_n, !GROUPED && ep_in);
+  const uint32_t ep_a = load_word(rsa, W4_F32, (uint32_t)ep_m, ep_in && p.a_scales);
+  const uint32_t ep_b = load_word(rb, p.out_dtype, (uint32_t)ep_n, ep_in && p.bias);
+  uint32_t zpc[NS][4];
+  if constexpr (OP == OP_BF16 && !GROUPED) {
+#pragma unroll
+    for (int j = 0; j < NS; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        zpc[j][i] = load_word(rz, zdt, (uint32_t)((nb0 + j) * 16 + 4 * kq + i) * p.G, p.z != nullptr);
+  }
+
   u32x4 wv[2][U][NS];
   u32x4 av[2][U][AV];
   uint32_t sc[2][U][NS][4];   // group scales (grouped) for rows n_d + i
@@ -344,7 +364,7 @@ __global__ __launch_bounds__(64 * kSkinnyMaxWaves) void w4_gemm_skinny(GemmArgs 
     }
   };
 
-  const int nbatch = (KB - wave + S - 1) / S;   // K blocks of this wave
+  const int nbatch = wave < S ? (KB - wave + S - 1) / S : 0;   // K blocks of this wave
   load_batch(0, 0);
   for (int kb = 0; kb < nbatch; kb += 2 * U) {
     load_batch(1, kb + U);
@@ -355,7 +375,7 @@ __global__ __launch_bounds__(64 * kSkinnyMaxWaves) void w4_gemm_skinny(GemmArgs 
   }
 
   // Sum the waves' results in wave order through LDS.
-  __shared__ uint32_t red[kSkinnyMaxWaves][NS][64][4];
+  __shared__ uint32_t red[skinny_max_waves(OP, GROUPED)][NS][64][4];
 #pragma unroll
   for (int j = 0; j < NS; ++j) {
     const int64_t n_d = (nb0 + j) * 16 + 4 * kq;
@@ -367,7 +387,9 @@ __global__ __launch_bounds__(64 * kSkinnyMaxWaves) void w4_gemm_skinny(GemmArgs 
       } else if constexpr (OP == OP_I8) {
         bits = (uint32_t)acc[j][i];
       } else {
-        const float zc = (OP == OP_BF16) ? 128.0f + zero_point(p, n_d + i, 0) : 0.0f;
+        float zc = 0.0f;
+        if constexpr (OP == OP_BF16)
+          zc = 128.0f + (p.z ? word_to_f32(zpc[j][i], zdt, (uint32_t)(n_d + i) * p.G) : 8.0f);
         bits = __float_as_uint(partial_value<OP>(acc[j], ones, zc, i));
       }
       red[wave][j][lane][i] = bits;
@@ -375,11 +397,9 @@ __global__ __launch_bounds__(64 * kSkinnyMaxWaves) void w4_gemm_skinny(GemmArgs 
   }
   __syncthreads();
   if (GROUPED && partials) return;
-  for (int t = threadIdx.x; t < 256 * NS; t += blockDim.x) {
-    const int j = t >> 8, l = (t >> 2) & 63, i = t & 3;
-    const int64_t m = l & 15;
-    const int64_t n = (nb0 + j) * 16 + 4 * (l >> 4) + i;
-    if (m >= p.M || n >= p.N) continue;
+  // One output element per thread (the launch provides at least 256 NS).
+  if (ep_in) {
+    const int j = ep_j, l = ep_l, i = ep_i;
     float fv = 0.0f;
     int32_t iv = 0;
     for (int w = 0; w < S; ++w) {
@@ -389,9 +409,18 @@ __global__ __launch_bounds__(64 * kSkinnyMaxWaves) void w4_gemm_skinny(GemmArgs 
         fv += __uint_as_float(red[w][j][l][i]);
     }
     if (partials) {
-      if (in_window(p, m, n)) store_partial<OP>(p, 0, m, n, fv, iv >> 4);
+      if (in_window(p, ep_m, ep_n)) store_partial<OP>(p, 0, ep_m, ep_n, fv, iv >> 4);
     } else {
-      store_out(p, m, n, finalize<OP, GROUPED>(p, m, n, fv, iv));
+      float v;
+      if constexpr (GROUPED) {
+        v = fv;
+      } else {
+        const float sn = word_to_f32(ep_s, p.s_dtype, (uint32_t)ep_n);
+        v = (OP == OP_I8) ? (float)iv * (sn * 0.0625f) : fv * sn;
+      }
+      if (p.a_scales) v *= __uint_as_float(ep_a);
+      if (p.bias) v += word_to_f32(ep_b, p.out_dtype, (uint32_t)ep_n);
+      store_out(p, ep_m, ep_n, v);
     }
   }
 }
@@ -834,22 +863,23 @@ void tiled_tile(int op, bool grouped, int* bm, int* bn) {
 template <int OP, bool GROUPED, bool FLIP>
 static hipError_t launch_typed(const GemmArgs& args, const GemmPlan& plan, hipStream_t stream) {
   if (plan.path == PATH_SKINNY) {
-    const unsigned waves = (unsigned)plan.splitk;
+    // S waves split K; at least 4 NS waves are launched so that every output
+    // element of the workgroup has a thread in the epilogue.
+    const int S = plan.splitk;
+    const int ns = plan.bn / 16;
+    const unsigned threads = 64u * (unsigned)(S > 4 * ns ? S : 4 * ns);
+    const dim3 grid((unsigned)(args.N / plan.bn));
     const bool part = args.mode == MODE_PARTIALS;
-    if (plan.bn == 32) {
+    if (ns == 2) {
       if (part)
-        hipLaunchKernelGGL((w4_gemm_skinny<OP, GROUPED, FLIP, 2, true>), dim3((unsigned)(args.N / 32)),
-                           dim3(64 * waves), 0, stream, args);
+        hipLaunchKernelGGL((w4_gemm_skinny<OP, GROUPED, FLIP, 2, true>), grid, dim3(threads), 0, stream, args, S);
       else
-        hipLaunchKernelGGL((w4_gemm_skinny<OP, GROUPED, FLIP, 2, false>), dim3((unsigned)(args.N / 32)),
-                           dim3(64 * waves), 0, stream, args);
+        hipLaunchKernelGGL((w4_gemm_skinny<OP, GROUPED, FLIP, 2, false>), grid, dim3(threads), 0, stream, args, S);
     } else {
       if (part)
-        hipLaunchKernelGGL((w4_gemm_skinny<OP, GROUPED, FLIP, 1, true>), dim3((unsigned)(args.N / 16)),
-                           dim3(64 * waves), 0, stream, args);
+        hipLaunchKernelGGL((w4_gemm_skinny<OP, GROUPED, FLIP, 1, true>), grid, dim3(threads), 0, stream, args, S);
       else
-        hipLaunchKernelGGL((w4_gemm_skinny<OP, GROUPED, FLIP, 1, false>), dim3((unsigned)(args.N / 16)),
-                           dim3(64 * waves), 0, stream, args);
+        hipLaunchKernelGGL((w4_gemm_skinny<OP, GROUPED, FLIP, 1, false>), grid, dim3(threads), 0, stream, args, S);
     }
     return hipGetLastError();
   }

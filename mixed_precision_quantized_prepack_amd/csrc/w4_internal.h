@@ -31,6 +31,14 @@ struct GemmArgs {
   int64_t m0, m1, n0, n1;  // partials window
 };
 
+// Largest workgroup of the small-M kernel, in waves (each wave takes every
+// S-th K block of the workgroup's strips).  Ungrouped 8-bit problems fit in
+// 128 registers per lane and may use 16 waves; the others keep more state
+// per wave and are limited to 8.
+constexpr int skinny_max_waves(int op, bool grouped) {
+  return (op == OP_I8 || op == OP_FP8) && !grouped ? 16 : 8;
+}
+
 struct GemmPlan {
   int path;    // PATH_SKINNY or PATH_TILED
   int splitk;  // skinny: waves per workgroup splitting K; tiled: K splits across workgroups
