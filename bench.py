@@ -39,6 +39,7 @@ INT8_PEAK_TOPS = 5000.0         # MI355X dense int8 MFMA
 METRIC = "W4A8 GEMM TOPS + weight GB/s (% roofline), N=8192 K=21760, M=1..4096"
 CALIB_BYTES = 256 << 20          # plain copy of known size: reads and writes this many bytes
 TRAFFIC_MD = os.path.join(ROOT, "profiles", "w4a8_i8_pc_8192x21760_hbm_traffic.md")
+STATS_MD = os.path.join(ROOT, "profiles", "w4a8_i8_pc_8192x21760_kernel_stats.md")
 GEMM_SOURCES = ["mixed_precision_quantized_prepack_amd/csrc/w4_gemm.hip",
                 "mixed_precision_quantized_prepack_amd/csrc/w4_device.h",
                 "mixed_precision_quantized_prepack_amd/csrc/w4_api.cpp"]
@@ -174,7 +175,42 @@ def summarize(trace_dir: str, fetch_dir: str, write_dir: str) -> int:
     with open(TRAFFIC_MD, "w") as fh:
         fh.write("\n".join(lines))
     print(TRAFFIC_MD)
+    write_kernel_stats(trace_dir)
     return 0
+
+
+def write_kernel_stats(trace_dir: str) -> None:
+    """Kernel-time summary of the trace run (rocprofv3 --kernel-trace --stats)."""
+    rows = sorted(_read_csv(trace_dir, "kernel_stats.csv"), key=lambda r: -float(r["TotalDurationNs"]))
+    lines = ["# Kernel statistics: W4A8 int8 per-channel, N=8192 K=21760, M sweep {1,16,64,256,1024,4096}", "",
+             "Command (repository root, one MI355X):", "", "```",
+             f"rocprofv3 --kernel-trace --stats --output-format csv -d {trace_dir} -o trace -- "
+             "python -u bench.py --steps 2 --warmup 1 --no-cpu-baseline --calibrate-copy", "```", "",
+             "Each timed step runs the per-token quantisation and the GEMM for every M; the small-M GEMMs "
+             "(M = 1, 16) are also launched 30 times back to back per M for their per-launch time.  "
+             "Durations are per dispatch, from the kernel trace.", "",
+             "| kernel | calls | avg us | min us | max us | % time |", "|---|---|---|---|---|---|"]
+    for r in rows:
+        lines.append(f"| `{_short(r['Name'])[:100]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                     f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
+                     f"{float(r['Percentage']):.2f} |")
+    per_grid = {}
+    for r in _read_csv(trace_dir, "kernel_trace.csv"):
+        k = _short(r["Kernel_Name"])
+        if not k.startswith("w4::w4_gemm"):
+            continue
+        key = (k, int(float(r.get("Grid_Size_X", r.get("Grid_Size", 0)) or 0)))
+        per_grid.setdefault(key, []).append(((int(r["Start_Timestamp"]), int(r["End_Timestamp"]))))
+    lines += ["", "GEMM launches by grid (threads; one grid per M except M = 1 and 16, which share one), in "
+              "launch order (the first belongs to the warm-up step):", "",
+              "| kernel | grid | calls | avg us | per launch us |", "|---|---|---|---|---|"]
+    for (k, g), v in sorted(per_grid.items(), key=lambda kv: kv[0][1]):
+        d = [(e - b) / 1e3 for b, e in sorted(v)]
+        shown = ", ".join(f"{x:.1f}" for x in d[:8]) + (", ..." if len(d) > 8 else "")
+        lines.append(f"| `{k[:100]}` | {g} | {len(d)} | {sum(d) / len(d):.1f} | {shown} |")
+    with open(STATS_MD, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print(STATS_MD)
 
 
 def traffic_for(label: str, Ms) -> "float | None":
@@ -190,8 +226,8 @@ def traffic_for(label: str, Ms) -> "float | None":
         return None
     grids = {M: grid_of(label, M) for M in Ms}
     vals = [v["hbm_bytes_per_launch"] for k, v in data["kernels"].items()
-            if v.get("hbm_bytes_per_launch") and any(k.endswith(f"grid={g}") and kernel_matches(k, label)
-                                                      for g in grids.values())]
+            if v.get("hbm_bytes_per_launch") and kernel_matches(k, label)
+            and ("skinny" in label or any(k.endswith(f"grid={g}") for g in grids.values()))]
     return round(sum(vals) / len(vals)) if vals else None
 
 
