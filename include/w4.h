@@ -242,7 +242,7 @@ W4_API int w4a16_gemm_partials(const void* a, int a_dtype, const void* b_packed,
  *   "skinny_strips": 0 = automatic, 1 or 2 16-column strips per wave of the
  *                  small-M kernel (2 needs N % 32 == 0)
  *   "tiled_bm"   : 0 = automatic, 64 or 128 rows per tile of the tiled kernel
- *                  (128 only for int8 / fp8 per-channel problems)
+ *                  (128 only for int8 per-channel problems)
  * Returns W4_OK, or W4_E_UNSUPPORTED for an unknown key / W4_E_SHAPE for an
  * out-of-range value.
  * ------------------------------------------------------------------------- */

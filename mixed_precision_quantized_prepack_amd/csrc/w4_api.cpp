@@ -134,9 +134,9 @@ int make_plan(int64_t M, int64_t N, int64_t K, bool grouped, int op, GemmPlan* p
                   smax);
     plan->splitk = (int)s;
   } else {
-    // 8-bit per-channel problems: 128-row tiles when they give at least two
+    // int8 per-channel problems: 128-row tiles when they give at least two
     // workgroups per CU, 64-row tiles otherwise
-    const bool tall_ok = (op == OP_I8 || op == OP_FP8) && !grouped;
+    const bool tall_ok = op == OP_I8 && !grouped;
     const int64_t fbm = g_tiled_bm.load();
     if (tall_ok) {
       const int64_t tiles128 = ((M + 127) / 128) * ((N + plan->bn - 1) / plan->bn);
@@ -149,7 +149,7 @@ int make_plan(int64_t M, int64_t N, int64_t K, bool grouped, int op, GemmPlan* p
       s = fs;
     } else {
       const int64_t tiles = ((M + plan->bm - 1) / plan->bm) * ((N + plan->bn - 1) / plan->bn);
-      const int64_t slots = (tall_ok ? 2LL : 1LL) * cu;   // resident workgroups
+      const int64_t slots = 2LL * cu;   // resident workgroups (two per CU)
       s = 1;
       while (tiles * s < slots && s * 2 <= 8 && KB / (s * 2) >= 4) s *= 2;
     }

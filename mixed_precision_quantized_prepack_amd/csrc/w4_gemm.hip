@@ -525,7 +525,7 @@ __device__ __forceinline__ void stage_barrier() {
 }
 
 template <int OP, bool GROUPED, bool FLIP, int NT, int MT, bool SPLIT, bool PARTIALS>
-__global__ __launch_bounds__(256, GROUPED ? 1 : 2) void w4_gemm_tiled(GemmArgs p, int splitk) {
+__global__ __launch_bounds__(256, 2) void w4_gemm_tiled(GemmArgs p, int splitk) {
   using Acc = typename OpTraits<OP>::Acc;
   constexpr int EB = OpTraits<OP>::kElemBytes;
   constexpr int AV = act_vecs<OP>();
@@ -537,7 +537,17 @@ __global__ __launch_bounds__(256, GROUPED ? 1 : 2) void w4_gemm_tiled(GemmArgs p
   constexpr int STAGE = BM * ROWB;          // bytes of one tile
   static_assert(BM % (4 * RPL) == 0, "tile rows must split evenly over the 4 waves");
   static_assert(3 * STAGE <= 65536, "fragment offsets must fit the LDS immediate");
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[3 * STAGE];
+  // Grouped problems also keep a two-slot table of column scales (and, bf16
+  // W4A16, of 128 + z) after the three tile stages.  One LDS array holds
+  // everything: a second array would give LDS accesses alias scopes, and the
+  // compiler would then order the fragment reads after the in-flight tile
+  // loads of later stages.
+  constexpr bool kFold = GROUPED && !PARTIALS;
+  constexpr int BNW = 4 * NT * 16;   // columns of the workgroup
+  constexpr int kTables = kFold ? (OP == OP_BF16 ? 2 : 1) : 0;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[3 * STAGE + kTables * 2 * BNW * 4];
+  float* const gsc = reinterpret_cast<float*>(lds + 3 * STAGE);   // [2][BNW]
+  float* const gzc = gsc + 2 * BNW;                               // [2][BNW]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -602,11 +612,12 @@ __global__ __launch_bounds__(256, GROUPED ? 1 : 2) void w4_gemm_tiled(GemmArgs p
     if constexpr (GROUPED) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
+        if constexpr (PARTIALS && OP == OP_BF16) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint32_t n = (uint32_t)((nb_base + nt) * 16 + 4 * kq + i);
-          x.sc[nt][i] = load_word(rs, p.s_dtype, n * p.G + kb, !partials && kb < kb1);
-          if constexpr (OP == OP_BF16) x.zd[nt][i] = load_word(rz, zdt, n * p.G + kb, kb < kb1 && p.z);
+          for (int i = 0; i < 4; ++i) {
+            const uint32_t n = (uint32_t)((nb_base + nt) * 16 + 4 * kq + i);
+            x.zd[nt][i] = load_word(rz, zdt, n * p.G + kb, kb < kb1 && p.z);
+          }
         }
         if constexpr (OP == OP_F16)
           x.wz[nt] = load_word(rz, zdt, (uint32_t)(((nb_base + nt) * 16 + r) * p.G + kb), kb < kb1 && p.z);
@@ -640,6 +651,33 @@ __global__ __launch_bounds__(256, GROUPED ? 1 : 2) void w4_gemm_tiled(GemmArgs p
   int frag_off[AV];
 #pragma unroll
   for (int j = 0; j < AV; ++j) frag_off[j] = r * ROWB + (((kq * AV + j) ^ lds_swizzle<EB>(r)) * 16);
+
+  // Grouped problems fold each group's dot products into fp32 totals with the
+  // group scale.  The scales (and bf16 zero-point terms 128 + z) of the
+  // workgroup's BN columns are converted once per column and step by one
+  // thread each into the two-slot LDS table (slot (kb - kb0) & 1), written
+  // one step ahead; a lane then reads its four rows' values with one 16-byte
+  // LDS read per n-block.  int8 scales carry the 1/16 of the 16 w operand.
+  const int col = tid % BNW;
+  const uint32_t col_n = (uint32_t)((int64_t)by * BNW + col);
+  uint32_t col_sw = 0, col_zw = 0;   // raw words of the column for the step being prefetched
+  auto load_col = [&](int kb) {
+    if constexpr (kFold) {
+      const uint32_t idx = col_n * (uint32_t)p.G + (uint32_t)kb;
+      col_sw = load_word(rs, p.s_dtype, idx, kb < kb1 && col_n < (uint32_t)p.N);
+      if constexpr (OP == OP_BF16) col_zw = load_word(rz, zdt, idx, kb < kb1 && p.z && col_n < (uint32_t)p.N);
+    }
+  };
+  auto store_col = [&](int kb) {
+    if constexpr (kFold) {
+      const uint32_t idx = col_n * (uint32_t)p.G + (uint32_t)kb;
+      const int slot = (kb - kb0) & 1;
+      float sv = word_to_f32(col_sw, p.s_dtype, idx);
+      if constexpr (OP == OP_I8) sv *= 0.0625f;
+      gsc[slot * BNW + col] = sv;
+      if constexpr (OP == OP_BF16) gzc[slot * BNW + col] = 128.0f + (p.z ? word_to_f32(col_zw, zdt, idx) : 8.0f);
+    }
+  };
 
   // One K step: expand this step's weights, refill their registers with the
   // weights of step kb + 2, then run the MFMAs on LDS stage st.
@@ -678,44 +716,100 @@ __global__ __launch_bounds__(256, GROUPED ? 1 : 2) void w4_gemm_tiled(GemmArgs p
 #pragma unroll
       for (int j = 0; j < AV; ++j)
         af[mt][j] = *reinterpret_cast<const u32x4*>(src + mt * 16 * ROWB + frag_off[j]);
+    if constexpr (kFold) {
+      // This group's scales (and bf16 128 + z terms) for the lane's D rows.
+      const int slot = (kb - kb0) & 1;
+      f32x4 scv[NT], zcv[NT];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
+      for (int nt = 0; nt < NT; ++nt) {
+        scv[nt] = *reinterpret_cast<const f32x4*>(&gsc[slot * BNW + (wave * NT + nt) * 16 + 4 * kq]);
+        if constexpr (OP == OP_BF16)
+          zcv[nt] = *reinterpret_cast<const f32x4*>(&gzc[slot * BNW + (wave * NT + nt) * 16 + 4 * kq]);
+      }
+      // Row mt's MFMAs start from zero; row mt - 1 is folded while they run.
+      auto fold_row = [&](int mt) {
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) block_mma<OP>(e[nt], af[mt], acc[nt][mt]);
-      if constexpr (OP == OP_BF16) ones_mma(af[mt], ones[mt]);
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float pv;
+            if constexpr (OP == OP_I8)
+              pv = (float)acc[nt][mt][i];
+            else if constexpr (OP == OP_BF16)
+              pv = fmaf(-zcv[nt][i], ones[mt][i], acc[nt][mt][i]);
+            else
+              pv = acc[nt][mt][i];
+            tot[nt][mt][i] = fmaf(pv, scv[nt][i], tot[nt][mt][i]);
+          }
+      };
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          Acc t = Acc{};
+          block_mma<OP>(e[nt], af[mt], t);
+          acc[nt][mt] = t;
+        }
+        if constexpr (OP == OP_BF16) {
+          f32x4 o = f32x4{};
+          ones_mma(af[mt], o);
+          ones[mt] = o;
+        }
+        if (mt > 0) fold_row(mt - 1);
+      }
+      fold_row(MT - 1);
+      // Issue order: scale-table and fragment reads first, then per tile row
+      // one MFMA at a time with part of the previous row's fold between them;
+      // the fragment reads of row mt + 2 go out with the MFMAs of row mt.
+      constexpr int kMfmaPerRow = NT * kMfmaPerBlock<OP> + (OP == OP_BF16 ? 4 : 0);
+      constexpr int kFoldPerRow = NT * 4 * (OP == OP_I8 || OP == OP_BF16 ? 2 : 1);
+      constexpr int kValuPerMfma = (kFoldPerRow + kMfmaPerRow - 1) / kMfmaPerRow;
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * AV + NT * (OP == OP_BF16 ? 2 : 1), 0);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+        for (int q = 0; q < kMfmaPerRow; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if (mt > 0) __builtin_amdgcn_sched_group_barrier(0x002, kValuPerMfma, 0);
+        }
+        if (mt + 2 < MT) __builtin_amdgcn_sched_group_barrier(0x100, AV, 0);
+      }
+    } else {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) block_mma<OP>(e[nt], af[mt], acc[nt][mt]);
+        if constexpr (OP == OP_BF16) ones_mma(af[mt], ones[mt]);
+      }
+      // Issue order: the fragment reads of tile row mt + 2 go out with the
+      // MFMAs of row mt, so each read has two rows of MFMAs to land.
+      constexpr int kMfmaPerRow = NT * kMfmaPerBlock<OP> + (OP == OP_BF16 ? 4 : 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * AV, 0);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        __builtin_amdgcn_sched_group_barrier(0x008, kMfmaPerRow, 0);
+        if (mt + 2 < MT) __builtin_amdgcn_sched_group_barrier(0x100, AV, 0);
+      }
     }
-    // Issue order: the fragment reads of tile row mt + 2 go out with the
-    // MFMAs of row mt, so each read has two rows of MFMAs to land.
-    constexpr int kMfmaPerRow = NT * kMfmaPerBlock<OP> + (OP == OP_BF16 ? 4 : 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 2 * AV, 0);
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      __builtin_amdgcn_sched_group_barrier(0x008, kMfmaPerRow, 0);
-      if (mt + 2 < MT) __builtin_amdgcn_sched_group_barrier(0x100, AV, 0);
-    }
-    if constexpr (GROUPED) {
+    if constexpr (GROUPED && PARTIALS) {
+      // verification mode: store each group's dot products
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         const int64_t n_d = (nb_base + nt) * 16 + 4 * kq;
-        float scf[4], zc[4];
+        float zc[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const uint32_t idx = (uint32_t)(n_d + i) * p.G + kb;
-          scf[i] = word_to_f32(x.sc[nt][i], p.s_dtype, idx);
           zc[i] = (OP == OP_BF16) ? 128.0f + (p.z ? word_to_f32(x.zd[nt][i], zdt, idx) : 8.0f) : 0.0f;
         }
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
+          const int64_t m = m_base + mt * 16 + r;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const float pv = partial_value<OP>(acc[nt][mt], ones[mt], zc[i], i);
-            if (partials) {
-              const int64_t m = m_base + mt * 16 + r;
-              if (m < p.M && n_d < p.N && in_window(p, m, n_d + i))
-                store_partial<OP>(p, kb, m, n_d + i, pv, int_partial<OP>(acc[nt][mt], i));
-            } else {
-              tot[nt][mt][i] = fmaf(pv, scf[i], tot[nt][mt][i]);
-            }
+            if (m < p.M && n_d < p.N && in_window(p, m, n_d + i))
+              store_partial<OP>(p, kb, m, n_d + i, pv, int_partial<OP>(acc[nt][mt], i));
           }
           acc[nt][mt] = Acc{};
         }
@@ -728,14 +822,18 @@ __global__ __launch_bounds__(256, GROUPED ? 1 : 2) void w4_gemm_tiled(GemmArgs p
   // Pipeline: step kb computes from LDS stage kb mod 3 while the tiles of
   // steps kb + 1 and kb + 2 are in flight, and from weight registers that are
   // refilled with step kb + 2 as soon as they are expanded.  Each step issues
-  // its side inputs, then LPT tile loads, then NT weight loads, so at a
-  // barrier at most LPT + NT operations issued after the tile the next step
-  // reads (those of the previous step) may still be outstanding.
+  // its side inputs (column scales two steps ahead, per-lane values one step
+  // ahead), then LPT tile loads, then NT weight loads, so at a barrier at most
+  // LPT + NT operations issued after the tile the next step reads (those of
+  // the previous step) may still be outstanding.
   constexpr int kAfterTile = LPT + NT;
   u32x4 w0[NT], w1[NT];
   Aux x0, x1;
   // The prologue issues in the loop's order (the compiler's waits at the
   // loop head must hold for the first entry as well).
+  load_col(kb0);
+  store_col(kb0);
+  load_col(kb0 + 1);
   load_aux(kb0, x0);
   asm volatile("" ::: "memory");
   load_a(kb0, 0);
@@ -748,6 +846,8 @@ __global__ __launch_bounds__(256, GROUPED ? 1 : 2) void w4_gemm_tiled(GemmArgs p
   // its middle, so the compiler's wait analysis sees only the real order.
   auto phase = [&](int kb, int st, u32x4* w, Aux& cur, Aux& next) {
     stage_barrier<kAfterTile>();
+    store_col(kb + 1);
+    load_col(kb + 2);
     load_aux(kb + 1, next);
     load_a(kb + 2, st == 0 ? 2 : st - 1);
     step(kb, st, w, cur);
@@ -850,9 +950,9 @@ __global__ __launch_bounds__(256) void w4_splitk_reduce(GemmArgs p, int splitk) 
 // Host-side launchers.
 // ===========================================================================
 void tiled_tile(int op, bool grouped, int* bm, int* bn) {
-  // default (tallest) tile; 8-bit per-channel problems may also use bm = 64
+  // default (tallest) tile; int8 per-channel problems may also use bm = 64
   if (op == OP_I8 || op == OP_FP8) {
-    *bm = grouped ? 64 : 128;
+    *bm = (op == OP_I8 && !grouped) ? 128 : 64;
     *bn = 256;
   } else {
     *bm = 64;
@@ -919,7 +1019,7 @@ static hipError_t launch_typed(const GemmArgs& args, const GemmPlan& plan, hipSt
                            args, 1);
     }
   };
-  if constexpr (kByte && !GROUPED) {
+  if constexpr (OP == OP_I8 && !GROUPED) {
     if (plan.bm == 128) {
       launch(std::integral_constant<int, 8>{});
       return finish();
