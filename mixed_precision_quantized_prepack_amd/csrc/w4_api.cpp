@@ -108,9 +108,12 @@ int make_plan(int64_t M, int64_t N, int64_t K, bool grouped, int op, GemmPlan* p
   tiled_tile(op, grouped, &plan->bm, &plan->bn);
   if (plan->path == PATH_SKINNY) {
     if (M > 16) return fail(W4_E_UNSUPPORTED, "the small-M kernel handles M <= 16 (M=%lld)", (long long)M);
-    // strips of 16 columns per wave: two strips share one activation fragment
+    // strips of 16 columns per wave: two strips share one activation
+    // fragment.  Grouped problems take two only when the fragment is worth
+    // sharing (M >= 8) and N leaves enough workgroups.
     const int64_t fns = g_skinny_strips.load();
-    const int64_t ns = fns ? fns : ((!grouped && N % 32 == 0) ? 2 : 1);
+    const bool two = N % 32 == 0 && (!grouped || (M >= 8 && N >= 8192));
+    const int64_t ns = fns ? fns : (two ? 2 : 1);
     if (N % (16 * ns))
       return fail(W4_E_SHAPE, "small-M kernel with %lld strips per wave needs N %% %lld == 0", (long long)ns,
                   (long long)(16 * ns));
@@ -119,14 +122,13 @@ int make_plan(int64_t M, int64_t N, int64_t K, bool grouped, int op, GemmPlan* p
     if (fs) {
       s = fs;
     } else {
-      // ~16 resident waves per CU; grouped problems hold more registers per
-      // wave (prefetched scales), so fewer fit and fewer are asked for
+      // ~16 resident waves per CU, each with at least 8 K blocks (shorter
+      // waves spend most of their time waiting for their first loads)
       const int64_t groups = N / (16 * ns);
-      const int64_t per_cu = grouped ? 8 : 16;
-      const int64_t want = (per_cu * cu + groups - 1) / groups;
+      const int64_t want = (16 * cu + groups - 1) / groups;
       s = 1;
       while (s < want && s < 8) s *= 2;
-      while (s > 1 && KB / s < 2) s /= 2;
+      while (s > 1 && KB / s < 8) s /= 2;
     }
     const int smax = skinny_max_waves(op, grouped);
     if (s < 1 || s > smax || s > KB)

@@ -288,9 +288,12 @@ __global__ __launch_bounds__(64 * skinny_max_waves(OP, GROUPED)) void w4_gemm_sk
 
   u32x4 wv[2][U][NS];
   u32x4 av[2][U][AV];
-  uint32_t sc[2][U][NS][4];   // group scales (grouped) for rows n_d + i
-  uint32_t zd[2][U][NS][4];   // zero-points for rows n_d + i (bf16 W4A16)
-  uint32_t zo[2][U][NS];      // zero-point for row n_op (fp16 W4A16)
+  // Per-group side inputs, one word per lane for its operand row r (the D
+  // rows 4 kq + i a lane folds get theirs from lanes 4 kq + i by a lane
+  // permute): group scale, bf16 W4A16 zero-point, fp16 W4A16 zero-point.
+  uint32_t sc[2][U][NS];
+  uint32_t zd[2][U][NS];
+  uint32_t zo[2][U][NS];
 
   auto load_batch = [&](int buf, int kb) {   // kb: this wave's batch index in blocks of S
 #pragma unroll
@@ -307,17 +310,10 @@ __global__ __launch_bounds__(64 * skinny_max_waves(OP, GROUPED)) void w4_gemm_sk
       const int g = GROUPED ? k : 0;
 #pragma unroll
       for (int j = 0; j < NS; ++j) {
-        const uint32_t nd = (uint32_t)((nb0 + j) * 16 + 4 * kq);
-        if constexpr (GROUPED) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) sc[buf][u][j][i] = load_word(rs, p.s_dtype, (nd + i) * p.G + g, in && !partials);
-        }
-        if constexpr (OP == OP_BF16) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) zd[buf][u][j][i] = load_word(rz, zdt, (nd + i) * p.G + g, in && p.z);
-        }
-        if constexpr (OP == OP_F16)
-          zo[buf][u][j] = load_word(rz, zdt, (uint32_t)((nb0 + j) * 16 + r) * p.G + g, in && p.z);
+        const uint32_t idx = (uint32_t)((nb0 + j) * 16 + r) * p.G + g;
+        if constexpr (GROUPED) sc[buf][u][j] = load_word(rs, p.s_dtype, idx, in && !partials);
+        if constexpr (GROUPED && OP == OP_BF16) zd[buf][u][j] = load_word(rz, zdt, idx, in && p.z);
+        if constexpr (OP == OP_F16) zo[buf][u][j] = load_word(rz, zdt, idx, in && p.z);
       }
     }
   };
@@ -344,15 +340,25 @@ __global__ __launch_bounds__(64 * skinny_max_waves(OP, GROUPED)) void w4_gemm_sk
 #pragma unroll
           for (int j = 0; j < NS; ++j) {
             const int64_t n_d = (nb0 + j) * 16 + 4 * kq;
+            // this lane's row r values, then those of D rows 4 kq + i
+            const uint32_t idx = (uint32_t)((nb0 + j) * 16 + r) * p.G + g;
+            float sv = word_to_f32(sc[buf][u][j], p.s_dtype, idx);
+            if constexpr (OP == OP_I8) sv *= 0.0625f;   // the operand holds 16 w
+            float zv = 0.0f;
+            if constexpr (OP == OP_BF16) zv = 128.0f + (p.z ? word_to_f32(zd[buf][u][j], zdt, idx) : 8.0f);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              const uint32_t idx = (uint32_t)(n_d + i) * p.G + g;
-              const float zc = (OP == OP_BF16) ? 128.0f + (p.z ? word_to_f32(zd[buf][u][j][i], zdt, idx) : 8.0f) : 0.0f;
+              const int src = (4 * kq + i) * 4;   // byte address of lane 4 kq + i
+              const float zc = (OP == OP_BF16)
+                                   ? __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(zv)))
+                                   : 0.0f;
               const float pv = partial_value<OP>(acc[j], ones, zc, i);
               if (partials) {
                 if (in_window(p, r, n_d + i)) store_partial<OP>(p, g, r, n_d + i, pv, int_partial<OP>(acc[j], i));
               } else {
-                tot[j][i] = fmaf(pv, word_to_f32(sc[buf][u][j][i], p.s_dtype, idx), tot[j][i]);
+                const float si = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(sv)));
+                const float pf = (OP == OP_I8) ? (float)acc[j][i] : pv;
+                tot[j][i] = fmaf(pf, si, tot[j][i]);
               }
             }
           }
