@@ -129,7 +129,7 @@ W4_API int w4_prepack_B(const void* w_logical, void* w_packed, int64_t N, int64_
  * x       : device, [M][K] of x_dtype (W4_F16 or W4_BF16); finite values.
  * xq      : device, [M][K] of q_dtype (W4_I8, or W4_FP8_E4M3 as raw bytes).
  * scales  : device, [M] fp32.
- * Requires K > 0, K % 8 == 0, M >= 0.  Errors: W4_E_NULL, W4_E_SHAPE,
+ * Requires 0 < K <= 2^29, K % 8 == 0, M >= 0.  Errors: W4_E_NULL, W4_E_SHAPE,
  * W4_E_DTYPE, W4_E_ALIGN, W4_E_HIP.
  * ------------------------------------------------------------------------- */
 W4_API int w4_quant_act_per_token(const void* x, int x_dtype, void* xq, int q_dtype, float* scales,

@@ -237,8 +237,9 @@ int w4_quant_act_per_token(const void* x, int x_dtype, void* xq, int q_dtype, fl
   if (x_dtype != W4_F16 && x_dtype != W4_BF16) return fail(W4_E_DTYPE, "x_dtype must be W4_F16 or W4_BF16");
   if (q_dtype != W4_I8 && q_dtype != W4_FP8_E4M3)
     return fail(W4_E_DTYPE, "q_dtype must be W4_I8 or W4_FP8_E4M3");
-  if (M < 0 || K <= 0 || K % 8 || M > ((int64_t)1 << 31) - 1 || K > ((int64_t)1 << 30))
-    return fail(W4_E_SHAPE, "need M >= 0, 0 < K <= 2^30, K %% 8 == 0 (M=%lld K=%lld)", (long long)M,
+  // a row is addressed with 32-bit buffer offsets: at most 2^29 elements
+  if (M < 0 || K <= 0 || K % 8 || M > ((int64_t)1 << 31) - 1 || K > ((int64_t)1 << 29))
+    return fail(W4_E_SHAPE, "need M >= 0, 0 < K <= 2^29, K %% 8 == 0 (M=%lld K=%lld)", (long long)M,
                 (long long)K);
   if (M == 0) return ok();
   if (!x || !xq || !scales) return fail(W4_E_NULL, "x, xq and scales are required");

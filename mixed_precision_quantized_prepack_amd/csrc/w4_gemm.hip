@@ -919,20 +919,27 @@ __global__ __launch_bounds__(256, 2) void w4_gemm_tiled(GemmArgs p, int splitk) 
 }
 
 // Sum the split-K slots of the tiled kernel in split order, then the epilogue.
+// A thread owns four consecutive columns of one row; the slots are loaded
+// eight at a time (all in flight together; slots past the last read zero)
+// and added in slot order.
 template <int OP, bool GROUPED>
 __global__ __launch_bounds__(256) void w4_splitk_reduce(GemmArgs p, int splitk) {
   const int64_t quads = p.N >> 2;
   const int64_t total = p.M * quads;
   const bool partials = p.mode == MODE_PARTIALS;
+  const int64_t slot_words = p.M * p.N;
+  // the workspace as a buffer: offsets are per slot, so any M * N * 4 below
+  // the descriptor limit works; larger problems use plain loads
+  const bool use_rsrc = slot_words * 4 * splitk < 0x7FFFFFF0LL;
+  const __amdgpu_buffer_rsrc_t rws = make_rsrc(p.ws, use_rsrc ? slot_words * 4 * splitk : 0);
   for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total;
        t += (int64_t)gridDim.x * blockDim.x) {
     const int64_t m = t / quads;
     const int64_t n = (t - m * quads) * 4;
-    const uint32_t* src = static_cast<const uint32_t*>(p.ws) + m * p.N + n;
+    const int64_t base = m * p.N + n;   // word index in slot 0
     float fv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     int32_t iv[4] = {0, 0, 0, 0};
-    for (int s = 0; s < splitk; ++s) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(src + (int64_t)s * p.M * p.N);
+    auto add = [&](const u32x4& v) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         if (!GROUPED && OP == OP_I8)
@@ -940,14 +947,34 @@ __global__ __launch_bounds__(256) void w4_splitk_reduce(GemmArgs p, int splitk) 
         else
           fv[i] += __uint_as_float(v[i]);
       }
+    };
+    if (use_rsrc) {
+      for (int s0 = 0; s0 < splitk; s0 += 8) {
+        u32x4 v[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+          v[q] = buffer_load16(rws, s0 + q < splitk ? (uint32_t)(((s0 + q) * slot_words + base) * 4) : kOutOfRange);
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+          if (s0 + q < splitk) add(v[q]);
+      }
+    } else {
+      for (int s = 0; s < splitk; ++s)
+        add(*reinterpret_cast<const u32x4*>(static_cast<const uint32_t*>(p.ws) + s * slot_words + base));
     }
     if (partials) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         if (in_window(p, m, n + i)) store_partial<OP>(p, 0, m, n + i, fv[i], iv[i] >> 4);
     } else {
+      uint16_t o[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) store_out(p, m, n + i, finalize<OP, GROUPED>(p, m, n + i, fv[i], iv[i]));
+      for (int i = 0; i < 4; ++i) {
+        const float v = finalize<OP, GROUPED>(p, m, n + i, fv[i], iv[i]);
+        o[i] = p.out_dtype == W4_F16 ? f32_to_f16_bits(v) : f32_to_bf16_bits(v);
+      }
+      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + m * p.N + n) =
+          make_uint2((uint32_t)o[0] | ((uint32_t)o[1] << 16), (uint32_t)o[2] | ((uint32_t)o[3] << 16));
     }
   }
 }

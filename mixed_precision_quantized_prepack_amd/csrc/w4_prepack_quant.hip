@@ -80,7 +80,7 @@ hipError_t launch_prepack(const void* w_logical, void* w_packed, int64_t N, int6
 // the row's absolute maximum.
 //
 // One workgroup per row (256 threads, or 1024 when there are few rows so that
-// a single row is not latency bound).  Each thread keeps up to kChunks
+// a single row is not latency bound).  Each thread keeps up to kMaxChunks
 // 16-byte chunks (8 elements) of the row in registers, so the row is read from
 // HBM once: pass 1 takes the absolute maximum, a wave reduction plus an LDS
 // exchange gives the row maximum, pass 2 forms the quotients and stores the
@@ -94,7 +94,10 @@ hipError_t launch_prepack(const void* w_logical, void* w_packed, int64_t N, int6
 // is too small for that (bf16 inputs near the bottom of the exponent range)
 // use the plain division.
 // ---------------------------------------------------------------------------
-constexpr int kChunks = 12;
+// Chunks a thread keeps in registers: the launch picks the smallest of
+// 4, 8 or 12 that covers the row (a chunk slot past the row still costs an
+// address-pipeline pass, which matters when few rows share a CU).
+constexpr int kMaxChunks = 12;
 
 template <int XT>
 __device__ __forceinline__ float elem(const uint4& v, int j) {
@@ -152,28 +155,41 @@ __device__ __forceinline__ uint2 quant_chunk(const uint4& v, float s, float y) {
   return make_uint2(out[0], out[1]);
 }
 
-template <int XT, int QT, int THREADS>
+// The row's chunks are read and written with buffer operations: chunk
+// indices past the row get an out-of-range offset, which loads zeros (no
+// effect on the maximum) and drops the store, so no load or store sits in a
+// branch (a branch around a load makes the compiler wait for it on the spot).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+constexpr uint32_t kRowOutOfRange = 0x80000000u;
+
+template <int XT, int QT, int THREADS, int CH>
 __global__ __launch_bounds__(THREADS) void w4_quant_kernel(const uint16_t* __restrict__ x,
                                                            uint8_t* __restrict__ xq,
                                                            float* __restrict__ scales, int64_t K) {
   const int64_t row = blockIdx.x;
   const int tid = threadIdx.x;
-  const uint4* xr = reinterpret_cast<const uint4*>(x + row * K);
-  uint2* qr = reinterpret_cast<uint2*>(xq + row * K);
   const int nchunks = (int)(K / 8);
+  const __amdgpu_buffer_rsrc_t rx = row_rsrc(x + row * K, K * 2);
+  const __amdgpu_buffer_rsrc_t rq = row_rsrc(xq + row * K, K);
+  auto load = [&](int idx) -> uint4 {
+    const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(
+        rx, (int)(idx < nchunks ? (uint32_t)idx * 16u : kRowOutOfRange), 0, 0);
+    return make_uint4(w.x, w.y, w.z, w.w);
+  };
+  auto store = [&](int idx, uint2 q) {
+    __builtin_amdgcn_raw_buffer_store_b64(u32x2{q.x, q.y}, rq,
+                                          (int)(idx < nchunks ? (uint32_t)idx * 8u : kRowOutOfRange), 0, 0);
+  };
 
-  uint4 v[kChunks];
+  uint4 v[CH];
   float amax = 0.0f;
 #pragma unroll
-  for (int c = 0; c < kChunks; ++c) {
-    const int idx = c * THREADS + tid;
-    if (idx < nchunks) {
-      v[c] = xr[idx];
-      amax = chunk_absmax<XT>(amax, v[c]);
-    }
-  }
-  for (int idx = kChunks * THREADS + tid; idx < nchunks; idx += THREADS)
-    amax = chunk_absmax<XT>(amax, xr[idx]);
+  for (int c = 0; c < CH; ++c) v[c] = load(c * THREADS + tid);
+#pragma unroll
+  for (int c = 0; c < CH; ++c) amax = chunk_absmax<XT>(amax, v[c]);
+  for (int idx = CH * THREADS + tid; idx < nchunks; idx += THREADS) amax = chunk_absmax<XT>(amax, load(idx));
 
   // row maximum: wave butterfly, then one value per wave through LDS
 #pragma unroll
@@ -189,53 +205,60 @@ __global__ __launch_bounds__(THREADS) void w4_quant_kernel(const uint16_t* __res
   const float s = amax / qmax;
   if (tid == 0) scales[row] = s;
   if (s == 0.0f) {
-    for (int idx = tid; idx < nchunks; idx += THREADS) qr[idx] = make_uint2(0u, 0u);
+    for (int idx = tid; idx < nchunks; idx += THREADS) store(idx, make_uint2(0u, 0u));
     return;
   }
   const float y = 1.0f / s;
   if (s >= 0x1p-100f) {
 #pragma unroll
-    for (int c = 0; c < kChunks; ++c) {
-      const int idx = c * THREADS + tid;
-      if (idx < nchunks) qr[idx] = quant_chunk<XT, QT, true>(v[c], s, y);
-    }
-    for (int idx = kChunks * THREADS + tid; idx < nchunks; idx += THREADS)
-      qr[idx] = quant_chunk<XT, QT, true>(xr[idx], s, y);
+    for (int c = 0; c < CH; ++c) store(c * THREADS + tid, quant_chunk<XT, QT, true>(v[c], s, y));
+    for (int idx = CH * THREADS + tid; idx < nchunks; idx += THREADS)
+      store(idx, quant_chunk<XT, QT, true>(load(idx), s, y));
   } else {
 #pragma unroll
-    for (int c = 0; c < kChunks; ++c) {
-      const int idx = c * THREADS + tid;
-      if (idx < nchunks) qr[idx] = quant_chunk<XT, QT, false>(v[c], s, y);
-    }
-    for (int idx = kChunks * THREADS + tid; idx < nchunks; idx += THREADS)
-      qr[idx] = quant_chunk<XT, QT, false>(xr[idx], s, y);
+    for (int c = 0; c < CH; ++c) store(c * THREADS + tid, quant_chunk<XT, QT, false>(v[c], s, y));
+    for (int idx = CH * THREADS + tid; idx < nchunks; idx += THREADS)
+      store(idx, quant_chunk<XT, QT, false>(load(idx), s, y));
   }
 }
 
-template <int THREADS>
+template <int THREADS, int CH>
 static void launch_quant_t(const void* x, int x_dtype, void* xq, int q_dtype, float* scales, int64_t M,
                            int64_t K, hipStream_t stream) {
   const dim3 grid((unsigned)M), block(THREADS);
   const uint16_t* xp = (const uint16_t*)x;
   uint8_t* qp = (uint8_t*)xq;
   if (x_dtype == W4_F16 && q_dtype == W4_I8)
-    hipLaunchKernelGGL((w4_quant_kernel<W4_F16, W4_I8, THREADS>), grid, block, 0, stream, xp, qp, scales, K);
+    hipLaunchKernelGGL((w4_quant_kernel<W4_F16, W4_I8, THREADS, CH>), grid, block, 0, stream, xp, qp, scales, K);
   else if (x_dtype == W4_F16)
-    hipLaunchKernelGGL((w4_quant_kernel<W4_F16, W4_FP8_E4M3, THREADS>), grid, block, 0, stream, xp, qp, scales, K);
-  else if (q_dtype == W4_I8)
-    hipLaunchKernelGGL((w4_quant_kernel<W4_BF16, W4_I8, THREADS>), grid, block, 0, stream, xp, qp, scales, K);
-  else
-    hipLaunchKernelGGL((w4_quant_kernel<W4_BF16, W4_FP8_E4M3, THREADS>), grid, block, 0, stream, xp, qp, scales,
+    hipLaunchKernelGGL((w4_quant_kernel<W4_F16, W4_FP8_E4M3, THREADS, CH>), grid, block, 0, stream, xp, qp, scales,
                        K);
+  else if (q_dtype == W4_I8)
+    hipLaunchKernelGGL((w4_quant_kernel<W4_BF16, W4_I8, THREADS, CH>), grid, block, 0, stream, xp, qp, scales, K);
+  else
+    hipLaunchKernelGGL((w4_quant_kernel<W4_BF16, W4_FP8_E4M3, THREADS, CH>), grid, block, 0, stream, xp, qp,
+                       scales, K);
+}
+
+template <int THREADS>
+static void launch_quant_c(const void* x, int x_dtype, void* xq, int q_dtype, float* scales, int64_t M,
+                           int64_t K, hipStream_t stream) {
+  const int64_t per_thread = (K / 8 + THREADS - 1) / THREADS;
+  if (per_thread <= 4)
+    launch_quant_t<THREADS, 4>(x, x_dtype, xq, q_dtype, scales, M, K, stream);
+  else if (per_thread <= 8)
+    launch_quant_t<THREADS, 8>(x, x_dtype, xq, q_dtype, scales, M, K, stream);
+  else
+    launch_quant_t<THREADS, kMaxChunks>(x, x_dtype, xq, q_dtype, scales, M, K, stream);
 }
 
 hipError_t launch_quant(const void* x, int x_dtype, void* xq, int q_dtype, float* scales, int64_t M,
                         int64_t K, hipStream_t stream) {
   // few rows: a whole CU per row
   if (M <= 512 && K >= 8 * 1024)
-    launch_quant_t<1024>(x, x_dtype, xq, q_dtype, scales, M, K, stream);
+    launch_quant_c<1024>(x, x_dtype, xq, q_dtype, scales, M, K, stream);
   else
-    launch_quant_t<256>(x, x_dtype, xq, q_dtype, scales, M, K, stream);
+    launch_quant_c<256>(x, x_dtype, xq, q_dtype, scales, M, K, stream);
   return hipGetLastError();
 }
 

@@ -31,7 +31,9 @@ def test_prepack_bit_exact_full_size(N, K, operand):
 @pytest.mark.parametrize("q_dtype", ["i8", "fp8"])
 @pytest.mark.parametrize("M,K,dist", [(1, 128, "normal"), (3, 4096, "normal"), (16, 512, "wide"),
                                       (5, 8, "normal"), (7, 40000, "normal"), (33, 21760, "wide"),
-                                      (64, 8192, "normal")])
+                                      (64, 8192, "normal"),
+                                      # rows longer than the register-resident chunks: tail pass
+                                      (520, 30000, "normal"), (2, 100000, "wide")])
 def test_quant_bit_exact(x_dtype, q_dtype, M, K, dist):
     x = workloads.activations(M, K, x_dtype, seed=M * 31 + K, dist=dist)
     if M >= 3:
