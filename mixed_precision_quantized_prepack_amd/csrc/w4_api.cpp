@@ -150,10 +150,15 @@ int make_plan(int64_t M, int64_t N, int64_t K, bool grouped, int op, GemmPlan* p
     if (fs) {
       s = fs;
     } else {
+      // K splits: the fewest that give two workgroups per CU, or one per CU
+      // when there are very few tiles (each split adds an M x N fp32 slot
+      // that the reduce reads back, which outweighs the second workgroup
+      // there)
       const int64_t tiles = ((M + plan->bm - 1) / plan->bm) * ((N + plan->bn - 1) / plan->bn);
-      const int64_t slots = 2LL * cu;   // resident workgroups (two per CU)
+      const int64_t target = tiles < cu / 2 ? cu : 2LL * cu;
       s = 1;
-      while (tiles * s < slots && s * 2 <= 8 && KB / (s * 2) >= 4) s *= 2;
+      while (tiles * s < target && s * 2 <= 8) s *= 2;
+      while (s > 1 && KB / s < 4) s /= 2;
     }
     if (s < 1 || s > 64 || s > KB)
       return fail(W4_E_SHAPE, "tiled kernel: K split %lld not in [1, min(64, K/128)]", (long long)s);

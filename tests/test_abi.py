@@ -127,6 +127,20 @@ def test_partials_window_validation(lib):
     assert f(FAKE, 3, FAKE, 0, 128, 4, 32, 256, 0, 4, 0, 32, None, None, 0, None) == E_NULL
 
 
+def test_plan_choices(lib):
+    """Kernel choice and K split for the int8 per-channel 8192x21760 sweep on a
+    256-CU part (the CU count the library assumes without a device)."""
+    plans = {M: w4.gemm_plan(M, 8192, 21760, -1, w4.I8) for M in (1, 16, 64, 128, 256, 512, 1024, 4096)}
+    assert plans[1][0] == plans[16][0] == 1                      # small-M kernel
+    assert plans[1][3] == 32                                     # two 16-column strips per wave
+    assert [plans[M][1] for M in (64, 128, 256, 512, 1024)] == [8, 4, 4, 2, 1]
+    assert plans[4096][1:] == (1, 128, 256)                      # one 128 x 256 tile per workgroup
+    # grouped small M: one strip below M = 8, two from there when N >= 8192
+    assert w4.gemm_plan(1, 22016, 4096, 128, w4.I8)[3] == 16
+    assert w4.gemm_plan(16, 22016, 4096, 128, w4.I8)[3] == 32
+    assert w4.gemm_plan(16, 4096, 11008, 128, w4.I8)[3] == 16
+
+
 def test_options_and_plans(lib):
     try:
         assert lib.w4_set_option(b"nonsense", 1) == E_UNSUP
