@@ -733,21 +733,23 @@ __global__ __launch_bounds__(256, 2) void w4_gemm_tiled(GemmArgs p, int splitk) 
           zcv[nt] = *reinterpret_cast<const f32x4*>(&gzc[slot * BNW + (wave * NT + nt) * 16 + 4 * kq]);
       }
       // Row mt's MFMAs start from zero; row mt - 1 is folded while they run.
-      auto fold_row = [&](int mt) {
+      auto fold_block = [&](int nt, int mt) {
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            float pv;
-            if constexpr (OP == OP_I8)
-              pv = (float)acc[nt][mt][i];
-            else if constexpr (OP == OP_BF16)
-              pv = fmaf(-zcv[nt][i], ones[mt][i], acc[nt][mt][i]);
-            else
-              pv = acc[nt][mt][i];
-            tot[nt][mt][i] = fmaf(pv, scv[nt][i], tot[nt][mt][i]);
-          }
+        for (int i = 0; i < 4; ++i) {
+          float pv;
+          if constexpr (OP == OP_I8)
+            pv = (float)acc[nt][mt][i];
+          else if constexpr (OP == OP_BF16)
+            pv = fmaf(-zcv[nt][i], ones[mt][i], acc[nt][mt][i]);
+          else
+            pv = acc[nt][mt][i];
+          tot[nt][mt][i] = fmaf(pv, scv[nt][i], tot[nt][mt][i]);
+        }
       };
+      // Issue order, pinned: per tile row, the fragment reads of row mt + 2,
+      // then per n-block the row's MFMAs followed by the fold of the same
+      // n-block of row mt - 1 (whose MFMAs finished a row earlier), so the
+      // fold's VALU work runs in the MFMAs' shadow.
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
@@ -755,31 +757,17 @@ __global__ __launch_bounds__(256, 2) void w4_gemm_tiled(GemmArgs p, int splitk) 
           Acc t = Acc{};
           block_mma<OP>(e[nt], af[mt], t);
           acc[nt][mt] = t;
+          if (nt == NT - 1 && OP == OP_BF16) {
+            f32x4 o = f32x4{};
+            ones_mma(af[mt], o);
+            ones[mt] = o;
+          }
+          if (mt > 0) fold_block(nt, mt - 1);
+          __builtin_amdgcn_sched_barrier(0);
         }
-        if constexpr (OP == OP_BF16) {
-          f32x4 o = f32x4{};
-          ones_mma(af[mt], o);
-          ones[mt] = o;
-        }
-        if (mt > 0) fold_row(mt - 1);
       }
-      fold_row(MT - 1);
-      // Issue order: scale-table and fragment reads first, then per tile row
-      // one MFMA at a time with part of the previous row's fold between them;
-      // the fragment reads of row mt + 2 go out with the MFMAs of row mt.
-      constexpr int kMfmaPerRow = NT * kMfmaPerBlock<OP> + (OP == OP_BF16 ? 4 : 0);
-      constexpr int kFoldPerRow = NT * 4 * (OP == OP_I8 || OP == OP_BF16 ? 2 : 1);
-      constexpr int kValuPerMfma = (kFoldPerRow + kMfmaPerRow - 1) / kMfmaPerRow;
-      __builtin_amdgcn_sched_group_barrier(0x100, 2 * AV + NT * (OP == OP_BF16 ? 2 : 1), 0);
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-#pragma unroll
-        for (int q = 0; q < kMfmaPerRow; ++q) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          if (mt > 0) __builtin_amdgcn_sched_group_barrier(0x002, kValuPerMfma, 0);
-        }
-        if (mt + 2 < MT) __builtin_amdgcn_sched_group_barrier(0x100, AV, 0);
-      }
+      for (int nt = 0; nt < NT; ++nt) fold_block(nt, MT - 1);
     } else {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
