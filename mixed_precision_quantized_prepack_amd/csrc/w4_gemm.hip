@@ -192,13 +192,13 @@ __device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_
 // cache-policy bits of its weight loads (2 = non-temporal: the weight stream
 // is read once).
 #ifndef W4_SKINNY_U8
-#define W4_SKINNY_U8 2
+#define W4_SKINNY_U8 1
 #endif
 #ifndef W4_SKINNY_U16
-#define W4_SKINNY_U16 2
+#define W4_SKINNY_U16 1
 #endif
 #ifndef W4_SKINNY_UG
-#define W4_SKINNY_UG 2   // grouped problems also prefetch per-block scales
+#define W4_SKINNY_UG 1   // grouped problems also prefetch per-block scales
 #endif
 #ifndef W4_SKINNY_WPOLICY
 #define W4_SKINNY_WPOLICY 2
@@ -370,13 +370,22 @@ __global__ __launch_bounds__(64 * skinny_max_waves(OP, GROUPED)) void w4_gemm_sk
     }
   };
 
-  const int nbatch = wave < S ? (KB - wave + S - 1) / S : 0;   // K blocks of this wave
-  load_batch(0, 0);
-  for (int kb = 0; kb < nbatch; kb += 2 * U) {
+  // Whole pairs of batches, then one last pair whose second batch may lie
+  // (partly) past K: its loads read zero and add nothing.  The loop has no
+  // exit in its middle, so the loads of the next batch stay in flight across
+  // the back edge instead of being waited for at the loop head.
+  if (wave < S) {
+    const int nbatch = (KB - wave + S - 1) / S;   // K blocks of this wave
+    load_batch(0, 0);
+    int kb = 0;
+    for (; kb + 2 * U < nbatch; kb += 2 * U) {
+      load_batch(1, kb + U);
+      compute_batch(0, kb);
+      load_batch(0, kb + 2 * U);
+      compute_batch(1, kb + U);
+    }
     load_batch(1, kb + U);
     compute_batch(0, kb);
-    if (kb + U >= nbatch) break;
-    load_batch(0, kb + 2 * U);
     compute_batch(1, kb + U);
   }
 
