@@ -152,9 +152,9 @@ def summarize(trace_dir: str, fetch_dir: str, write_dir: str) -> int:
              f"rocprofv3 --kernel-trace --stats --output-format csv -d {trace_dir} -o trace -- "
              "python -u bench.py --steps 2 --warmup 1 --no-cpu-baseline --calibrate-copy",
              f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {fetch_dir} -o fetch -- "
-             "python -u bench.py --steps 2 --warmup 1 --no-cpu-baseline --calibrate-copy",
+             "python -u bench.py --steps 2 --warmup 1 --no-cpu-baseline --calibrate-copy --settle-ms 0",
              f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {write_dir} -o write -- "
-             "python -u bench.py --steps 2 --warmup 1 --no-cpu-baseline --calibrate-copy",
+             "python -u bench.py --steps 2 --warmup 1 --no-cpu-baseline --calibrate-copy --settle-ms 0",
              f"python bench.py --summarize {trace_dir} {fetch_dir} {write_dir}", "```", "",
              "FETCH_SIZE / WRITE_SIZE are KiB per dispatch.  They are scaled by what the same counters read "
              f"for a plain copy kernel that reads and writes {CALIB_BYTES >> 20} MiB "
@@ -186,9 +186,11 @@ def write_kernel_stats(trace_dir: str) -> None:
              "Command (repository root, one MI355X):", "", "```",
              f"rocprofv3 --kernel-trace --stats --output-format csv -d {trace_dir} -o trace -- "
              "python -u bench.py --steps 2 --warmup 1 --no-cpu-baseline --calibrate-copy", "```", "",
-             "Each timed step runs the per-token quantisation and the GEMM for every M; the small-M GEMMs "
-             "(M = 1, 16) are also launched 30 times back to back per M for their per-launch time.  "
-             "Durations are per dispatch, from the kernel trace.", "",
+             "Each step runs the per-token quantisation and the GEMM for every M: about 100 ms of untimed "
+             "steps while the clocks settle, the warm-up step, two timed steps and two more with events "
+             "around each launch; the small-M GEMMs (M = 1, 16) are also launched 30 times back to back "
+             "per M for their per-launch time.  Durations are per dispatch, from the kernel trace; the "
+             "median per grid leaves out the first steps, which run before the clocks have risen.", "",
              "| kernel | calls | avg us | min us | max us | % time |", "|---|---|---|---|---|---|"]
     for r in rows:
         lines.append(f"| `{_short(r['Name'])[:100]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
@@ -201,13 +203,14 @@ def write_kernel_stats(trace_dir: str) -> None:
             continue
         key = (k, int(float(r.get("Grid_Size_X", r.get("Grid_Size", 0)) or 0)))
         per_grid.setdefault(key, []).append(((int(r["Start_Timestamp"]), int(r["End_Timestamp"]))))
-    lines += ["", "GEMM launches by grid (threads; one grid per M except M = 1 and 16, which share one), in "
-              "launch order (the first belongs to the warm-up step):", "",
-              "| kernel | grid | calls | avg us | per launch us |", "|---|---|---|---|---|"]
+    lines += ["", "GEMM launches by grid (threads; one grid per M except M = 1 and 16, which share one); "
+              "the last column lists the last eight launches in launch order:", "",
+              "| kernel | grid | calls | avg us | median us | last launches us |", "|---|---|---|---|---|---|"]
     for (k, g), v in sorted(per_grid.items(), key=lambda kv: kv[0][1]):
         d = [(e - b) / 1e3 for b, e in sorted(v)]
-        shown = ", ".join(f"{x:.1f}" for x in d[:8]) + (", ..." if len(d) > 8 else "")
-        lines.append(f"| `{k[:100]}` | {g} | {len(d)} | {sum(d) / len(d):.1f} | {shown} |")
+        med = sorted(d)[len(d) // 2]
+        shown = ("..., " if len(d) > 8 else "") + ", ".join(f"{x:.1f}" for x in d[-8:])
+        lines.append(f"| `{k[:100]}` | {g} | {len(d)} | {sum(d) / len(d):.1f} | {med:.1f} | {shown} |")
     with open(STATS_MD, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print(STATS_MD)
@@ -255,6 +258,8 @@ def main(argv=None) -> int:
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--settle-ms", type=float, default=100.0,
+                    help="untimed steps for at least this long before the warm-up steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--ms", default=",".join(str(m) for m in MS))
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -335,6 +340,17 @@ def main(argv=None) -> int:
             if evs is not None:
                 evs[i][2].record()
 
+    # Clock settle: the GPU raises its clocks over the first tens of ms of
+    # sustained work (a step after ~3 ms of warm-up runs ~13% slower than one
+    # after 100 ms), so untimed steps run for at least --settle-ms before the
+    # W warm-up steps.
+    settle_steps = 0
+    t_settle = time.perf_counter()
+    while (time.perf_counter() - t_settle) * 1e3 < args.settle_ms:
+        for _ in range(5):
+            step(None)
+        settle_steps += 5
+        torch.cuda.synchronize()
     for _ in range(args.warmup):
         step(None)
     torch.cuda.synchronize()
@@ -344,13 +360,24 @@ def main(argv=None) -> int:
     t_start, t_end = mk(), mk()
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
+    # The headline: K steps with nothing between the launches.  An event
+    # recorded between two kernels costs several us of dispatch latency, so
+    # the per-launch durations come from a second pass of K steps with events
+    # around every launch on the launch stream.
     t_start.record()
     for s in range(args.steps):
-        step(all_evs[s])
+        step(None)
     t_end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_per_step = t_start.elapsed_time(t_end) / args.steps
+    e_start, e_end = mk(), mk()
+    e_start.record()
+    for s in range(args.steps):
+        step(all_evs[s])
+    e_end.record()
+    torch.cuda.synchronize()
+    ms_per_step_events = e_start.elapsed_time(e_end) / args.steps
 
     # ---- per-launch durations of the small-M kernel ----------------------
     # A launch of ~20 us bracketed by two events also counts the event-to-
@@ -404,8 +431,8 @@ def main(argv=None) -> int:
     roofline = {"bound": "mfma", "achieved": round(ach, 2), "peak": INT8_PEAK_TOPS, "unit": "TFLOP/s",
                 "frac": round(ach / INT8_PEAK_TOPS, 4), "traffic": traffic_for(dom_name, [pm["M"] for pm in dom]),
                 "kernel": dom_name, "launches": [pm["M"] for pm in dom], "avg_launch_us": round(dur, 2),
-                "note": "int8 ops (2 per multiply-add) per second; avg_launch_us from the timed steps "
-                        "(events around each launch on the launch stream)"}
+                "note": "int8 ops (2 per multiply-add) per second; avg_launch_us from a second pass of "
+                        "the timed steps with events around each launch on the launch stream"}
     small = [pm for pm in per_m if pm["kernel"].startswith("w4_gemm_skinny")]
     roofline_small = None
     if small:
@@ -427,6 +454,8 @@ def main(argv=None) -> int:
                    "activations": "fp16 ~N(0,1), dynamic per-token int8", "weights": "int4 uniform [-8,7], PB-v1",
                    "scales": "fp32 per channel ~U(0.005,0.02)", "out": "fp16", "weight_copies": copies},
         "weight_GBps_step": round(copies * (N * K / 2) / (ms_per_step * 1e-3) / 1e9, 1),
+        "ms_per_step_with_launch_events": round(ms_per_step_events, 4),
+        "settle_steps": settle_steps,
         "per_m": per_m,
         "roofline": roofline,
         "roofline_small_m": roofline_small,
