@@ -37,6 +37,12 @@ notes):
   are round-to-nearest-even of the fp32 quotient x / scale (a correctly rounded
   IEEE fp32 division); int8 codes are clamped to [-127, 127]; fp8 codes are
   OCP e4m3fn with saturation at +-448.  A row of zeros gets scale 0 and codes 0.
+* Fused RMSNorm + per-token quantisation returns exactly what an RMSNorm
+  producing its output in the activation dtype, followed by the per-token
+  quantisation above, would.  The normalisation takes the exact sum of
+  squares (rounded once to float64), the reciprocal square root of
+  mean + eps in float64 rounded to fp32, and the products x * r * gamma in
+  fp32 in that order.
 * The logical (unpacked) weight is [N, K/2] bytes, even k in the low nibble.
 * Everything downstream of the stored inputs is exact or float64: integer
   partial sums are exact, scales are applied in float64 and the output is
@@ -49,6 +55,7 @@ products are exact whatever order the library sums in.
 """
 from __future__ import annotations
 
+import math
 from typing import Optional
 
 import numpy as np
@@ -211,6 +218,57 @@ def quant_act_per_token(x_bits: np.ndarray, x_dtype: str, q_dtype: str):
     else:
         raise ValueError(q_dtype)
     return q, s
+
+
+def rmsnorm_rows(x_bits: np.ndarray, x_dtype: str, gamma_bits: np.ndarray, eps: float):
+    """The normalisation step of ``rmsnorm_quant_per_token`` before its final
+    rounding to the activation dtype: returns (r [M] fp32, y [M, K] fp32).
+
+    ss[m]   = sum_k x[m, k]**2               exact, rounded once to float64
+    var[m]  = fp64(fp64(ss[m] / K) + eps)      eps given as fp32
+    r[m]    = fp32(fp64(1 / fp64(sqrt(var[m]))))
+    y[m, k] = fp32(fp32(x[m, k] * r[m]) * gamma[k])
+
+    Each square of an fp16/bf16 value is exact in float64 and math.fsum
+    returns the correctly rounded sum, so ss does not depend on any summation
+    order.  eps must be positive.
+    """
+    if not eps > 0:
+        raise ValueError("eps must be positive")
+    x = F.decode(x_bits, x_dtype)                       # float64, exact
+    g = F.decode(gamma_bits, x_dtype)
+    M, K = x.shape
+    if K == 0:
+        raise ValueError("K must be positive")
+    eps64 = float(np.float32(eps))
+    r = np.empty((M,), dtype=np.float32)
+    for m in range(M):
+        ss = math.fsum(float(v) * float(v) for v in x[m])
+        var = ss / K + eps64
+        r[m] = np.float32(1.0 / math.sqrt(var))
+    y = (x.astype(np.float32) * r[:, None]) * g.astype(np.float32)[None, :]
+    return r, y
+
+
+def rmsnorm_quant_per_token(x_bits: np.ndarray, x_dtype: str, gamma_bits: np.ndarray, eps: float,
+                            q_dtype: str):
+    """RMSNorm followed by dynamic per-token quantisation, as one operation.
+
+    vLLM PR "[ Kernel ] Enable Dynamic Per Token fp8", review discussion: one
+    scale per token makes it easy to fuse the RMSNorm that precedes a linear
+    layer with the quantisation of its output.  The pages fix neither the
+    normalisation's precision nor the rounding between the two steps; the
+    reading taken here is that the fused operation returns exactly what the
+    RMSNorm, producing its output in the activation dtype, followed by
+    ``quant_act_per_token`` would: y = dtype(rmsnorm_rows(x)) rounded to
+    nearest even, then codes, scales = quant_act_per_token(y).
+
+    Returns (codes, scales, y_bits).
+    """
+    _, y32 = rmsnorm_rows(x_bits, x_dtype, gamma_bits, eps)
+    y_bits = F.round_and_encode(y32.astype(np.float64), x_dtype)
+    codes, scales = quant_act_per_token(y_bits, x_dtype, q_dtype)
+    return codes, scales, y_bits
 
 
 def activation_integers(codes: np.ndarray, q_dtype: str) -> np.ndarray:

@@ -8,6 +8,7 @@ from __future__ import annotations
 
 import struct
 from fractions import Fraction
+from math import isqrt
 
 # (significand bits p, minimum normal exponent, largest finite value)
 FMT = {
@@ -15,6 +16,7 @@ FMT = {
     "f16": (11, -14, Fraction(65504)),
     "bf16": (8, -126, Fraction((2 ** 8 - 1) * 2 ** 120)),
     "e4m3fn": (4, -6, Fraction(448)),
+    "f64": (53, -1022, Fraction((2 ** 53 - 1) * 2 ** 971)),
 }
 
 
@@ -121,3 +123,27 @@ def nearest_e4m3fn_bruteforce(q: Fraction) -> int:
     if c == 0 and q < 0:
         c = 0x80
     return c
+
+
+def sqrt_rounded(v: Fraction, fmt: str = "f64") -> Fraction:
+    """Nearest ``fmt`` value to sqrt(v) for a rational v > 0, ties to even,
+    from an integer square root (no floating point)."""
+    p = FMT[fmt][0]
+    # scale v by 4**j so that the integer square root carries p + 8 bits
+    j = 0
+    while v * Fraction(4) ** j < Fraction(2) ** (2 * (p + 8)):
+        j += 1
+    while v * Fraction(4) ** j >= Fraction(2) ** (2 * (p + 10)):
+        j -= 1
+    t = v * Fraction(4) ** j
+    n = isqrt(t.numerator // t.denominator)
+    exact = Fraction(n * n) == t
+    # sqrt(v) = (n + f) / 2**j with 0 <= f < 1 (f = 0 iff exact); n has at
+    # least p + 8 bits, so rounding n + f to p bits never sees a tie unless
+    # f = 0, and then n decides it alone
+    if exact:
+        return round_fraction(Fraction(n, 2 ** j) if j >= 0 else Fraction(n * 2 ** -j), fmt)
+    # inexact: round (n + 1/2) / 2**j; no p-bit tie can fall strictly inside
+    # (n, n + 1), so the midpoint stands for the whole interval
+    mid = Fraction(2 * n + 1, 2)
+    return round_fraction(mid / Fraction(2) ** j, fmt)
