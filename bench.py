@@ -400,6 +400,29 @@ def main(argv=None) -> int:
         torch.cuda.synchronize()
         iso_us[M] = e0.elapsed_time(e1) * 1e3 / REPS
 
+    # ---- fused RMSNorm + per-token quantisation, next to the plain quantiser
+    # (same activations; both read 2 B and write 1 B per element), REPS
+    # launches back to back between two events
+    gamma = workloads.norm_weight(K, "f16", seed=2025).to(dev)
+    norm_quant = []
+    for M in sorted({min(Ms), max(Ms)}):
+        row = {"M": M, "K": K}
+        for name, fn in (("quant_us", lambda: w4.quant_act_per_token(a[:M], "i8", out=aq[M], scales=sa[M])),
+                         ("rmsnorm_quant_us", lambda: w4.rmsnorm_quant_per_token(a[:M], gamma, 1e-6, "i8",
+                                                                                 out=aq[M], scales=sa[M]))):
+            fn()
+            e0, e1 = mk(), mk()
+            e0.record()
+            for _ in range(REPS):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            row[name] = round(e0.elapsed_time(e1) * 1e3 / REPS, 2)
+        nbytes = M * K * 3 + 4 * M + 2 * K
+        row["rmsnorm_quant_GBps"] = round(nbytes / (row["rmsnorm_quant_us"] * 1e-6) / 1e9, 1)
+        row["hbm_frac"] = round(row["rmsnorm_quant_GBps"] / HBM_PEAK_GBPS, 4)
+        norm_quant.append(row)
+
     # ---- per-M figures ----------------------------------------------------
     per_m = []
     total_ops = 0.0
@@ -459,6 +482,7 @@ def main(argv=None) -> int:
         "per_m": per_m,
         "roofline": roofline,
         "roofline_small_m": roofline_small,
+        "rmsnorm_quant": norm_quant,
         "prepack": {"median_us": round(prepack_us[len(prepack_us) // 2], 2),
                     "GBps_read_plus_write": round(N * K / (prepack_us[len(prepack_us) // 2] * 1e-6) / 1e9, 1)},
         "wall_s_timed": round(wall, 3),

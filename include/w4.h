@@ -136,6 +136,31 @@ W4_API int w4_quant_act_per_token(const void* x, int x_dtype, void* xq, int q_dt
                            int64_t M, int64_t K, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Fused RMSNorm + dynamic per-token activation quantisation.
+ *
+ * "[ Kernel ] Enable Dynamic Per Token fp8", review discussion: per-token
+ * scales make it easy to fuse the RMSNorm before a linear layer with the
+ * quantisation of its output.  The result is exactly that of an RMSNorm whose
+ * output is in x_dtype, followed by w4_quant_act_per_token.  Per row m:
+ *   ss   = sum_k x[m,k]^2, exact, rounded once to fp64 (no dependence on
+ *          summation order)
+ *   r    = fp32( 1 / sqrt( ss / K + eps ) )        (fp64 arithmetic)
+ *   y    = x_dtype( fp32( fp32(x[m,k] * r) * gamma[k] ) )   (round to nearest even)
+ *   xq, scales = w4_quant_act_per_token(y)
+ * x and gamma are read once; y is never stored.
+ *
+ * x       : device, [M][K] of x_dtype (W4_F16 or W4_BF16); finite values.
+ * gamma   : device, [K] of x_dtype; every y must be finite in x_dtype.
+ * eps     : positive, finite.
+ * xq      : device, [M][K] of q_dtype (W4_I8, or W4_FP8_E4M3 as raw bytes).
+ * scales  : device, [M] fp32.
+ * Requires 0 < K <= 2^29, K % 8 == 0, M >= 0; x, gamma, xq 16-byte aligned.
+ * Errors: W4_E_NULL, W4_E_SHAPE (shape or eps), W4_E_DTYPE, W4_E_ALIGN, W4_E_HIP.
+ * ------------------------------------------------------------------------- */
+W4_API int w4_rmsnorm_quant_per_token(const void* x, int x_dtype, const void* gamma, float eps, void* xq,
+                               int q_dtype, float* scales, int64_t M, int64_t K, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Workspace.
  *
  * Some (M, N, K) are split along K across workgroups; the partial results go
@@ -243,6 +268,9 @@ W4_API int w4a16_gemm_partials(const void* a, int a_dtype, const void* b_packed,
  *                  small-M kernel (2 needs N % 32 == 0)
  *   "tiled_bm"   : 0 = automatic, 64 or 128 rows per tile of the tiled kernel
  *                  (128 only for int8 per-channel problems)
+ *   "norm_exact_sum": 1 = w4_rmsnorm_quant_per_token always re-sums the squares
+ *                  with error-free pair arithmetic (the path it otherwise takes
+ *                  only when the fast sum cannot decide r); same results
  * Returns W4_OK, or W4_E_UNSUPPORTED for an unknown key / W4_E_SHAPE for an
  * out-of-range value.
  * ------------------------------------------------------------------------- */

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -20,6 +21,7 @@ thread_local std::string g_last_error;
 
 std::atomic<int64_t> g_force_path{0};
 std::atomic<int64_t> g_splitk{0};
+std::atomic<int64_t> g_norm_exact_sum{0};
 std::atomic<int64_t> g_skinny_strips{0};
 std::atomic<int64_t> g_tiled_bm{0};
 
@@ -255,6 +257,25 @@ int w4_quant_act_per_token(const void* x, int x_dtype, void* xq, int q_dtype, fl
   return ok();
 }
 
+int w4_rmsnorm_quant_per_token(const void* x, int x_dtype, const void* gamma, float eps, void* xq, int q_dtype,
+                               float* scales, int64_t M, int64_t K, void* stream) {
+  if (x_dtype != W4_F16 && x_dtype != W4_BF16) return fail(W4_E_DTYPE, "x_dtype must be W4_F16 or W4_BF16");
+  if (q_dtype != W4_I8 && q_dtype != W4_FP8_E4M3)
+    return fail(W4_E_DTYPE, "q_dtype must be W4_I8 or W4_FP8_E4M3");
+  if (M < 0 || K <= 0 || K % 8 || M > ((int64_t)1 << 31) - 1 || K > ((int64_t)1 << 29))
+    return fail(W4_E_SHAPE, "need M >= 0, 0 < K <= 2^29, K %% 8 == 0 (M=%lld K=%lld)", (long long)M,
+                (long long)K);
+  if (!(eps > 0.0f) || !std::isfinite(eps)) return fail(W4_E_SHAPE, "eps must be positive and finite");
+  if (M == 0) return ok();
+  if (!x || !gamma || !xq || !scales) return fail(W4_E_NULL, "x, gamma, xq and scales are required");
+  if (!aligned(x, 16) || !aligned(gamma, 16) || !aligned(xq, 16) || !aligned(scales, 4))
+    return fail(W4_E_ALIGN, "x, gamma and xq must be 16-byte aligned, scales 4-byte aligned");
+  hipError_t e = launch_rmsnorm_quant(x, x_dtype, gamma, eps, xq, q_dtype, scales, M, K,
+                                     (int)g_norm_exact_sum.load(), (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "rmsnorm-quant launch");
+  return ok();
+}
+
 size_t w4_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t group_size, int a_dtype) {
   const int op = op_of(a_dtype);
   if (op < 0 || check_shape(M, N, K) || check_group(group_size, K)) return 0;
@@ -446,6 +467,11 @@ int w4_set_option(const char* key, int64_t value) {
     g_tiled_bm.store(value);
     return ok();
   }
+  if (!strcmp(key, "norm_exact_sum")) {
+    if (value != 0 && value != 1) return fail(W4_E_SHAPE, "norm_exact_sum must be 0 or 1");
+    g_norm_exact_sum.store(value);
+    return ok();
+  }
   return fail(W4_E_UNSUPPORTED, "unknown option '%s'", key);
 }
 
@@ -455,6 +481,7 @@ int64_t w4_get_option(const char* key) {
   if (!strcmp(key, "splitk")) return g_splitk.load();
   if (!strcmp(key, "skinny_strips")) return g_skinny_strips.load();
   if (!strcmp(key, "tiled_bm")) return g_tiled_bm.load();
+  if (!strcmp(key, "norm_exact_sum")) return g_norm_exact_sum.load();
   return -1;
 }
 

@@ -52,6 +52,8 @@ hipError_t launch_prepack(const void* w_logical, void* w_packed, int64_t N, int6
                           hipStream_t stream);
 hipError_t launch_quant(const void* x, int x_dtype, void* xq, int q_dtype, float* scales, int64_t M,
                         int64_t K, hipStream_t stream);
+hipError_t launch_rmsnorm_quant(const void* x, int x_dtype, const void* gamma, float eps, void* xq, int q_dtype,
+                                float* scales, int64_t M, int64_t K, int exact_sum, hipStream_t stream);
 hipError_t launch_gemm(const GemmArgs& args, int op, bool grouped, bool flip, const GemmPlan& plan,
                        hipStream_t stream);
 

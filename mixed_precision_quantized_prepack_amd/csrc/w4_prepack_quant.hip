@@ -96,7 +96,8 @@ hipError_t launch_prepack(const void* w_logical, void* w_packed, int64_t N, int6
 // ---------------------------------------------------------------------------
 // Chunks a thread keeps in registers: the launch picks the smallest of
 // 4, 8 or 12 that covers the row (a chunk slot past the row still costs an
-// address-pipeline pass, which matters when few rows share a CU).
+// address-pipeline pass, which matters when few rows share a CU), and at
+// most 4 in 1024-thread workgroups.
 constexpr int kMaxChunks = 12;
 
 template <int XT>
@@ -155,6 +156,85 @@ __device__ __forceinline__ uint2 quant_chunk(const uint4& v, float s, float y) {
   return make_uint2(out[0], out[1]);
 }
 
+// ---------------------------------------------------------------------------
+// Fused RMSNorm.  "[ Kernel ] Enable Dynamic Per Token fp8", review
+// discussion: per-token scales make it easy to fuse the preceding RMSNorm
+// with the quantisation.  The fused operation returns what the RMSNorm
+// (output in the activation dtype) followed by the quantisation above would:
+//   ss = sum_k x^2 (rounded once to fp64), r = fp32(1 / sqrt(ss / K + eps))
+//   (fp64 arithmetic), y = dtype(fp32(fp32(x * r) * gamma)), then quantise y.
+// The sum of squares decides integer codes, so r must be the one its exact
+// sum gives.  Each square is exact in fp64.  Fast path: every thread sums its
+// n terms with fp64 FMAs; the terms are positive, so the result is within
+// n * 2^-53 (relative) of their exact sum, and the threads' sums are combined
+// as unevaluated pairs hi + lo (error-free two-sums).  r is computed from both
+// ends of that interval through the same monotone fp64 steps, widened by a
+// few ulps; when both round to the same fp32 value, that value is r.  Else
+// (about one row in 2^22) the exact path re-sums the row's squares as pairs,
+// with an error-free two-sum per term (within ~2^-100 of the exact sum), so
+// that hi is the sum rounded once.
+// ---------------------------------------------------------------------------
+struct DD {
+  double hi, lo;
+};
+
+// hi + lo += p, with the rounding error of hi + p kept exactly (two-sum)
+__device__ __forceinline__ void dd_add_term(DD& a, double p) {
+  const double s = a.hi + p;
+  const double bp = s - a.hi;
+  const double e = (a.hi - (s - bp)) + (p - bp);
+  a.hi = s;
+  a.lo += e;
+}
+
+// (a.hi + a.lo) + (b.hi + b.lo), renormalised so that hi is the pair rounded
+// once.  Symmetric in a and b, so both lanes of a butterfly agree.
+__device__ __forceinline__ DD dd_add(const DD& a, const DD& b) {
+  const double s = a.hi + b.hi;
+  const double bp = s - a.hi;
+  double e = (a.hi - (s - bp)) + (b.hi - bp);
+  e += a.lo + b.lo;
+  const double hi = s + e;
+  return DD{hi, e - (hi - s)};
+}
+
+template <int XT>
+__device__ __forceinline__ void dd_add_chunk(DD& a, const uint4& v) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const double x = (double)elem<XT>(v, j);
+    dd_add_term(a, x * x);   // exact: at most 22 significant bits
+  }
+}
+
+// 1 / sqrt(ss / K + eps) in fp64: monotone (non-increasing) in ss
+__device__ __forceinline__ double rms_recip(double ss, int64_t K, float eps) {
+  return 1.0 / sqrt(ss / (double)K + (double)eps);
+}
+
+template <int XT>
+__device__ __forceinline__ uint32_t to_dtype_bits(float v) {
+  return XT == W4_F16 ? (uint32_t)f32_to_f16_bits(v) : (uint32_t)f32_to_bf16_bits(v);
+}
+
+// y = dtype(fp32(fp32(x * r) * gamma)) for the 8 elements of a chunk, packed
+// in the chunk layout elem() reads.  The fp32 product passes through an empty
+// asm statement: otherwise the compiler fuses the multiply with the fp16
+// conversion (v_fma_mixlo_f16), which rounds the exact product once instead
+// of rounding the fp32 product, and differs from it at fp16 ties.
+template <int XT>
+__device__ __forceinline__ uint4 norm_chunk(const uint4& x, const uint4& g, float r) {
+  uint32_t w[4];
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    float y0 = (elem<XT>(x, 2 * h) * r) * elem<XT>(g, 2 * h);
+    float y1 = (elem<XT>(x, 2 * h + 1) * r) * elem<XT>(g, 2 * h + 1);
+    asm volatile("" : "+v"(y0), "+v"(y1));
+    w[h] = to_dtype_bits<XT>(y0) | (to_dtype_bits<XT>(y1) << 16);
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
 // The row's chunks are read and written with buffer operations: chunk
 // indices past the row get an out-of-range offset, which loads zeros (no
 // effect on the maximum) and drops the store, so no load or store sits in a
@@ -164,19 +244,34 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* base, int
 }
 constexpr uint32_t kRowOutOfRange = 0x80000000u;
 
-template <int XT, int QT, int THREADS, int CH>
-__global__ __launch_bounds__(THREADS) void w4_quant_kernel(const uint16_t* __restrict__ x,
+// 256-thread int8 workgroups: three per CU (at most 168 VGPRs); the fp8
+// coder needs more registers than that with 12 chunks per thread.
+template <int XT, int QT, int THREADS, int CH, bool NORM>
+__global__ __launch_bounds__(THREADS, (THREADS == 256 && QT == W4_I8) ? 3 : 1) void w4_quant_kernel(const uint16_t* __restrict__ x,
                                                            uint8_t* __restrict__ xq,
-                                                           float* __restrict__ scales, int64_t K) {
+                                                           float* __restrict__ scales, int64_t K,
+                                                           const uint16_t* __restrict__ gamma, float eps,
+                                                           int exact_sum) {
   const int64_t row = blockIdx.x;
   const int tid = threadIdx.x;
   const int nchunks = (int)(K / 8);
   const __amdgpu_buffer_rsrc_t rx = row_rsrc(x + row * K, K * 2);
   const __amdgpu_buffer_rsrc_t rq = row_rsrc(xq + row * K, K);
-  auto load = [&](int idx) -> uint4 {
+  const __amdgpu_buffer_rsrc_t rg = row_rsrc(gamma, NORM ? K * 2 : 0);
+  auto load_raw = [&](const __amdgpu_buffer_rsrc_t& rsrc, int idx) -> uint4 {
     const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(
-        rx, (int)(idx < nchunks ? (uint32_t)idx * 16u : kRowOutOfRange), 0, 0);
+        rsrc, (int)(idx < nchunks ? (uint32_t)idx * 16u : kRowOutOfRange), 0, 0);
     return make_uint4(w.x, w.y, w.z, w.w);
+  };
+  __shared__ float wave_max[THREADS / 64];
+  __shared__ DD wave_ss[NORM ? THREADS / 64 : 1];
+  // fused RMSNorm: the row's scale factor, computed once the row is loaded
+  float r = 1.0f;
+  // a chunk of the quantiser's input: x itself, or the normalised x
+  auto load = [&](int idx) -> uint4 {
+    const uint4 v = load_raw(rx, idx);
+    if constexpr (NORM) return norm_chunk<XT>(v, load_raw(rg, idx), r);
+    return v;
   };
   auto store = [&](int idx, uint2 q) {
     __builtin_amdgcn_raw_buffer_store_b64(u32x2{q.x, q.y}, rq,
@@ -186,7 +281,57 @@ __global__ __launch_bounds__(THREADS) void w4_quant_kernel(const uint16_t* __res
   uint4 v[CH];
   float amax = 0.0f;
 #pragma unroll
-  for (int c = 0; c < CH; ++c) v[c] = load(c * THREADS + tid);
+  for (int c = 0; c < CH; ++c) v[c] = load_raw(rx, c * THREADS + tid);
+  if constexpr (NORM) {
+    // pairs summed over the workgroup: wave butterfly, then the waves in order
+    auto block_sum = [&](DD a) -> DD {
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1)
+        a = dd_add(a, DD{__shfl_xor(a.hi, off, 64), __shfl_xor(a.lo, off, 64)});
+      __syncthreads();   // the previous sum's readers are done with wave_ss
+      if ((tid & 63) == 0) wave_ss[tid >> 6] = a;
+      __syncthreads();
+      a = wave_ss[0];
+#pragma unroll
+      for (int w = 1; w < THREADS / 64; ++w) a = dd_add(a, wave_ss[w]);
+      return a;
+    };
+    double acc = 0.0;
+#pragma unroll
+    for (int c = 0; c < CH; ++c)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const double xv = (double)elem<XT>(v[c], j);
+        acc = fma(xv, xv, acc);
+      }
+    for (int idx = CH * THREADS + tid; idx < nchunks; idx += THREADS) {
+      const uint4 t = load_raw(rx, idx);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const double xv = (double)elem<XT>(t, j);
+        acc = fma(xv, xv, acc);
+      }
+    }
+    const DD ss = block_sum(DD{acc, 0.0});
+    // a thread sums at most n terms; the bound also covers the roundings of
+    // the pair sums and of ss * (1 +- rho)
+    const int64_t n = 8 * (((int64_t)nchunks + THREADS - 1) / THREADS);
+    const double rho = (double)(n + 8) * 0x1p-53;
+    const float r_lo = (float)(rms_recip(ss.hi * (1.0 + rho), K, eps) * (1.0 - 0x1p-50));
+    const float r_hi = (float)(rms_recip(ss.hi * (1.0 - rho), K, eps) * (1.0 + 0x1p-50));
+    if (r_lo == r_hi && !exact_sum) {
+      r = r_lo;
+    } else {
+      DD e{0.0, 0.0};
+      // the row is read again (rather than taken from the chunks in
+      // registers, which the compiler would then keep in twice the registers)
+      for (int idx = tid; idx < nchunks; idx += THREADS) dd_add_chunk<XT>(e, load_raw(rx, idx));
+      e = block_sum(dd_add(DD{0.0, 0.0}, e));
+      r = (float)rms_recip(e.hi, K, eps);
+    }
+#pragma unroll
+    for (int c = 0; c < CH; ++c) v[c] = norm_chunk<XT>(v[c], load_raw(rg, c * THREADS + tid), r);
+  }
 #pragma unroll
   for (int c = 0; c < CH; ++c) amax = chunk_absmax<XT>(amax, v[c]);
   for (int idx = CH * THREADS + tid; idx < nchunks; idx += THREADS) amax = chunk_absmax<XT>(amax, load(idx));
@@ -194,7 +339,6 @@ __global__ __launch_bounds__(THREADS) void w4_quant_kernel(const uint16_t* __res
   // row maximum: wave butterfly, then one value per wave through LDS
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
-  __shared__ float wave_max[THREADS / 64];
   if ((tid & 63) == 0) wave_max[tid >> 6] = amax;
   __syncthreads();
   amax = wave_max[0];
@@ -222,43 +366,63 @@ __global__ __launch_bounds__(THREADS) void w4_quant_kernel(const uint16_t* __res
   }
 }
 
-template <int THREADS, int CH>
+template <int THREADS, int CH, bool NORM>
 static void launch_quant_t(const void* x, int x_dtype, void* xq, int q_dtype, float* scales, int64_t M,
-                           int64_t K, hipStream_t stream) {
+                           int64_t K, const void* gamma, float eps, int exact, hipStream_t stream) {
   const dim3 grid((unsigned)M), block(THREADS);
   const uint16_t* xp = (const uint16_t*)x;
+  const uint16_t* gp = (const uint16_t*)gamma;
   uint8_t* qp = (uint8_t*)xq;
   if (x_dtype == W4_F16 && q_dtype == W4_I8)
-    hipLaunchKernelGGL((w4_quant_kernel<W4_F16, W4_I8, THREADS, CH>), grid, block, 0, stream, xp, qp, scales, K);
+    hipLaunchKernelGGL((w4_quant_kernel<W4_F16, W4_I8, THREADS, CH, NORM>), grid, block, 0, stream, xp, qp,
+                       scales, K, gp, eps, exact);
   else if (x_dtype == W4_F16)
-    hipLaunchKernelGGL((w4_quant_kernel<W4_F16, W4_FP8_E4M3, THREADS, CH>), grid, block, 0, stream, xp, qp, scales,
-                       K);
+    hipLaunchKernelGGL((w4_quant_kernel<W4_F16, W4_FP8_E4M3, THREADS, CH, NORM>), grid, block, 0, stream, xp, qp,
+                       scales, K, gp, eps, exact);
   else if (q_dtype == W4_I8)
-    hipLaunchKernelGGL((w4_quant_kernel<W4_BF16, W4_I8, THREADS, CH>), grid, block, 0, stream, xp, qp, scales, K);
+    hipLaunchKernelGGL((w4_quant_kernel<W4_BF16, W4_I8, THREADS, CH, NORM>), grid, block, 0, stream, xp, qp,
+                       scales, K, gp, eps, exact);
   else
-    hipLaunchKernelGGL((w4_quant_kernel<W4_BF16, W4_FP8_E4M3, THREADS, CH>), grid, block, 0, stream, xp, qp,
-                       scales, K);
+    hipLaunchKernelGGL((w4_quant_kernel<W4_BF16, W4_FP8_E4M3, THREADS, CH, NORM>), grid, block, 0, stream, xp,
+                       qp, scales, K, gp, eps, exact);
 }
 
-template <int THREADS>
+// 1024-thread workgroups keep at most 4 chunks per thread (128 VGPRs per
+// thread at that size; 8 or 12 chunks would spill), longer rows re-read
+// their tail.
+template <int THREADS, bool NORM>
 static void launch_quant_c(const void* x, int x_dtype, void* xq, int q_dtype, float* scales, int64_t M,
-                           int64_t K, hipStream_t stream) {
+                           int64_t K, const void* gamma, float eps, int exact, hipStream_t stream) {
   const int64_t per_thread = (K / 8 + THREADS - 1) / THREADS;
-  if (per_thread <= 4)
-    launch_quant_t<THREADS, 4>(x, x_dtype, xq, q_dtype, scales, M, K, stream);
+  if constexpr (THREADS > 256)
+    launch_quant_t<THREADS, 4, NORM>(x, x_dtype, xq, q_dtype, scales, M, K, gamma, eps, exact, stream);
+  else if (per_thread <= 4)
+    launch_quant_t<THREADS, 4, NORM>(x, x_dtype, xq, q_dtype, scales, M, K, gamma, eps, exact, stream);
   else if (per_thread <= 8)
-    launch_quant_t<THREADS, 8>(x, x_dtype, xq, q_dtype, scales, M, K, stream);
+    launch_quant_t<THREADS, 8, NORM>(x, x_dtype, xq, q_dtype, scales, M, K, gamma, eps, exact, stream);
   else
-    launch_quant_t<THREADS, kMaxChunks>(x, x_dtype, xq, q_dtype, scales, M, K, stream);
+    launch_quant_t<THREADS, kMaxChunks, NORM>(x, x_dtype, xq, q_dtype, scales, M, K, gamma, eps, exact, stream);
+}
+
+template <bool NORM>
+static void launch_quant_n(const void* x, int x_dtype, void* xq, int q_dtype, float* scales, int64_t M,
+                           int64_t K, const void* gamma, float eps, int exact, hipStream_t stream) {
+  // few rows: a whole CU per row
+  if (M <= 512 && K >= 8 * 1024)
+    launch_quant_c<1024, NORM>(x, x_dtype, xq, q_dtype, scales, M, K, gamma, eps, exact, stream);
+  else
+    launch_quant_c<256, NORM>(x, x_dtype, xq, q_dtype, scales, M, K, gamma, eps, exact, stream);
 }
 
 hipError_t launch_quant(const void* x, int x_dtype, void* xq, int q_dtype, float* scales, int64_t M,
                         int64_t K, hipStream_t stream) {
-  // few rows: a whole CU per row
-  if (M <= 512 && K >= 8 * 1024)
-    launch_quant_c<1024>(x, x_dtype, xq, q_dtype, scales, M, K, stream);
-  else
-    launch_quant_c<256>(x, x_dtype, xq, q_dtype, scales, M, K, stream);
+  launch_quant_n<false>(x, x_dtype, xq, q_dtype, scales, M, K, nullptr, 0.0f, 0, stream);
+  return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm_quant(const void* x, int x_dtype, const void* gamma, float eps, void* xq, int q_dtype,
+                                float* scales, int64_t M, int64_t K, int exact_sum, hipStream_t stream) {
+  launch_quant_n<true>(x, x_dtype, xq, q_dtype, scales, M, K, gamma, eps, exact_sum, stream);
   return hipGetLastError();
 }
 

@@ -34,7 +34,7 @@ def header_functions():
 
 def test_header_declares_the_documented_entry_points():
     names = header_functions()
-    for n in ("w4_prepack_B", "w4_quant_act_per_token", "w4a8_gemm", "w4a16_gemm"):
+    for n in ("w4_prepack_B", "w4_quant_act_per_token", "w4_rmsnorm_quant_per_token", "w4a8_gemm", "w4a16_gemm"):
         assert n in names
     assert sorted(names) == sorted(w4.EXPORTED_SYMBOLS)
 
@@ -79,6 +79,20 @@ def test_quant_validation(lib):
     assert q(None, 0, FAKE, 3, FAKE, 4, 64, None) == E_NULL
     assert q(MISALIGNED, 0, FAKE, 3, FAKE, 4, 64, None) == E_ALIGN
     assert q(None, 0, None, 3, None, 0, 64, None) == W4_OK        # M = 0: nothing to do
+
+
+def test_rmsnorm_quant_validation(lib):
+    f = lib.w4_rmsnorm_quant_per_token
+    assert f(FAKE, 7, FAKE, 1e-6, FAKE, 3, FAKE, 4, 64, None) == E_DTYPE
+    assert f(FAKE, 0, FAKE, 1e-6, FAKE, 5, FAKE, 4, 64, None) == E_DTYPE
+    assert f(FAKE, 0, FAKE, 1e-6, FAKE, 3, FAKE, 4, 60, None) == E_SHAPE
+    assert f(FAKE, 0, FAKE, 0.0, FAKE, 3, FAKE, 4, 64, None) == E_SHAPE
+    assert f(FAKE, 0, FAKE, -1.0, FAKE, 3, FAKE, 4, 64, None) == E_SHAPE
+    assert f(FAKE, 0, FAKE, float("nan"), FAKE, 3, FAKE, 4, 64, None) == E_SHAPE
+    assert f(FAKE, 0, FAKE, float("inf"), FAKE, 3, FAKE, 4, 64, None) == E_SHAPE
+    assert f(FAKE, 0, None, 1e-6, FAKE, 3, FAKE, 4, 64, None) == E_NULL
+    assert f(FAKE, 0, MISALIGNED, 1e-6, FAKE, 3, FAKE, 4, 64, None) == E_ALIGN
+    assert f(None, 0, None, 1e-6, None, 3, None, 0, 64, None) == W4_OK      # M = 0: nothing to do
 
 
 def _w4a8(lib, aq=FAKE, a_dtype=3, a_scales=FAKE, b=FAKE, wtype=0, bs=FAKE, s_dtype=2, gs=128,
@@ -147,6 +161,10 @@ def test_options_and_plans(lib):
         assert lib.w4_set_option(b"force_path", 5) == E_SHAPE
         assert w4.gemm_plan(1, 8192, 21760, -1, w4.I8)[0] == 1     # small M -> skinny
         assert w4.gemm_plan(4096, 8192, 21760, -1, w4.I8)[0] == 2  # large M -> tiled
+        assert lib.w4_set_option(b"norm_exact_sum", 2) == E_SHAPE
+        w4.set_option("norm_exact_sum", 1)
+        assert w4.get_option("norm_exact_sum") == 1
+        w4.set_option("norm_exact_sum", 0)
         w4.set_option("force_path", 1)
         with pytest.raises(w4.W4Error):
             w4.gemm_plan(64, 8192, 21760, -1, w4.I8)               # skinny handles M <= 16

@@ -107,6 +107,12 @@ def activations(M: int, K: int, dtype: str, seed: int, dist: str = "normal") -> 
     return x.to(TORCH_DTYPES[dtype]).contiguous()
 
 
+def norm_weight(K: int, dtype: str, seed: int) -> torch.Tensor:
+    """[K] RMSNorm weight ~U(0.25, 1.75) stored in ``dtype``."""
+    g = _gen(seed)
+    return (torch.rand((K,), generator=g, dtype=torch.float32) * 1.5 + 0.25).to(TORCH_DTYPES[dtype]).contiguous()
+
+
 def int4_codes(N: int, K: int, wtype: str, seed: int, lo: Optional[int] = None,
                hi: Optional[int] = None) -> torch.Tensor:
     """Logical 4-bit weight values as an int16 tensor [N, K].
