@@ -243,7 +243,7 @@ def rmsnorm_rows(x_bits: np.ndarray, x_dtype: str, gamma_bits: np.ndarray, eps: 
     eps64 = float(np.float32(eps))
     r = np.empty((M,), dtype=np.float32)
     for m in range(M):
-        ss = math.fsum(float(v) * float(v) for v in x[m])
+        ss = math.fsum((x[m] * x[m]).tolist())          # squares exact in float64
         var = ss / K + eps64
         r[m] = np.float32(1.0 / math.sqrt(var))
     y = (x.astype(np.float32) * r[:, None]) * g.astype(np.float32)[None, :]
