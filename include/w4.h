@@ -267,7 +267,8 @@ W4_API int w4a16_gemm_partials(const void* a, int a_dtype, const void* b_packed,
  *   "skinny_strips": 0 = automatic, 1 or 2 16-column strips per wave of the
  *                  small-M kernel (2 needs N % 32 == 0)
  *   "tiled_bm"   : 0 = automatic, 64 or 128 rows per tile of the tiled kernel
- *                  (128 only for int8 per-channel problems)
+ *                  (128 only for int8 and fp8 activations; its tile is
+ *                  128 x 256 for int8 per channel, 128 x 128 otherwise)
  *   "norm_exact_sum": 1 = w4_rmsnorm_quant_per_token always re-sums the squares
  *                  with error-free pair arithmetic (the path it otherwise takes
  *                  only when the fast sum cannot decide r); same results

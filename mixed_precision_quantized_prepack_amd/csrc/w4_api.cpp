@@ -107,7 +107,7 @@ int make_plan(int64_t M, int64_t N, int64_t K, bool grouped, int op, GemmPlan* p
   const int64_t KB = K / 128;
   const int cu = cu_count();
   plan->path = fp ? (int)fp : (M <= 16 ? PATH_SKINNY : PATH_TILED);
-  tiled_tile(op, grouped, &plan->bm, &plan->bn);
+  tiled_tile(op, grouped, 0, &plan->bm, &plan->bn);
   if (plan->path == PATH_SKINNY) {
     if (M > 16) return fail(W4_E_UNSUPPORTED, "the small-M kernel handles M <= 16 (M=%lld)", (long long)M);
     // strips of 16 columns per wave: two strips share one activation
@@ -138,13 +138,18 @@ int make_plan(int64_t M, int64_t N, int64_t K, bool grouped, int op, GemmPlan* p
                   smax);
     plan->splitk = (int)s;
   } else {
-    // int8 per-channel problems: 128-row tiles when they give at least two
-    // workgroups per CU, 64-row tiles otherwise
-    const bool tall_ok = op == OP_I8 && !grouped;
+    // 8-bit operands: 128-row tiles when there are enough of them (int8
+    // per channel: two workgroups per CU; grouped and fp8, whose tall tile
+    // is 128 x 128: one), 64 x 256 tiles otherwise
+    const bool byte = op == OP_I8 || op == OP_FP8;
     const int64_t fbm = g_tiled_bm.load();
-    if (tall_ok) {
-      const int64_t tiles128 = ((M + 127) / 128) * ((N + plan->bn - 1) / plan->bn);
-      plan->bm = fbm ? (int)fbm : (tiles128 >= 2LL * cu ? 128 : 64);
+    if (byte) {
+      int tall_bm, tall_bn;
+      tiled_tile(op, grouped, 1, &tall_bm, &tall_bn);
+      const int64_t tall_tiles = ((M + tall_bm - 1) / tall_bm) * ((N + tall_bn - 1) / tall_bn);
+      const int64_t need = (op == OP_I8 && !grouped) ? 2LL * cu : (int64_t)cu;
+      const bool tall = fbm ? fbm == 128 : tall_tiles >= need;
+      tiled_tile(op, grouped, tall ? 1 : 0, &plan->bm, &plan->bn);
     } else if (fbm && fbm != plan->bm) {
       return fail(W4_E_SHAPE, "tiled_bm=%lld is not available for this problem", (long long)fbm);
     }

@@ -979,11 +979,14 @@ __global__ __launch_bounds__(256) void w4_splitk_reduce(GemmArgs p, int splitk) 
 // ===========================================================================
 // Host-side launchers.
 // ===========================================================================
-void tiled_tile(int op, bool grouped, int* bm, int* bn) {
-  // default (tallest) tile; int8 per-channel problems may also use bm = 64
+void tiled_tile(int op, bool grouped, int tall, int* bm, int* bn) {
+  // 8-bit operands: 64 x 256, or the tall tile, 128 x 256 for int8 per
+  // channel and 128 x 128 otherwise (2 n-blocks per wave: grouped and fp8
+  // waves spend more VALU per weight block, which 8 tile rows amortise)
   if (op == OP_I8 || op == OP_FP8) {
-    *bm = (op == OP_I8 && !grouped) ? 128 : 64;
-    *bn = 256;
+    const bool wide = op == OP_I8 && !grouped;
+    *bm = tall ? 128 : 64;
+    *bn = (tall && !wide) ? 128 : 256;
   } else {
     *bm = 64;
     *bn = 128;
@@ -1014,8 +1017,6 @@ static hipError_t launch_typed(const GemmArgs& args, const GemmPlan& plan, hipSt
     return hipGetLastError();
   }
   constexpr bool kByte = (OP == OP_I8 || OP == OP_FP8);
-  constexpr int NT = kByte ? 4 : 2;
-  const int64_t BN = NT * 64;
   auto finish = [&]() -> hipError_t {
     hipError_t e = hipGetLastError();
     // grouped partials are stored by the tiled kernel itself
@@ -1027,9 +1028,10 @@ static hipError_t launch_typed(const GemmArgs& args, const GemmPlan& plan, hipSt
                        plan.splitk);
     return hipGetLastError();
   };
-  auto launch = [&](auto mt_tag) {
+  auto launch = [&](auto mt_tag, auto nt_tag) {
     constexpr int MT = decltype(mt_tag)::value;
-    const int64_t BM = MT * 16;
+    constexpr int NT = decltype(nt_tag)::value;
+    const int64_t BM = MT * 16, BN = NT * 64;
     const dim3 grid((unsigned)((args.M + BM - 1) / BM), (unsigned)((args.N + BN - 1) / BN),
                     (unsigned)plan.splitk);
     const bool part = args.mode == MODE_PARTIALS;
@@ -1049,13 +1051,16 @@ static hipError_t launch_typed(const GemmArgs& args, const GemmPlan& plan, hipSt
                            args, 1);
     }
   };
-  if constexpr (OP == OP_I8 && !GROUPED) {
-    if (plan.bm == 128) {
-      launch(std::integral_constant<int, 8>{});
-      return finish();
-    }
+  if constexpr (kByte) {
+    if (plan.bm == 128 && plan.bn == 256)
+      launch(std::integral_constant<int, 8>{}, std::integral_constant<int, 4>{});
+    else if (plan.bm == 128)
+      launch(std::integral_constant<int, 8>{}, std::integral_constant<int, 2>{});
+    else
+      launch(std::integral_constant<int, 4>{}, std::integral_constant<int, 4>{});
+  } else {
+    launch(std::integral_constant<int, 4>{}, std::integral_constant<int, 2>{});
   }
-  launch(std::integral_constant<int, 4>{});
   return finish();
 }
 

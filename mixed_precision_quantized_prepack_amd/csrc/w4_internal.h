@@ -46,7 +46,7 @@ struct GemmPlan {
 };
 
 // Block tile of the tiled kernel for an operand class / grouping.
-void tiled_tile(int op, bool grouped, int* bm, int* bn);
+void tiled_tile(int op, bool grouped, int tall, int* bm, int* bn);
 
 hipError_t launch_prepack(const void* w_logical, void* w_packed, int64_t N, int64_t K, int operand,
                           hipStream_t stream);

@@ -153,6 +153,11 @@ def test_plan_choices(lib):
     assert w4.gemm_plan(1, 22016, 4096, 128, w4.I8)[3] == 16
     assert w4.gemm_plan(16, 22016, 4096, 128, w4.I8)[3] == 32
     assert w4.gemm_plan(16, 4096, 11008, 128, w4.I8)[3] == 16
+    # grouped int8 and fp8: 128 x 128 tiles once there is one per CU, else 64 x 256
+    assert w4.gemm_plan(1024, 22016, 4096, 128, w4.I8)[2:] == (128, 128)
+    assert w4.gemm_plan(128, 22016, 4096, 128, w4.I8)[2:] == (64, 256)
+    assert w4.gemm_plan(8192, 28672, 8192, 128, w4.FP8_E4M3)[1:] == (1, 128, 128)
+    assert w4.gemm_plan(32, 28672, 8192, 128, w4.FP8_E4M3)[2:] == (64, 256)
 
 
 def test_options_and_plans(lib):

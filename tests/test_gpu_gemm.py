@@ -23,14 +23,16 @@ pytestmark = pytest.mark.gpu
 
 
 @contextlib.contextmanager
-def options(path=0, splitk=0):
+def options(path=0, splitk=0, bm=0):
     w4.set_option("force_path", path)
     w4.set_option("splitk", splitk)
+    w4.set_option("tiled_bm", bm)
     try:
         yield
     finally:
         w4.set_option("force_path", 0)
         w4.set_option("splitk", 0)
+        w4.set_option("tiled_bm", 0)
 
 
 def run_w4a8(dc: DeviceCase):
@@ -63,6 +65,20 @@ def test_int8_partials_bit_exact(wl, path, M, split, wtype):
     assert np.array_equal(part.cpu().numpy().astype(np.int64), want)
 
 
+@pytest.mark.parametrize("wl", ["w4a8_i8_pc_256x512", "w4a8_i8_g128_o"])
+@pytest.mark.parametrize("M,split", [(17, 1), (130, 1), (200, 3), (256, 2)])
+def test_int8_partials_bit_exact_tall_tiles(wl, M, split):
+    """128-row tiles (128 x 256 per channel, 128 x 128 grouped), ragged M and N."""
+    dc = DeviceCase(wl, M, N=272, K=640, seed_base=M * 11 + 5)
+    packed = w4.prepack_B(dc.w_logical, "i8")
+    aq, _ = w4.quant_act_per_token(dc.a, "i8")
+    gs = -1 if dc.gs == dc.K else dc.gs
+    with options(2, split, 128):
+        part = w4.w4a8_gemm_partials(aq, packed, dc.N, gs)
+    want = O.w4a8_group_partials(aq.cpu().numpy(), "i8", dc.case.w_logical.numpy(), dc.K, "int4", dc.gs)
+    assert np.array_equal(part.cpu().numpy().astype(np.int64), want)
+
+
 def test_int8_partials_window():
     dc = DeviceCase("w4a8_i8_g128_o", 40, N=512, K=1024, seed_base=3)
     packed = w4.prepack_B(dc.w_logical, "i8")
@@ -74,12 +90,12 @@ def test_int8_partials_window():
     assert np.array_equal(part.cpu().numpy().astype(np.int64), want)
 
 
-@pytest.mark.parametrize("path,M,split", [(1, 5, 4), (2, 70, 2)])
-def test_fp8_partials_within_bound(path, M, split):
-    dc = DeviceCase("w4a8_fp8_g128_28672x8192", M, N=256, K=512, seed_base=11)
+@pytest.mark.parametrize("path,M,split,bm", [(1, 5, 4, 0), (2, 70, 2, 64), (2, 70, 2, 128), (2, 150, 1, 128)])
+def test_fp8_partials_within_bound(path, M, split, bm):
+    dc = DeviceCase("w4a8_fp8_g128_28672x8192", M, N=272, K=512, seed_base=11)
     packed = w4.prepack_B(dc.w_logical, "i8")
     aq, _ = w4.quant_act_per_token(dc.a, "fp8")
-    with options(path, split):
+    with options(path, split, bm):
         part = w4.w4a8_gemm_partials(aq, packed, dc.N, 128).cpu().numpy().astype(np.float64)
     codes = aq.cpu().numpy()
     P = O.w4a8_group_partials(codes, "fp8", dc.case.w_logical.numpy(), dc.K, "int4", 128)
@@ -135,15 +151,16 @@ def test_w4a8_outputs(wl, wtype, M, bias):
 
 
 @pytest.mark.parametrize("wl", ["w4a8_i8_pc_256x512", "w4a8_fp8_g128_28672x8192", "w4a8_i8_g128_down"])
-@pytest.mark.parametrize("path,split", [(1, 1), (1, 8), (2, 1), (2, 2), (2, 5)])
-def test_w4a8_forced_paths_agree(wl, path, split):
-    M = 16 if path == 1 else 48
-    dc = DeviceCase(wl, M, N=512, K=1280, seed_base=77)
-    with options(path, split):
+@pytest.mark.parametrize("path,split,bm", [(1, 1, 0), (1, 8, 0), (2, 1, 64), (2, 2, 64), (2, 5, 64),
+                                           (2, 1, 128), (2, 3, 128)])
+def test_w4a8_forced_paths_agree(wl, path, split, bm):
+    M = 16 if path == 1 else (48 if bm == 64 else 150)
+    dc = DeviceCase(wl, M, N=528, K=1280, seed_base=77)
+    with options(path, split, bm):
         out, *_ = run_w4a8(dc)
     codes, sa = dc.oracle_quant()
     assert_w4a8(out, dc.oracle_w4a8(codes, sa), dc.wl.out_dtype, dc.wl.q_dtype, dc.G,
-                label=f"{wl} path={path} split={split}")
+                label=f"{wl} path={path} split={split} bm={bm}")
 
 
 @pytest.mark.parametrize("a_dtype", ["bf16", "f16"])
