@@ -108,14 +108,25 @@ int make_plan(int64_t M, int64_t N, int64_t K, bool grouped, int op, GemmPlan* p
   const int cu = cu_count();
   plan->path = fp ? (int)fp : (M <= 16 ? PATH_SKINNY : PATH_TILED);
   tiled_tile(op, grouped, 0, &plan->bm, &plan->bn);
+  // strips of 16 columns per wave of the small-M kernel: two strips share
+  // one activation fragment.  Grouped problems take two only when the
+  // fragment is worth sharing (M >= 8) and N leaves enough workgroups.
+  const int64_t fns = g_skinny_strips.load();
+  const bool two = N % 32 == 0 && (!grouped || (M >= 8 && N >= 8192));
+  int64_t ns = fns ? fns : (two ? 2 : 1);
+  const int64_t groups = grouped ? KB : 1;
+  if (plan->path == PATH_SKINNY && skinny_table_bytes(op, grouped, groups, (int)ns) > kSkinnyTableMax) {
+    // the scale / zero-point tables would not fit the small-M kernel's LDS
+    if (!fns && ns == 2 && skinny_table_bytes(op, grouped, groups, 1) <= kSkinnyTableMax) {
+      ns = 1;
+    } else if (fp || fns) {
+      return fail(W4_E_UNSUPPORTED, "the small-M kernel's LDS tables do not fit K=%lld", (long long)K);
+    } else {
+      plan->path = PATH_TILED;
+    }
+  }
   if (plan->path == PATH_SKINNY) {
     if (M > 16) return fail(W4_E_UNSUPPORTED, "the small-M kernel handles M <= 16 (M=%lld)", (long long)M);
-    // strips of 16 columns per wave: two strips share one activation
-    // fragment.  Grouped problems take two only when the fragment is worth
-    // sharing (M >= 8) and N leaves enough workgroups.
-    const int64_t fns = g_skinny_strips.load();
-    const bool two = N % 32 == 0 && (!grouped || (M >= 8 && N >= 8192));
-    const int64_t ns = fns ? fns : (two ? 2 : 1);
     if (N % (16 * ns))
       return fail(W4_E_SHAPE, "small-M kernel with %lld strips per wave needs N %% %lld == 0", (long long)ns,
                   (long long)(16 * ns));

@@ -197,8 +197,11 @@ __device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_
 #ifndef W4_SKINNY_U16
 #define W4_SKINNY_U16 1
 #endif
-#ifndef W4_SKINNY_UG
-#define W4_SKINNY_UG 1   // grouped problems also prefetch per-block scales
+#ifndef W4_SKINNY_UG1
+#define W4_SKINNY_UG1 2   // grouped, one strip per wave
+#endif
+#ifndef W4_SKINNY_UG2
+#define W4_SKINNY_UG2 1   // grouped, two strips per wave
 #endif
 #ifndef W4_SKINNY_WPOLICY
 #define W4_SKINNY_WPOLICY 2
@@ -219,6 +222,10 @@ __device__ __forceinline__ float word_to_f32(uint32_t w, int dtype, uint32_t i) 
   return dtype == W4_F32 ? __uint_as_float(w) : (dtype == W4_F16 ? f16 : bf);
 }
 
+// s_waitcnt immediate (gfx9 encoding): at most `vm` vector-memory operations
+// outstanding, every LDS operation done, export count left free.
+constexpr int waitcnt_vm_lgkm0(int vm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4); }
+
 // Small-M kernel (M <= 16).
 //
 // Workgroup = S waves over the same NS 16-column strips of W; the K blocks are
@@ -231,12 +238,20 @@ __device__ __forceinline__ float word_to_f32(uint32_t w, int dtype, uint32_t i) 
 // MFMAs of batch i.  Rows past M and blocks past K are buffer loads with
 // out-of-range offsets: they read as zero without memory traffic.  The
 // waves' results are summed through LDS in wave order.
+//
+// Group scales (times 1/16 for int8) and W4A16 zero-point terms are staged
+// once per workgroup into an LDS table, group-major ([strip][group][row]),
+// while the first batch is in flight: a lane then reads the four values of
+// its D rows for a K block with one 16-byte LDS read, instead of a 64-lane
+// gather from memory per block (which costs the address pipeline as much as
+// the block's weights).  The table's size is set at launch.
 template <int OP, bool GROUPED, bool FLIP, int NS, bool PARTIALS>
 __global__ __launch_bounds__(64 * skinny_max_waves(OP, GROUPED)) void w4_gemm_skinny(GemmArgs p, int S) {
   using Acc = typename OpTraits<OP>::Acc;
   constexpr int EB = OpTraits<OP>::kElemBytes;
   constexpr int AV = act_vecs<OP>();
-  constexpr int U = GROUPED ? W4_SKINNY_UG : (EB == 1) ? W4_SKINNY_U8 : W4_SKINNY_U16;  // K blocks per batch
+  constexpr int U = GROUPED ? (NS == 1 ? W4_SKINNY_UG1 : W4_SKINNY_UG2)
+                            : (EB == 1) ? W4_SKINNY_U8 : W4_SKINNY_U16;   // K blocks per batch
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -251,7 +266,10 @@ __global__ __launch_bounds__(64 * skinny_max_waves(OP, GROUPED)) void w4_gemm_sk
       make_rsrc(reinterpret_cast<const uint8_t*>(p.b) + nb0 * KB * 1024, (int64_t)NS * KB * 1024);
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a, p.M * p.K * EB);
   const int sbytes = p.s_dtype == W4_F32 ? 4 : 2;
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.s, p.N * p.G * sbytes);
+  // scales are absent (null) in the partials entry points: an empty buffer
+  // (a product, not a branch: a branch here would wait for the kernel
+  // arguments before anything else is issued)
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.s, (int64_t)(p.s != nullptr) * p.N * p.G * sbytes);
   const __amdgpu_buffer_rsrc_t rz = make_rsrc(p.z, p.z ? p.N * p.G * 2 : 0);
   const uint32_t w_lane = (uint32_t)lane * 16;
   const uint32_t a_lane = (uint32_t)((r * p.K + kq * 32) * EB);
@@ -277,6 +295,15 @@ __global__ __launch_bounds__(64 * skinny_max_waves(OP, GROUPED)) void w4_gemm_sk
   const uint32_t ep_s = load_word(rs, p.s_dtype, (uint32_t)ep_n, !GROUPED && ep_in);
   const uint32_t ep_a = load_word(rsa, W4_F32, (uint32_t)ep_m, ep_in && p.a_scales);
   const uint32_t ep_b = load_word(rb, p.out_dtype, (uint32_t)ep_n, ep_in && p.bias);
+  // fp16 W4A16 per channel: the zero-point of this lane's operand row
+  float zrow[NS];
+  if constexpr (OP == OP_F16 && !GROUPED) {
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      const uint32_t zi = (uint32_t)((nb0 + j) * 16 + r) * p.G;
+      zrow[j] = p.z ? word_to_f32(load_word(rz, zdt, zi, true), zdt, zi) : 8.0f;
+    }
+  }
   uint32_t zpc[NS][4];
   if constexpr (OP == OP_BF16 && !GROUPED) {
 #pragma unroll
@@ -288,18 +315,20 @@ __global__ __launch_bounds__(64 * skinny_max_waves(OP, GROUPED)) void w4_gemm_sk
 
   u32x4 wv[2][U][NS];
   u32x4 av[2][U][AV];
-  // Per-group side inputs, one word per lane for its operand row r (the D
-  // rows 4 kq + i a lane folds get theirs from lanes 4 kq + i by a lane
-  // permute): group scale, bf16 W4A16 zero-point, fp16 W4A16 zero-point.
-  uint32_t sc[2][U][NS];
-  uint32_t zd[2][U][NS];
-  uint32_t zo[2][U][NS];
+  // LDS tables: tsc = group scales (grouped), tz = 128 + z (grouped bf16
+  // W4A16) or z (grouped fp16 W4A16), each [NS][G][16] fp32.
+  constexpr bool kTab = skinny_tables(OP, GROUPED) > 0;
+  extern __shared__ __attribute__((aligned(16))) float skinny_tab[];
+  // (each table is followed by a 16-float pad that takes the stores of
+  // staging slots past its end)
+  float* const tsc = skinny_tab;
+  float* const tz = skinny_tab + (GROUPED ? NS * p.G * 16 + 16 : 0);
 
   auto load_batch = [&](int buf, int kb) {   // kb: this wave's batch index in blocks of S
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int k = wave + (kb + u) * S;     // K block
-      const bool in = k < KB;
+      const bool in = k < KB && wave < S;    // waves past S only finalise
 #pragma unroll
       for (int j = 0; j < NS; ++j)
         wv[buf][u][j] = __builtin_amdgcn_raw_buffer_load_b128(
@@ -307,17 +336,19 @@ __global__ __launch_bounds__(64 * skinny_max_waves(OP, GROUPED)) void w4_gemm_sk
 #pragma unroll
       for (int a = 0; a < AV; ++a)
         av[buf][u][a] = buffer_load16(ra, in ? a_lane + (uint32_t)(k * 128 * EB + 16 * a) : kOutOfRange);
-      const int g = GROUPED ? k : 0;
-#pragma unroll
-      for (int j = 0; j < NS; ++j) {
-        const uint32_t idx = (uint32_t)((nb0 + j) * 16 + r) * p.G + g;
-        if constexpr (GROUPED) sc[buf][u][j] = load_word(rs, p.s_dtype, idx, in && !partials);
-        if constexpr (GROUPED && OP == OP_BF16) zd[buf][u][j] = load_word(rz, zdt, idx, in && p.z);
-        if constexpr (OP == OP_F16) zo[buf][u][j] = load_word(rz, zdt, idx, in && p.z);
-      }
     }
   };
-  auto compute_batch = [&](int buf, int kb) {
+  auto compute_batch = [&](int buf, int kb, bool pin) {
+    // pin: loads issued before this point stay before it, and the weight
+    // words enter an asm statement here, so none of this batch's work moves
+    // above the previous refill (which would make its wait cover that refill)
+    if (pin) {
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int j = 0; j < NS; ++j) asm volatile("" : "+v"(wv[buf][u][j]));
+    }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int k = wave + (kb + u) * S;
@@ -327,7 +358,7 @@ __global__ __launch_bounds__(64 * skinny_max_waves(OP, GROUPED)) void w4_gemm_sk
       for (int j = 0; j < NS; ++j) {
         f16x2 nz = {};
         if constexpr (OP == OP_F16) {
-          const float z = p.z ? word_to_f32(zo[buf][u][j], zdt, (uint32_t)((nb0 + j) * 16 + r) * p.G + g) : 8.0f;
+          const float z = GROUPED ? (k < KB ? tz[(j * p.G + g) * 16 + r] : 8.0f) : zrow[j];
           const _Float16 h = (_Float16)(-(1024.0f + z));
           nz = f16x2{h, h};
         }
@@ -340,25 +371,19 @@ __global__ __launch_bounds__(64 * skinny_max_waves(OP, GROUPED)) void w4_gemm_sk
 #pragma unroll
           for (int j = 0; j < NS; ++j) {
             const int64_t n_d = (nb0 + j) * 16 + 4 * kq;
-            // this lane's row r values, then those of D rows 4 kq + i
-            const uint32_t idx = (uint32_t)((nb0 + j) * 16 + r) * p.G + g;
-            float sv = word_to_f32(sc[buf][u][j], p.s_dtype, idx);
-            if constexpr (OP == OP_I8) sv *= 0.0625f;   // the operand holds 16 w
-            float zv = 0.0f;
-            if constexpr (OP == OP_BF16) zv = 128.0f + (p.z ? word_to_f32(zd[buf][u][j], zdt, idx) : 8.0f);
+            // the group's scales and (bf16) 128 + z terms of D rows 4 kq + i
+            const int slot = (j * p.G + g) * 16 + 4 * kq;
+            const f32x4 sv = *reinterpret_cast<const f32x4*>(&tsc[slot]);
+            f32x4 zc = {};
+            if constexpr (OP == OP_BF16) zc = *reinterpret_cast<const f32x4*>(&tz[slot]);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              const int src = (4 * kq + i) * 4;   // byte address of lane 4 kq + i
-              const float zc = (OP == OP_BF16)
-                                   ? __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(zv)))
-                                   : 0.0f;
-              const float pv = partial_value<OP>(acc[j], ones, zc, i);
+              const float pv = partial_value<OP>(acc[j], ones, zc[i], i);
               if (partials) {
                 if (in_window(p, r, n_d + i)) store_partial<OP>(p, g, r, n_d + i, pv, int_partial<OP>(acc[j], i));
               } else {
-                const float si = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(sv)));
                 const float pf = (OP == OP_I8) ? (float)acc[j][i] : pv;
-                tot[j][i] = fmaf(pf, si, tot[j][i]);
+                tot[j][i] = fmaf(pf, sv[i], tot[j][i]);
               }
             }
           }
@@ -370,24 +395,94 @@ __global__ __launch_bounds__(64 * skinny_max_waves(OP, GROUPED)) void w4_gemm_sk
     }
   };
 
-  // Whole pairs of batches, then one last pair whose second batch may lie
-  // (partly) past K: its loads read zero and add nothing.  The loop has no
-  // exit in its middle, so the loads of the next batch stay in flight across
-  // the back edge instead of being waited for at the loop head.
-  if (wave < S) {
-    const int nbatch = (KB - wave + S - 1) / S;   // K blocks of this wave
-    load_batch(0, 0);
-    int kb = 0;
-    for (; kb + 2 * U < nbatch; kb += 2 * U) {
-      load_batch(1, kb + U);
-      compute_batch(0, kb);
-      load_batch(0, kb + 2 * U);
-      compute_batch(1, kb + U);
+  // Table staging (grouped problems; the first round of loads is issued
+  // before the first two batches, so that waiting for it does not wait for
+  // the batches): thread t takes row t mod 16 NS of the workgroup's rows and
+  // groups t / (16 NS) + i step, i < 8, so consecutive threads write
+  // consecutive table words.  The stores are branch-free (a branch around a
+  // store would make the compiler's wait for its load cover the batches
+  // issued after it): groups past the last go to the table's pad.
+  const int G = p.G;
+  const int tab_total = kTab ? NS * 16 * G : 0;
+  constexpr int RW = 16 * NS;
+  const int srow = (int)threadIdx.x % RW;
+  const int gstep = (int)blockDim.x / RW;   // blockDim.x is a multiple of 64
+  const int gfirst = (int)threadIdx.x / RW;
+  uint32_t tws[8], twz[8];
+  auto stage_load = [&](int g0) {
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const int g = g0 + gfirst + t * gstep;
+      const uint32_t idx = (uint32_t)((nb0 * 16 + srow) * G + g);
+      if constexpr (GROUPED) tws[t] = load_word(rs, p.s_dtype, idx, g < G && !partials);
+      if constexpr (OP == OP_BF16 || OP == OP_F16) twz[t] = load_word(rz, zdt, idx, g < G && p.z);
     }
-    load_batch(1, kb + U);
-    compute_batch(0, kb);
-    compute_batch(1, kb + U);
+  };
+  auto stage_store = [&](int g0) {
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const int g = g0 + gfirst + t * gstep;
+      const uint32_t idx = (uint32_t)((nb0 * 16 + srow) * G + g);
+      const int slot = g < G ? ((srow >> 4) * G + g) * 16 + (srow & 15) : tab_total + (srow & 15);
+      if constexpr (GROUPED) {
+        float sv = word_to_f32(tws[t], p.s_dtype, idx);
+        if constexpr (OP == OP_I8) sv *= 0.0625f;   // the operand holds 16 w
+        tsc[slot] = sv;
+      }
+      if constexpr (OP == OP_BF16) tz[slot] = 128.0f + (p.z ? word_to_f32(twz[t], zdt, idx) : 8.0f);
+      if constexpr (OP == OP_F16) tz[slot] = p.z ? word_to_f32(twz[t], zdt, idx) : 8.0f;
+    }
+  };
+  if constexpr (kTab) {
+    stage_load(0);
+    asm volatile("" ::: "memory");
+    load_batch(0, 0);
+    load_batch(1, U);
+    asm volatile("" ::: "memory");
+    stage_store(0);
+    for (int g0 = 8 * gstep; g0 < G; g0 += 8 * gstep) {
+      stage_load(g0);
+      stage_store(g0);
+    }
+    // LDS writes done and visible; the two batches stay in flight
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(63));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    // Both buffers are in flight: each step computes a buffer and refills it
+    // with the batch two ahead (past K: zeros, no traffic).
+    if (wave < S) {
+      const int nbatch = (KB - wave + S - 1) / S;   // K blocks of this wave
+      int kb = 0;
+      for (; kb + 2 * U < nbatch; kb += 2 * U) {
+        compute_batch(0, kb, true);
+        load_batch(0, kb + 2 * U);
+        compute_batch(1, kb + U, true);
+        load_batch(1, kb + 3 * U);
+      }
+      compute_batch(0, kb, true);
+      compute_batch(1, kb + U, true);
+    }
+  } else {
+    // Each step issues the next batch, then computes the current one.
+    if (wave < S) {
+      const int nbatch = (KB - wave + S - 1) / S;   // K blocks of this wave
+      load_batch(0, 0);
+      int kb = 0;
+      for (; kb + 2 * U < nbatch; kb += 2 * U) {
+        load_batch(1, kb + U);
+        compute_batch(0, kb, false);
+        load_batch(0, kb + 2 * U);
+        compute_batch(1, kb + U, false);
+      }
+      load_batch(1, kb + U);
+      compute_batch(0, kb, false);
+      compute_batch(1, kb + U, false);
+    }
   }
+  // (either way: whole pairs of batches, then the last pair, whose second
+  // batch may lie past K; a loop without an exit in its middle keeps the next
+  // batch's loads in flight across the back edge)
 
   // Sum the waves' results in wave order through LDS.
   __shared__ uint32_t red[skinny_max_waves(OP, GROUPED)][NS][64][4];
@@ -522,9 +617,6 @@ __device__ __forceinline__ void pin_words(uint32_t* e) {
                  "+v"(e[i + 5]), "+v"(e[i + 6]), "+v"(e[i + 7])::"memory");
 }
 
-// s_waitcnt immediate (gfx9 encoding): at most `vm` vector-memory operations
-// outstanding, every LDS operation done, export count left free.
-constexpr int waitcnt_vm_lgkm0(int vm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4); }
 
 // Block-wide barrier that first waits until at most VM of this wave's vector
 // memory operations are outstanding.  The direct-to-LDS loads that fill a
@@ -587,7 +679,10 @@ __global__ __launch_bounds__(256, 2) void w4_gemm_tiled(GemmArgs p, int splitk) 
   const __amdgpu_buffer_rsrc_t rw =
       make_rsrc(reinterpret_cast<const uint8_t*>(p.b) + nb_base * KB * 1024, (NB - nb_base) * KB * 1024);
   const int sbytes = p.s_dtype == W4_F32 ? 4 : 2;
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.s, p.N * p.G * sbytes);
+  // scales are absent (null) in the partials entry points: an empty buffer
+  // (a product, not a branch: a branch here would wait for the kernel
+  // arguments before anything else is issued)
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.s, (int64_t)(p.s != nullptr) * p.N * p.G * sbytes);
   const __amdgpu_buffer_rsrc_t rz = make_rsrc(p.z, p.z ? p.N * p.G * 2 : 0);
   const int zdt = p.out_dtype;  // W4A16: zero-points in the activation dtype
 
@@ -1003,16 +1098,17 @@ static hipError_t launch_typed(const GemmArgs& args, const GemmPlan& plan, hipSt
     const unsigned threads = 64u * (unsigned)(S > 4 * ns ? S : 4 * ns);
     const dim3 grid((unsigned)(args.N / plan.bn));
     const bool part = args.mode == MODE_PARTIALS;
+    const size_t tab = (size_t)skinny_table_bytes(OP, GROUPED, args.G, ns);   // checked by the plan
     if (ns == 2) {
       if (part)
-        hipLaunchKernelGGL((w4_gemm_skinny<OP, GROUPED, FLIP, 2, true>), grid, dim3(threads), 0, stream, args, S);
+        hipLaunchKernelGGL((w4_gemm_skinny<OP, GROUPED, FLIP, 2, true>), grid, dim3(threads), tab, stream, args, S);
       else
-        hipLaunchKernelGGL((w4_gemm_skinny<OP, GROUPED, FLIP, 2, false>), grid, dim3(threads), 0, stream, args, S);
+        hipLaunchKernelGGL((w4_gemm_skinny<OP, GROUPED, FLIP, 2, false>), grid, dim3(threads), tab, stream, args, S);
     } else {
       if (part)
-        hipLaunchKernelGGL((w4_gemm_skinny<OP, GROUPED, FLIP, 1, true>), grid, dim3(threads), 0, stream, args, S);
+        hipLaunchKernelGGL((w4_gemm_skinny<OP, GROUPED, FLIP, 1, true>), grid, dim3(threads), tab, stream, args, S);
       else
-        hipLaunchKernelGGL((w4_gemm_skinny<OP, GROUPED, FLIP, 1, false>), grid, dim3(threads), 0, stream, args, S);
+        hipLaunchKernelGGL((w4_gemm_skinny<OP, GROUPED, FLIP, 1, false>), grid, dim3(threads), tab, stream, args, S);
     }
     return hipGetLastError();
   }

@@ -39,6 +39,18 @@ constexpr int skinny_max_waves(int op, bool grouped) {
   return (op == OP_I8 || op == OP_FP8) && !grouped ? 16 : 8;
 }
 
+// LDS tables of the small-M kernel (grouped problems only): group scales,
+// and for W4A16 the zero-point terms, each [strips][groups][16] fp32
+// followed by a 16-float pad.
+constexpr int skinny_tables(int op, bool grouped) {
+  return grouped ? ((op == OP_BF16 || op == OP_F16) ? 2 : 1) : 0;
+}
+inline int64_t skinny_table_bytes(int op, bool grouped, int64_t groups, int strips) {
+  return (int64_t)skinny_tables(op, grouped) * (strips * groups * 16 + 16) * 4;
+}
+// Largest table the small-M kernel stages; larger problems use the tiled kernel.
+constexpr int64_t kSkinnyTableMax = 48 * 1024;
+
 struct GemmPlan {
   int path;    // PATH_SKINNY or PATH_TILED
   int splitk;  // skinny: waves per workgroup splitting K; tiled: K splits across workgroups

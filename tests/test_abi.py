@@ -158,6 +158,14 @@ def test_plan_choices(lib):
     assert w4.gemm_plan(128, 22016, 4096, 128, w4.I8)[2:] == (64, 256)
     assert w4.gemm_plan(8192, 28672, 8192, 128, w4.FP8_E4M3)[1:] == (1, 128, 128)
     assert w4.gemm_plan(32, 28672, 8192, 128, w4.FP8_E4M3)[2:] == (64, 256)
+    # a grouped K whose LDS scale table would not fit the small-M kernel: tiled
+    assert w4.gemm_plan(1, 8192, 131072, 128, w4.I8)[0] == 2
+    try:
+        w4.set_option("force_path", 1)
+        with pytest.raises(w4.W4Error):
+            w4.gemm_plan(1, 8192, 131072, 128, w4.I8)
+    finally:
+        w4.set_option("force_path", 0)
 
 
 def test_options_and_plans(lib):
