@@ -154,6 +154,26 @@ def prepack_B(w_logical: np.ndarray, N: int, K: int, operand: str,
     return words.view(np.uint8).copy()
 
 
+def exllama_to_logical(words: np.ndarray, N: int, K: int) -> np.ndarray:
+    """ExLlama-shuffled int32 words [N, K/8] -> logical [N, K/2] bytes.
+
+    vLLM API page "...mixed_precision.rdna_hybrid_w4a16", docstring of
+    ``_triton_w4a16_skinny_fmt_kernel``: each word holds 8 consecutive k
+    (k = 8 w + j) with k-offset j at bit (j // 2) * 4 + (j % 2) * 16.
+    """
+    W = np.asarray(words).view(np.uint32).reshape(N, K // 8)
+    vals = np.empty((N, K), dtype=np.uint8)
+    for j in range(8):
+        vals[:, j::8] = (W >> np.uint32((j // 2) * 4 + (j % 2) * 16)) & np.uint32(0xF)
+    return (vals[:, 0::2] | (vals[:, 1::2] << 4)).astype(np.uint8)
+
+
+def prepack_B_from_exllama(words: np.ndarray, N: int, K: int, operand: str) -> np.ndarray:
+    """PB-v1 bytes of a weight given as ExLlama-shuffled words [N, K/8]: the
+    same bytes as prepacking its logical form."""
+    return prepack_B(exllama_to_logical(words, N, K), N, K, operand)
+
+
 def unprepack_B(packed: np.ndarray, N: int, K: int, operand: str) -> np.ndarray:
     """PB-v1 bytes -> logical [N, K/2] bytes, walking the packed words.
 

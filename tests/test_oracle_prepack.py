@@ -154,3 +154,53 @@ def test_public_prepack_entry():
     N, K = 16, 128
     w = _random_logical(N, K, 3)
     assert np.array_equal(oracle.prepack_B(w, N, K, "i8"), O.prepack_B(w, N, K, "i8"))
+
+
+def test_exllama_unshuffle_matches_printed_packing():
+    """The golden words were evaluated by hand from the printed packing
+    expression; unshuffling each must give back its eight values in k order."""
+    with open(os.path.join(GOLDEN, "exllama_word.json")) as f:
+        g = json.load(f)
+    N, K = 1, 8
+    for case in g["cases"]:
+        word = np.array([int(case["expected_word"], 16)], dtype=np.uint32)
+        logical = O.exllama_to_logical(word, N, K)
+        got = [int(logical[0, k // 2] >> (4 * (k % 2))) & 0xF for k in range(8)]
+        assert got == case["vals"]
+
+
+def test_exllama_import_of_f16_class_is_a_word_relocation():
+    """The ExLlama order is the F16-class word order, so importing for fp16 /
+    bf16 GEMMs moves whole words: PB-v1 word (block, lane, kw) is source word
+    (n, k / 8) of its lane's k range, unchanged."""
+    N, K = 32, 384
+    rng = np.random.default_rng(17)
+    src = rng.integers(0, 2 ** 32, size=(N, K // 8), dtype=np.uint64).astype(np.uint32)
+    words = O.prepack_B_from_exllama(src, N, K, "f16").view(np.uint32)
+    KB = K // 128
+    for n in range(N):
+        for w in range(K // 8):
+            k = 8 * w
+            kb, kq, kw = k // 128, (k % 128) // 32, (k % 32) // 8
+            lane = 16 * kq + n % 16
+            assert words[((n // 16) * KB + kb) * 256 + lane * 4 + kw] == src[n, w]
+
+
+def test_exllama_import_equals_prepack_of_the_unpacked_codes():
+    """Brute force on a small weight: pack random codes with the page's
+    shuffle, one value at a time, then import; the result must equal
+    prepacking the codes' logical bytes (both operand classes)."""
+    N, K = 16, 256
+    rng = np.random.default_rng(23)
+    codes = rng.integers(0, 16, size=(N, K), dtype=np.uint8)
+    src = np.zeros((N, K // 8), dtype=np.uint32)
+    for n in range(N):
+        for k in range(K):
+            j = k % 8
+            src[n, k // 8] |= np.uint32(int(codes[n, k]) << ((j // 2) * 4 + (j % 2) * 16))
+    logical = np.zeros((N, K // 2), dtype=np.uint8)
+    for n in range(N):
+        for k in range(K):
+            logical[n, k // 2] |= np.uint8(int(codes[n, k]) << (4 * (k % 2)))
+    for operand in ("i8", "f16"):
+        assert np.array_equal(O.prepack_B_from_exllama(src, N, K, operand), O.prepack_B(logical, N, K, operand))
