@@ -327,6 +327,18 @@ def main(argv=None) -> int:
     torch.cuda.synchronize()
     prepack_us = sorted(s.elapsed_time(e) * 1e3 for s, e in pev)
     del logical
+    # import of the same-size weight from ExLlama-shuffled int32 words
+    words = torch.randint(-2 ** 31, 2 ** 31 - 1, (N, K // 8), dtype=torch.int32, device=dev)
+    scratch = torch.empty(N * K // 2, dtype=torch.uint8, device=dev)
+    w4.prepack_B_from_exllama(words, "i8", out=scratch)
+    xev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(5)]
+    for e0, e1 in xev:
+        e0.record()
+        w4.prepack_B_from_exllama(words, "i8", out=scratch)
+        e1.record()
+    torch.cuda.synchronize()
+    import_us = sorted(a.elapsed_time(b) * 1e3 for a, b in xev)
+    del words, scratch
 
     def step(evs):
         for i, M in enumerate(Ms):
@@ -485,6 +497,8 @@ def main(argv=None) -> int:
         "rmsnorm_quant": norm_quant,
         "prepack": {"median_us": round(prepack_us[len(prepack_us) // 2], 2),
                     "GBps_read_plus_write": round(N * K / (prepack_us[len(prepack_us) // 2] * 1e-6) / 1e9, 1)},
+        "prepack_from_exllama": {"median_us": round(import_us[len(import_us) // 2], 2),
+                                 "GBps_read_plus_write": round(N * K / (import_us[len(import_us) // 2] * 1e-6) / 1e9, 1)},
         "wall_s_timed": round(wall, 3),
     }
     if calib:

@@ -117,6 +117,24 @@ W4_API int w4_prepack_B(const void* w_logical, void* w_packed, int64_t N, int64_
                  void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Prepack from ExLlama-shuffled int32 words.
+ *
+ * vLLM API page "...mixed_precision.rdna_hybrid_w4a16", docstring of
+ * _triton_w4a16_skinny_fmt_kernel: the weight as [N][K/8] int32 words, each
+ * holding 8 consecutive k (k = 8 w + j) with k-offset j at bit
+ * (j / 2) * 4 + (j % 2) * 16.  Writes the same PB-v1 bytes as w4_prepack_B
+ * of the equivalent logical weight, in one pass (for W4_OPERAND_F16 the
+ * words move unchanged: the two orders coincide).  Codes are taken as they
+ * are (raw 4-bit values; their signedness is chosen by the GEMM's wtype).
+ *
+ * w_words  : device, [N][K/8] 32-bit words, N*K/2 bytes, 16-byte aligned.
+ * w_packed : device, N*K/2 bytes, 16-byte aligned, not overlapping w_words.
+ * Requirements and errors as w4_prepack_B.
+ * ------------------------------------------------------------------------- */
+W4_API int w4_prepack_B_from_exllama(const void* w_words, void* w_packed, int64_t N, int64_t K, int operand,
+                              void* stream);
+
+/* ---------------------------------------------------------------------------
  * Dynamic per-token activation quantisation.
  *
  * Follows "[ Kernel ] Enable Dynamic Per Token fp8", summary and review

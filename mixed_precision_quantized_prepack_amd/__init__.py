@@ -21,7 +21,7 @@ import os
 from typing import Optional
 
 __all__ = [
-    "LIB_PATH", "lib", "W4Error", "prepack_B", "prepack_B_bytes", "quant_act_per_token",
+    "LIB_PATH", "lib", "W4Error", "prepack_B", "prepack_B_from_exllama", "prepack_B_bytes", "quant_act_per_token",
     "rmsnorm_quant_per_token",
     "w4a8_gemm", "w4a16_gemm", "w4a8_gemm_partials", "w4a16_gemm_partials",
     "gemm_workspace_bytes", "gemm_plan", "set_option", "get_option", "EXPORTED_SYMBOLS",
@@ -51,6 +51,7 @@ _SIGNATURES = [
     ("w4_last_error", ctypes.c_char_p, []),
     ("w4_prepack_B_bytes", _sz, [_i64, _i64]),
     ("w4_prepack_B", _int, [_vp, _vp, _i64, _i64, _int, _vp]),
+    ("w4_prepack_B_from_exllama", _int, [_vp, _vp, _i64, _i64, _int, _vp]),
     ("w4_quant_act_per_token", _int, [_vp, _int, _vp, _int, _vp, _i64, _i64, _vp]),
     ("w4_rmsnorm_quant_per_token", _int, [_vp, _int, _vp, ctypes.c_float, _vp, _int, _vp, _i64, _i64, _vp]),
     ("w4_gemm_workspace_bytes", _sz, [_i64, _i64, _i64, _i64, _int]),
@@ -159,6 +160,22 @@ def prepack_B(w_logical, operand: str = "i8", out=None):
         out = torch.empty(N * K // 2, dtype=torch.uint8, device=w_logical.device)
     _check("w4_prepack_B", lib().w4_prepack_B(_dev_ptr(w_logical, "w_logical"), _dev_ptr(out, "out"),
                                               N, K, OPERANDS[operand], _stream(w_logical)))
+    return out
+
+
+def prepack_B_from_exllama(w_words, operand: str = "f16", out=None):
+    """PB-v1 prepack of a weight given as ExLlama-shuffled int32 words
+    [N, K/8] (see include/w4.h)."""
+    torch = _torch()
+    N, k8 = w_words.shape
+    K = 8 * k8
+    if w_words.dtype not in (torch.int32, torch.uint32):
+        raise ValueError("w_words must be int32 [N, K/8]")
+    if out is None:
+        out = torch.empty(N * K // 2, dtype=torch.uint8, device=w_words.device)
+    _check("w4_prepack_B_from_exllama",
+           lib().w4_prepack_B_from_exllama(_dev_ptr(w_words, "w_words"), _dev_ptr(out, "out"), N, K,
+                                           OPERANDS[operand], _stream(w_words)))
     return out
 
 

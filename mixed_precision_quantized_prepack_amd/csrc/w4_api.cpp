@@ -238,21 +238,31 @@ size_t w4_prepack_B_bytes(int64_t N, int64_t K) {
   return (size_t)N * (size_t)K / 2u;
 }
 
-int w4_prepack_B(const void* w_logical, void* w_packed, int64_t N, int64_t K, int operand,
-                 void* stream) {
-  if (!w_logical || !w_packed) return fail(W4_E_NULL, "w_logical and w_packed are required");
+static int prepack_common(const void* w_in, void* w_packed, int64_t N, int64_t K, int operand, bool exllama,
+                          void* stream) {
+  if (!w_in || !w_packed) return fail(W4_E_NULL, "the input weight and w_packed are required");
   if (int st = check_shape(0, N, K)) return st;
   if (operand != W4_OPERAND_I8 && operand != W4_OPERAND_F16)
     return fail(W4_E_DTYPE, "operand must be W4_OPERAND_I8 or W4_OPERAND_F16");
-  if (!aligned(w_logical, 16) || !aligned(w_packed, 16))
-    return fail(W4_E_ALIGN, "w_logical and w_packed must be 16-byte aligned");
-  const char* a = static_cast<const char*>(w_logical);
+  if (!aligned(w_in, 16) || !aligned(w_packed, 16))
+    return fail(W4_E_ALIGN, "the input weight and w_packed must be 16-byte aligned");
+  const char* a = static_cast<const char*>(w_in);
   const char* b = static_cast<const char*>(w_packed);
   const size_t bytes = w4_prepack_B_bytes(N, K);
   if (a < b + bytes && b < a + bytes) return fail(W4_E_SHAPE, "input and output overlap");
-  hipError_t e = launch_prepack(w_logical, w_packed, N, K, operand, (hipStream_t)stream);
+  hipError_t e = launch_prepack(w_in, w_packed, N, K, operand, exllama, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "prepack launch");
   return ok();
+}
+
+int w4_prepack_B(const void* w_logical, void* w_packed, int64_t N, int64_t K, int operand,
+                 void* stream) {
+  return prepack_common(w_logical, w_packed, N, K, operand, false, stream);
+}
+
+int w4_prepack_B_from_exllama(const void* w_words, void* w_packed, int64_t N, int64_t K, int operand,
+                              void* stream) {
+  return prepack_common(w_words, w_packed, N, K, operand, true, stream);
 }
 
 int w4_quant_act_per_token(const void* x, int x_dtype, void* xq, int q_dtype, float* scales,

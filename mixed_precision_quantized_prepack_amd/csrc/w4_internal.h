@@ -60,7 +60,7 @@ struct GemmPlan {
 // Block tile of the tiled kernel for an operand class / grouping.
 void tiled_tile(int op, bool grouped, int tall, int* bm, int* bn);
 
-hipError_t launch_prepack(const void* w_logical, void* w_packed, int64_t N, int64_t K, int operand,
+hipError_t launch_prepack(const void* w_in, void* w_packed, int64_t N, int64_t K, int operand, bool exllama,
                           hipStream_t stream);
 hipError_t launch_quant(const void* x, int x_dtype, void* xq, int q_dtype, float* scales, int64_t M,
                         int64_t K, hipStream_t stream);

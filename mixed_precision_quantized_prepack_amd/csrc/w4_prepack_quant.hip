@@ -16,6 +16,12 @@ namespace w4 {
 //   logical: nibble i (bits 4i) = k-offset i
 //   I8     : byte b = k-offset b (low nibble) | k-offset 4+b (high nibble)
 //   F16    : low half = k-offsets 0,2,4,6 ; high half = 1,3,5,7 (ExLlama)
+//
+// The importer of ExLlama-shuffled int32 words [N, K/8] (W4A16 page,
+// docstring of the skinny-format kernel) runs the same kernel: 16 bytes of
+// a source row are the 32 k of one PB-v1 lane slot as well, and its words
+// are in the F16 order already (identity), while reorder_i8 of an F16-order
+// word is its logical word, so I8 takes reorder_i8 twice.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t spread_nibbles_to_bytes(uint32_t x16) {
   // nibble b of a 16-bit value -> bits 8b..8b+3
@@ -34,7 +40,7 @@ __device__ __forceinline__ uint32_t reorder_f16(uint32_t w) {
   return gather_byte_nibbles(w & 0x0F0F0F0Fu) | (gather_byte_nibbles((w >> 4) & 0x0F0F0F0Fu) << 16);
 }
 
-template <bool F16CLASS>
+template <bool F16CLASS, bool EXLLAMA>
 __global__ __launch_bounds__(256) void w4_prepack_kernel(const uint4* __restrict__ in,
                                                          uint4* __restrict__ out, int64_t N,
                                                          int64_t K) {
@@ -48,9 +54,12 @@ __global__ __launch_bounds__(256) void w4_prepack_kernel(const uint4* __restrict
     const int64_t kb = rem >> 2;
     const int kq = (int)(rem & 3);
     uint4 v = in[u];
-    if (F16CLASS) {
+    if (EXLLAMA && !F16CLASS) {
+      v.x = reorder_i8(v.x); v.y = reorder_i8(v.y); v.z = reorder_i8(v.z); v.w = reorder_i8(v.w);
+    }
+    if (F16CLASS && !EXLLAMA) {
       v.x = reorder_f16(v.x); v.y = reorder_f16(v.y); v.z = reorder_f16(v.z); v.w = reorder_f16(v.w);
-    } else {
+    } else if (!F16CLASS) {
       v.x = reorder_i8(v.x); v.y = reorder_i8(v.y); v.z = reorder_i8(v.z); v.w = reorder_i8(v.w);
     }
     const int64_t block = (n >> 4) * KB + kb;
@@ -59,18 +68,23 @@ __global__ __launch_bounds__(256) void w4_prepack_kernel(const uint4* __restrict
   }
 }
 
-hipError_t launch_prepack(const void* w_logical, void* w_packed, int64_t N, int64_t K, int operand,
+hipError_t launch_prepack(const void* w_in, void* w_packed, int64_t N, int64_t K, int operand, bool exllama,
                           hipStream_t stream) {
   const int64_t total = N * (K / 32);
   const int threads = 256;
   int64_t blocks = (total + threads - 1) / threads;
   if (blocks > (1 << 20)) blocks = 1 << 20;  // grid-stride beyond this
-  if (operand == W4_OPERAND_F16)
-    hipLaunchKernelGGL(w4_prepack_kernel<true>, dim3((unsigned)blocks), dim3(threads), 0, stream,
-                       (const uint4*)w_logical, (uint4*)w_packed, N, K);
+  const dim3 g((unsigned)blocks), b(threads);
+  const uint4* in = (const uint4*)w_in;
+  uint4* out = (uint4*)w_packed;
+  if (operand == W4_OPERAND_F16 && exllama)
+    hipLaunchKernelGGL((w4_prepack_kernel<true, true>), g, b, 0, stream, in, out, N, K);
+  else if (operand == W4_OPERAND_F16)
+    hipLaunchKernelGGL((w4_prepack_kernel<true, false>), g, b, 0, stream, in, out, N, K);
+  else if (exllama)
+    hipLaunchKernelGGL((w4_prepack_kernel<false, true>), g, b, 0, stream, in, out, N, K);
   else
-    hipLaunchKernelGGL(w4_prepack_kernel<false>, dim3((unsigned)blocks), dim3(threads), 0, stream,
-                       (const uint4*)w_logical, (uint4*)w_packed, N, K);
+    hipLaunchKernelGGL((w4_prepack_kernel<false, false>), g, b, 0, stream, in, out, N, K);
   return hipGetLastError();
 }
 

@@ -70,6 +70,15 @@ def test_prepack_validation(lib):
     assert "overlap" in lib.w4_last_error().decode()
 
 
+def test_prepack_from_exllama_validation(lib):
+    f = lib.w4_prepack_B_from_exllama
+    assert f(None, FAKE, 16, 128, 0, None) == E_NULL
+    assert f(FAKE, ctypes.c_void_p(0x90000), 24, 128, 0, None) == E_SHAPE
+    assert f(FAKE, ctypes.c_void_p(0x90000), 16, 128, 9, None) == E_DTYPE
+    assert f(MISALIGNED, ctypes.c_void_p(0x90000), 16, 128, 0, None) == E_ALIGN
+    assert f(FAKE, ctypes.c_void_p(0x10010), 16, 128, 0, None) == E_SHAPE       # overlap
+
+
 def test_quant_validation(lib):
     q = lib.w4_quant_act_per_token
     assert q(FAKE, 7, FAKE, 3, FAKE, 4, 64, None) == E_DTYPE

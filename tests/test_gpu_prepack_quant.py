@@ -82,3 +82,29 @@ def test_quant_exhaustive_fp16_codes():
         qo, so = O.quant_act_per_token(vals, "f16", q_dtype)
         assert np.array_equal(s.cpu().numpy().view(np.uint32), so.view(np.uint32))
         assert np.array_equal(q.cpu().numpy().view(np.uint8), qo.view(np.uint8))
+
+
+@pytest.mark.parametrize("operand", ["i8", "f16"])
+@pytest.mark.parametrize("N,K", [(16, 128), (48, 384), (272, 640), (4096, 4096), (22016, 4096)])
+def test_prepack_from_exllama_bit_exact(operand, N, K):
+    g = torch.Generator().manual_seed(N + 3 * K)
+    words = torch.randint(-2 ** 31, 2 ** 31, (N, K // 8), generator=g, dtype=torch.int64).to(torch.int32)
+    got = w4.prepack_B_from_exllama(words.to(DEV), operand).cpu().numpy()
+    assert np.array_equal(got, O.prepack_B_from_exllama(words.numpy(), N, K, operand))
+
+
+def test_exllama_import_feeds_the_gemm():
+    """A W4A16 GEMM on imported words equals the one on the logical weight."""
+    N, K, M = 256, 512, 5
+    g = torch.Generator().manual_seed(9)
+    words = torch.randint(-2 ** 31, 2 ** 31, (N, K // 8), generator=g, dtype=torch.int64).to(torch.int32)
+    logical = torch.from_numpy(O.exllama_to_logical(words.numpy(), N, K))
+    a = torch.randn((M, K), generator=g).to(torch.bfloat16).to(DEV)
+    s = (torch.rand((N, K // 128), generator=g) * 0.01 + 0.005).to(torch.bfloat16).to(DEV)
+    z = torch.randint(0, 16, (N, K // 128), generator=g).to(torch.bfloat16).to(DEV)
+    p1 = w4.prepack_B_from_exllama(words.to(DEV), "f16")
+    p2 = w4.prepack_B(logical.to(DEV), "f16")
+    assert torch.equal(p1, p2)
+    o1 = w4.w4a16_gemm(a, p1, s, zeros=z, group_size=128)
+    o2 = w4.w4a16_gemm(a, p2, s, zeros=z, group_size=128)
+    assert torch.equal(o1, o2)
