@@ -108,8 +108,8 @@ W4_API const char* w4_last_error(void);
  *             k-offset j (0..7) sits at bit 8j (j < 4) / 8(j-4)+4 (j >= 4) for
  *             W4_OPERAND_I8 and at bit 4(j/2) + 16(j%2) (the ExLlama order of
  *             the W4A16 page) for W4_OPERAND_F16.
- * Requires N % 16 == 0, K % 128 == 0, N, K > 0.  Input and output must not
- * overlap.  Errors: W4_E_NULL, W4_E_SHAPE, W4_E_DTYPE (operand), W4_E_ALIGN,
+ * Requires N % 16 == 0, K % 128 == 0, N, K > 0, N * K < 2^43.  Input and
+ * output must not overlap.  Errors: W4_E_NULL, W4_E_SHAPE, W4_E_DTYPE (operand), W4_E_ALIGN,
  * W4_E_HIP.
  * ------------------------------------------------------------------------- */
 W4_API size_t w4_prepack_B_bytes(int64_t N, int64_t K);

@@ -242,6 +242,8 @@ static int prepack_common(const void* w_in, void* w_packed, int64_t N, int64_t K
                           void* stream) {
   if (!w_in || !w_packed) return fail(W4_E_NULL, "the input weight and w_packed are required");
   if (int st = check_shape(0, N, K)) return st;
+  if ((N / 16) * (K / 128) >= ((int64_t)1 << 32))
+    return fail(W4_E_SHAPE, "weights of 2^43 elements or more are not supported");
   if (operand != W4_OPERAND_I8 && operand != W4_OPERAND_F16)
     return fail(W4_E_DTYPE, "operand must be W4_OPERAND_I8 or W4_OPERAND_F16");
   if (!aligned(w_in, 16) || !aligned(w_packed, 16))

@@ -9,10 +9,13 @@ namespace w4 {
 // matrix-core operand layout before any GEMM; Machete W4A8 PR summary: the
 // reorder only moves data, so it is the same for every 4-bit weight type.
 //
-// One thread per (n, kb, kq): it reads the 16 logical bytes holding k in
-// [128 kb + 32 kq, +32) of row n (coalesced along the row), permutes the
-// nibbles inside each 32-bit word and writes the 16 bytes of PB-v1 lane
-// 16 kq + n%16 of block (n/16, kb).  Word-internal orders:
+// One thread per PB-v1 lane slot, 64 consecutive threads per 1 KiB block
+// (the writes of a wave are one contiguous KiB): thread u fills lane
+// l = u mod 64 = 16 kq + r of block u / 64 = (n / 16, kb), reading the 16
+// logical bytes that hold k in [128 kb + 32 kq, +32) of row n = 16 nb + r
+// (per wave, 64 contiguous bytes of each of 16 rows; the next wave reads the
+// rest of those lines), and permutes the nibbles inside each 32-bit word.
+// Word-internal orders:
 //   logical: nibble i (bits 4i) = k-offset i
 //   I8     : byte b = k-offset b (low nibble) | k-offset 4+b (high nibble)
 //   F16    : low half = k-offsets 0,2,4,6 ; high half = 1,3,5,7 (ExLlama)
@@ -49,11 +52,13 @@ __global__ __launch_bounds__(256) void w4_prepack_kernel(const uint4* __restrict
   const int64_t KB = K / 128;
   for (int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; u < total;
        u += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t n = u / units_per_row;
-    const int64_t rem = u - n * units_per_row;
-    const int64_t kb = rem >> 2;
-    const int kq = (int)(rem & 3);
-    uint4 v = in[u];
+    // block < N K / 2048 < 2^32 (the host rejects larger weights)
+    const uint32_t block = (uint32_t)(u >> 6);
+    const int lane = (int)(u & 63);
+    const int64_t nb = block / (uint32_t)KB, kb = block - (uint32_t)nb * (uint32_t)KB;
+    const int64_t n = nb * 16 + (lane & 15);
+    const int kq = lane >> 4;
+    uint4 v = in[n * units_per_row + kb * 4 + kq];
     if (EXLLAMA && !F16CLASS) {
       v.x = reorder_i8(v.x); v.y = reorder_i8(v.y); v.z = reorder_i8(v.z); v.w = reorder_i8(v.w);
     }
@@ -62,9 +67,7 @@ __global__ __launch_bounds__(256) void w4_prepack_kernel(const uint4* __restrict
     } else if (!F16CLASS) {
       v.x = reorder_i8(v.x); v.y = reorder_i8(v.y); v.z = reorder_i8(v.z); v.w = reorder_i8(v.w);
     }
-    const int64_t block = (n >> 4) * KB + kb;
-    const int lane = kq * 16 + (int)(n & 15);
-    out[block * 64 + lane] = v;
+    out[u] = v;
   }
 }
 

@@ -77,6 +77,7 @@ def test_prepack_from_exllama_validation(lib):
     assert f(FAKE, ctypes.c_void_p(0x90000), 16, 128, 9, None) == E_DTYPE
     assert f(MISALIGNED, ctypes.c_void_p(0x90000), 16, 128, 0, None) == E_ALIGN
     assert f(FAKE, ctypes.c_void_p(0x10010), 16, 128, 0, None) == E_SHAPE       # overlap
+    assert f(FAKE, ctypes.c_void_p(0x90000), 1 << 22, 1 << 22, 0, None) == E_SHAPE   # 2^44 elements
 
 
 def test_quant_validation(lib):
