@@ -240,6 +240,42 @@ def quant_act_per_token(x_bits: np.ndarray, x_dtype: str, q_dtype: str):
     return q, s
 
 
+def quant_act_per_tensor(x_bits: np.ndarray, x_dtype: str, q_dtype: str):
+    """Dynamic per-tensor symmetric quantisation: one scale for the whole
+    [M, K] tensor.
+
+    vLLM PR "[ Kernel ] Enable Dynamic Per Token fp8", *results* and review
+    discussion: dynamic per-tensor scaling is the alternative to per-token
+    (one scale, computed at run time over the whole tensor).  The codes are
+    formed as in ``quant_act_per_token`` with that one scale:
+
+    amax = max_{m,k} |x[m, k]|;  s = fp32(amax / qmax);  v = fp32(x / s)
+    int8 : q = clamp(round_half_even(v), -127, 127)
+    fp8  : q = e4m3fn(round_half_even(clamp(v, -448, 448)))
+    amax = 0: s = 0, q = 0.
+
+    Returns (codes [M, K], scales [M] fp32, every entry s).
+    """
+    x = F.decode(x_bits, x_dtype).astype(np.float32)          # exact widening
+    M, K = x.shape
+    if K == 0:
+        raise ValueError("K must be positive")
+    amax = np.abs(x).max() if M else np.float32(0.0)
+    s = np.float32(np.float32(amax) / QMAX[q_dtype])
+    with np.errstate(divide="ignore", invalid="ignore"):
+        v = (x / s).astype(np.float32)
+    if s == 0:
+        v = np.zeros_like(x)
+    if q_dtype == "i8":
+        q = np.clip(np.rint(v), -127, 127).astype(np.int8)
+    elif q_dtype == "fp8":
+        vc = np.clip(v, np.float32(-448.0), np.float32(448.0)).astype(np.float64)
+        q = F.round_and_encode(vc, "e4m3fn")
+    else:
+        raise ValueError(q_dtype)
+    return q, np.full((M,), s, dtype=np.float32)
+
+
 def rmsnorm_rows(x_bits: np.ndarray, x_dtype: str, gamma_bits: np.ndarray, eps: float):
     """The normalisation step of ``rmsnorm_quant_per_token`` before its final
     rounding to the activation dtype: returns (r [M] fp32, y [M, K] fp32).
