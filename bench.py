@@ -413,15 +413,19 @@ def main(argv=None) -> int:
         iso_us[M] = e0.elapsed_time(e1) * 1e3 / REPS
 
     # ---- fused RMSNorm + per-token quantisation, next to the plain quantiser
-    # (same activations; both read 2 B and write 1 B per element), REPS
-    # launches back to back between two events
+    # (same activations; both read 2 B and write 1 B per element) and the
+    # per-tensor quantiser (which reads the activations twice: the codes wait
+    # for the whole tensor's maximum), REPS launches back to back between two
+    # events
     gamma = workloads.norm_weight(K, "f16", seed=2025).to(dev)
     norm_quant = []
     for M in sorted({min(Ms), max(Ms)}):
         row = {"M": M, "K": K}
         for name, fn in (("quant_us", lambda: w4.quant_act_per_token(a[:M], "i8", out=aq[M], scales=sa[M])),
                          ("rmsnorm_quant_us", lambda: w4.rmsnorm_quant_per_token(a[:M], gamma, 1e-6, "i8",
-                                                                                 out=aq[M], scales=sa[M]))):
+                                                                                 out=aq[M], scales=sa[M])),
+                         ("quant_per_tensor_us", lambda: w4.quant_act_per_tensor(a[:M], "i8", out=aq[M],
+                                                                                 scales=sa[M]))):
             fn()
             e0, e1 = mk(), mk()
             e0.record()

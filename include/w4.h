@@ -154,6 +154,24 @@ W4_API int w4_quant_act_per_token(const void* x, int x_dtype, void* xq, int q_dt
                            int64_t M, int64_t K, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Dynamic per-tensor activation quantisation.
+ *
+ * "[ Kernel ] Enable Dynamic Per Token fp8", results and review discussion:
+ * the per-tensor alternative to per-token scales, one scale for the whole
+ * [M][K] tensor computed at run time:
+ *   amax = max_{m,k} |x[m,k]|;  s = fp32(amax / qmax)   (qmax 127 int8, 448 fp8)
+ *   q = as w4_quant_act_per_token, with s in place of every row's s[m]
+ * s is written to each of scales[0..M), so that the GEMMs, which take one
+ * scale per row, consume the result unchanged.  An all-zero tensor gets
+ * s = 0, q = 0.  x is read twice (its row maxima, then the codes): three
+ * launches on the stream, with scales holding the row maxima in between.
+ *
+ * Arguments, requirements and errors as w4_quant_act_per_token.
+ * ------------------------------------------------------------------------- */
+W4_API int w4_quant_act_per_tensor(const void* x, int x_dtype, void* xq, int q_dtype, float* scales,
+                            int64_t M, int64_t K, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Fused RMSNorm + dynamic per-token activation quantisation.
  *
  * "[ Kernel ] Enable Dynamic Per Token fp8", review discussion: per-token

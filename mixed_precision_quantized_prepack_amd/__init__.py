@@ -22,7 +22,7 @@ from typing import Optional
 
 __all__ = [
     "LIB_PATH", "lib", "W4Error", "prepack_B", "prepack_B_from_exllama", "prepack_B_bytes", "quant_act_per_token",
-    "rmsnorm_quant_per_token",
+    "quant_act_per_tensor", "rmsnorm_quant_per_token",
     "w4a8_gemm", "w4a16_gemm", "w4a8_gemm_partials", "w4a16_gemm_partials",
     "gemm_workspace_bytes", "gemm_plan", "set_option", "get_option", "EXPORTED_SYMBOLS",
 ]
@@ -53,6 +53,7 @@ _SIGNATURES = [
     ("w4_prepack_B", _int, [_vp, _vp, _i64, _i64, _int, _vp]),
     ("w4_prepack_B_from_exllama", _int, [_vp, _vp, _i64, _i64, _int, _vp]),
     ("w4_quant_act_per_token", _int, [_vp, _int, _vp, _int, _vp, _i64, _i64, _vp]),
+    ("w4_quant_act_per_tensor", _int, [_vp, _int, _vp, _int, _vp, _i64, _i64, _vp]),
     ("w4_rmsnorm_quant_per_token", _int, [_vp, _int, _vp, ctypes.c_float, _vp, _int, _vp, _i64, _i64, _vp]),
     ("w4_gemm_workspace_bytes", _sz, [_i64, _i64, _i64, _i64, _int]),
     ("w4a8_gemm", _int, [_vp, _int, _vp, _vp, _int, _vp, _int, _i64, _vp, _vp, _int,
@@ -193,6 +194,22 @@ def quant_act_per_token(x, q_dtype: str = "i8", out=None, scales=None):
     _check("w4_quant_act_per_token",
            lib().w4_quant_act_per_token(_dev_ptr(x, "x"), _dtype_code(x.dtype), _dev_ptr(out, "out"),
                                         qd, _dev_ptr(scales, "scales"), M, K, _stream(x)))
+    return out, scales
+
+
+def quant_act_per_tensor(x, q_dtype: str = "i8", out=None, scales=None):
+    """Dynamic per-tensor int8 / fp8-e4m3 quantisation -> (codes [M, K],
+    scales [M] fp32, every entry the tensor's one scale)."""
+    torch = _torch()
+    M, K = x.shape
+    qd = I8 if q_dtype == "i8" else FP8_E4M3
+    if out is None:
+        out = torch.empty((M, K), dtype=torch.int8 if qd == I8 else torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((M,), dtype=torch.float32, device=x.device)
+    _check("w4_quant_act_per_tensor",
+           lib().w4_quant_act_per_tensor(_dev_ptr(x, "x"), _dtype_code(x.dtype), _dev_ptr(out, "out"),
+                                         qd, _dev_ptr(scales, "scales"), M, K, _stream(x)))
     return out, scales
 
 

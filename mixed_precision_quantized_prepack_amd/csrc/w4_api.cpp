@@ -267,8 +267,8 @@ int w4_prepack_B_from_exllama(const void* w_words, void* w_packed, int64_t N, in
   return prepack_common(w_words, w_packed, N, K, operand, true, stream);
 }
 
-int w4_quant_act_per_token(const void* x, int x_dtype, void* xq, int q_dtype, float* scales,
-                           int64_t M, int64_t K, void* stream) {
+static int quant_common(const char* what, const void* x, int x_dtype, void* xq, int q_dtype, float* scales,
+                        int64_t M, int64_t K, void* stream, bool per_tensor) {
   if (x_dtype != W4_F16 && x_dtype != W4_BF16) return fail(W4_E_DTYPE, "x_dtype must be W4_F16 or W4_BF16");
   if (q_dtype != W4_I8 && q_dtype != W4_FP8_E4M3)
     return fail(W4_E_DTYPE, "q_dtype must be W4_I8 or W4_FP8_E4M3");
@@ -280,9 +280,20 @@ int w4_quant_act_per_token(const void* x, int x_dtype, void* xq, int q_dtype, fl
   if (!x || !xq || !scales) return fail(W4_E_NULL, "x, xq and scales are required");
   if (!aligned(x, 16) || !aligned(xq, 16) || !aligned(scales, 4))
     return fail(W4_E_ALIGN, "x and xq must be 16-byte aligned, scales 4-byte aligned");
-  hipError_t e = launch_quant(x, x_dtype, xq, q_dtype, scales, M, K, (hipStream_t)stream);
-  if (e != hipSuccess) return hip_fail(e, "quant launch");
+  hipError_t e = per_tensor ? launch_quant_per_tensor(x, x_dtype, xq, q_dtype, scales, M, K, (hipStream_t)stream)
+                            : launch_quant(x, x_dtype, xq, q_dtype, scales, M, K, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, what);
   return ok();
+}
+
+int w4_quant_act_per_token(const void* x, int x_dtype, void* xq, int q_dtype, float* scales,
+                           int64_t M, int64_t K, void* stream) {
+  return quant_common("quant launch", x, x_dtype, xq, q_dtype, scales, M, K, stream, false);
+}
+
+int w4_quant_act_per_tensor(const void* x, int x_dtype, void* xq, int q_dtype, float* scales,
+                            int64_t M, int64_t K, void* stream) {
+  return quant_common("per-tensor quant launch", x, x_dtype, xq, q_dtype, scales, M, K, stream, true);
 }
 
 int w4_rmsnorm_quant_per_token(const void* x, int x_dtype, const void* gamma, float eps, void* xq, int q_dtype,

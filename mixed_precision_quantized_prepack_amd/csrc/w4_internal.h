@@ -64,6 +64,8 @@ hipError_t launch_prepack(const void* w_in, void* w_packed, int64_t N, int64_t K
                           hipStream_t stream);
 hipError_t launch_quant(const void* x, int x_dtype, void* xq, int q_dtype, float* scales, int64_t M,
                         int64_t K, hipStream_t stream);
+hipError_t launch_quant_per_tensor(const void* x, int x_dtype, void* xq, int q_dtype, float* scales, int64_t M,
+                                   int64_t K, hipStream_t stream);
 hipError_t launch_rmsnorm_quant(const void* x, int x_dtype, const void* gamma, float eps, void* xq, int q_dtype,
                                 float* scales, int64_t M, int64_t K, int exact_sum, hipStream_t stream);
 hipError_t launch_gemm(const GemmArgs& args, int op, bool grouped, bool flip, const GemmPlan& plan,

@@ -261,9 +261,18 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* base, int
 }
 constexpr uint32_t kRowOutOfRange = 0x80000000u;
 
+// Where a row's scale comes from.  Per-token: the row's own maximum.  The
+// per-tensor scale ("[ Kernel ] Enable Dynamic Per Token fp8", results and
+// review discussion: one scale for the whole tensor, computed at run time)
+// takes three launches, since no row can be coded before every row has been
+// read: the row maxima (written to scales[row], no codes), their maximum
+// (w4_tensor_scale_kernel, which writes the tensor's scale to every
+// scales[row]), then the codes with the scale read from scales[row].
+enum { kScaleRow = 0, kScaleRowMaxOnly = 1, kScaleGiven = 2 };
+
 // 256-thread int8 workgroups: three per CU (at most 168 VGPRs); the fp8
 // coder needs more registers than that with 12 chunks per thread.
-template <int XT, int QT, int THREADS, int CH, bool NORM>
+template <int XT, int QT, int THREADS, int CH, bool NORM, int SC>
 __global__ __launch_bounds__(THREADS, (THREADS == 256 && QT == W4_I8) ? 3 : 1) void w4_quant_kernel(const uint16_t* __restrict__ x,
                                                            uint8_t* __restrict__ xq,
                                                            float* __restrict__ scales, int64_t K,
@@ -297,6 +306,8 @@ __global__ __launch_bounds__(THREADS, (THREADS == 256 && QT == W4_I8) ? 3 : 1) v
 
   uint4 v[CH];
   float amax = 0.0f;
+  // a given scale is read before the row, so its load is in flight with them
+  const float s_given = SC == kScaleGiven ? scales[row] : 0.0f;
 #pragma unroll
   for (int c = 0; c < CH; ++c) v[c] = load_raw(rx, c * THREADS + tid);
   if constexpr (NORM) {
@@ -349,22 +360,28 @@ __global__ __launch_bounds__(THREADS, (THREADS == 256 && QT == W4_I8) ? 3 : 1) v
 #pragma unroll
     for (int c = 0; c < CH; ++c) v[c] = norm_chunk<XT>(v[c], load_raw(rg, c * THREADS + tid), r);
   }
+  if constexpr (SC != kScaleGiven) {
 #pragma unroll
-  for (int c = 0; c < CH; ++c) amax = chunk_absmax<XT>(amax, v[c]);
-  for (int idx = CH * THREADS + tid; idx < nchunks; idx += THREADS) amax = chunk_absmax<XT>(amax, load(idx));
+    for (int c = 0; c < CH; ++c) amax = chunk_absmax<XT>(amax, v[c]);
+    for (int idx = CH * THREADS + tid; idx < nchunks; idx += THREADS) amax = chunk_absmax<XT>(amax, load(idx));
 
-  // row maximum: wave butterfly, then one value per wave through LDS
+    // row maximum: wave butterfly, then one value per wave through LDS
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
-  if ((tid & 63) == 0) wave_max[tid >> 6] = amax;
-  __syncthreads();
-  amax = wave_max[0];
+    for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+    if ((tid & 63) == 0) wave_max[tid >> 6] = amax;
+    __syncthreads();
+    amax = wave_max[0];
 #pragma unroll
-  for (int w = 1; w < THREADS / 64; ++w) amax = fmaxf(amax, wave_max[w]);
+    for (int w = 1; w < THREADS / 64; ++w) amax = fmaxf(amax, wave_max[w]);
+    if constexpr (SC == kScaleRowMaxOnly) {
+      if (tid == 0) scales[row] = amax;
+      return;
+    }
+  }
 
   const float qmax = (QT == W4_I8) ? 127.0f : 448.0f;
-  const float s = amax / qmax;
-  if (tid == 0) scales[row] = s;
+  const float s = SC == kScaleGiven ? s_given : amax / qmax;
+  if (SC == kScaleRow && tid == 0) scales[row] = s;
   if (s == 0.0f) {
     for (int idx = tid; idx < nchunks; idx += THREADS) store(idx, make_uint2(0u, 0u));
     return;
@@ -383,7 +400,28 @@ __global__ __launch_bounds__(THREADS, (THREADS == 256 && QT == W4_I8) ? 3 : 1) v
   }
 }
 
-template <int THREADS, int CH, bool NORM>
+// The tensor's scale from its row maxima (held in scales[0, M)):
+// s = fp32(max_m scales[m] / qmax), written to every scales[m].  One
+// workgroup; each thread writes only the entries it has read, after the
+// barrier that every read precedes.
+template <int QT>
+__global__ __launch_bounds__(1024) void w4_tensor_scale_kernel(float* __restrict__ scales, int64_t M) {
+  const int tid = threadIdx.x;
+  __shared__ float wave_max[16];
+  float m = 0.0f;
+  for (int64_t i = tid; i < M; i += 1024) m = fmaxf(m, scales[i]);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+  if ((tid & 63) == 0) wave_max[tid >> 6] = m;
+  __syncthreads();
+  m = wave_max[0];
+#pragma unroll
+  for (int w = 1; w < 16; ++w) m = fmaxf(m, wave_max[w]);
+  const float s = m / ((QT == W4_I8) ? 127.0f : 448.0f);
+  for (int64_t i = tid; i < M; i += 1024) scales[i] = s;
+}
+
+template <int THREADS, int CH, bool NORM, int SC = kScaleRow>
 static void launch_quant_t(const void* x, int x_dtype, void* xq, int q_dtype, float* scales, int64_t M,
                            int64_t K, const void* gamma, float eps, int exact, hipStream_t stream) {
   const dim3 grid((unsigned)M), block(THREADS);
@@ -391,49 +429,65 @@ static void launch_quant_t(const void* x, int x_dtype, void* xq, int q_dtype, fl
   const uint16_t* gp = (const uint16_t*)gamma;
   uint8_t* qp = (uint8_t*)xq;
   if (x_dtype == W4_F16 && q_dtype == W4_I8)
-    hipLaunchKernelGGL((w4_quant_kernel<W4_F16, W4_I8, THREADS, CH, NORM>), grid, block, 0, stream, xp, qp,
+    hipLaunchKernelGGL((w4_quant_kernel<W4_F16, W4_I8, THREADS, CH, NORM, SC>), grid, block, 0, stream, xp, qp,
                        scales, K, gp, eps, exact);
   else if (x_dtype == W4_F16)
-    hipLaunchKernelGGL((w4_quant_kernel<W4_F16, W4_FP8_E4M3, THREADS, CH, NORM>), grid, block, 0, stream, xp, qp,
+    hipLaunchKernelGGL((w4_quant_kernel<W4_F16, W4_FP8_E4M3, THREADS, CH, NORM, SC>), grid, block, 0, stream, xp, qp,
                        scales, K, gp, eps, exact);
   else if (q_dtype == W4_I8)
-    hipLaunchKernelGGL((w4_quant_kernel<W4_BF16, W4_I8, THREADS, CH, NORM>), grid, block, 0, stream, xp, qp,
+    hipLaunchKernelGGL((w4_quant_kernel<W4_BF16, W4_I8, THREADS, CH, NORM, SC>), grid, block, 0, stream, xp, qp,
                        scales, K, gp, eps, exact);
   else
-    hipLaunchKernelGGL((w4_quant_kernel<W4_BF16, W4_FP8_E4M3, THREADS, CH, NORM>), grid, block, 0, stream, xp,
+    hipLaunchKernelGGL((w4_quant_kernel<W4_BF16, W4_FP8_E4M3, THREADS, CH, NORM, SC>), grid, block, 0, stream, xp,
                        qp, scales, K, gp, eps, exact);
 }
 
 // 1024-thread workgroups keep at most 4 chunks per thread (128 VGPRs per
 // thread at that size; 8 or 12 chunks would spill), longer rows re-read
 // their tail.
-template <int THREADS, bool NORM>
+template <int THREADS, bool NORM, int SC>
 static void launch_quant_c(const void* x, int x_dtype, void* xq, int q_dtype, float* scales, int64_t M,
                            int64_t K, const void* gamma, float eps, int exact, hipStream_t stream) {
   const int64_t per_thread = (K / 8 + THREADS - 1) / THREADS;
   if constexpr (THREADS > 256)
-    launch_quant_t<THREADS, 4, NORM>(x, x_dtype, xq, q_dtype, scales, M, K, gamma, eps, exact, stream);
+    launch_quant_t<THREADS, 4, NORM, SC>(x, x_dtype, xq, q_dtype, scales, M, K, gamma, eps, exact, stream);
   else if (per_thread <= 4)
-    launch_quant_t<THREADS, 4, NORM>(x, x_dtype, xq, q_dtype, scales, M, K, gamma, eps, exact, stream);
+    launch_quant_t<THREADS, 4, NORM, SC>(x, x_dtype, xq, q_dtype, scales, M, K, gamma, eps, exact, stream);
   else if (per_thread <= 8)
-    launch_quant_t<THREADS, 8, NORM>(x, x_dtype, xq, q_dtype, scales, M, K, gamma, eps, exact, stream);
+    launch_quant_t<THREADS, 8, NORM, SC>(x, x_dtype, xq, q_dtype, scales, M, K, gamma, eps, exact, stream);
   else
-    launch_quant_t<THREADS, kMaxChunks, NORM>(x, x_dtype, xq, q_dtype, scales, M, K, gamma, eps, exact, stream);
+    launch_quant_t<THREADS, kMaxChunks, NORM, SC>(x, x_dtype, xq, q_dtype, scales, M, K, gamma, eps, exact,
+                                                  stream);
 }
 
-template <bool NORM>
+template <bool NORM, int SC = kScaleRow>
 static void launch_quant_n(const void* x, int x_dtype, void* xq, int q_dtype, float* scales, int64_t M,
                            int64_t K, const void* gamma, float eps, int exact, hipStream_t stream) {
   // few rows: a whole CU per row
   if (M <= 512 && K >= 8 * 1024)
-    launch_quant_c<1024, NORM>(x, x_dtype, xq, q_dtype, scales, M, K, gamma, eps, exact, stream);
+    launch_quant_c<1024, NORM, SC>(x, x_dtype, xq, q_dtype, scales, M, K, gamma, eps, exact, stream);
   else
-    launch_quant_c<256, NORM>(x, x_dtype, xq, q_dtype, scales, M, K, gamma, eps, exact, stream);
+    launch_quant_c<256, NORM, SC>(x, x_dtype, xq, q_dtype, scales, M, K, gamma, eps, exact, stream);
 }
 
 hipError_t launch_quant(const void* x, int x_dtype, void* xq, int q_dtype, float* scales, int64_t M,
                         int64_t K, hipStream_t stream) {
   launch_quant_n<false>(x, x_dtype, xq, q_dtype, scales, M, K, nullptr, 0.0f, 0, stream);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_per_tensor(const void* x, int x_dtype, void* xq, int q_dtype, float* scales, int64_t M,
+                                   int64_t K, hipStream_t stream) {
+  launch_quant_n<false, kScaleRowMaxOnly>(x, x_dtype, xq, q_dtype, scales, M, K, nullptr, 0.0f, 0, stream);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (q_dtype == W4_I8)
+    hipLaunchKernelGGL(w4_tensor_scale_kernel<W4_I8>, dim3(1), dim3(1024), 0, stream, scales, M);
+  else
+    hipLaunchKernelGGL(w4_tensor_scale_kernel<W4_FP8_E4M3>, dim3(1), dim3(1024), 0, stream, scales, M);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  launch_quant_n<false, kScaleGiven>(x, x_dtype, xq, q_dtype, scales, M, K, nullptr, 0.0f, 0, stream);
   return hipGetLastError();
 }
 

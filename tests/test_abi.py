@@ -34,7 +34,8 @@ def header_functions():
 
 def test_header_declares_the_documented_entry_points():
     names = header_functions()
-    for n in ("w4_prepack_B", "w4_quant_act_per_token", "w4_rmsnorm_quant_per_token", "w4a8_gemm", "w4a16_gemm"):
+    for n in ("w4_prepack_B", "w4_quant_act_per_token", "w4_quant_act_per_tensor", "w4_rmsnorm_quant_per_token",
+              "w4a8_gemm", "w4a16_gemm"):
         assert n in names
     assert sorted(names) == sorted(w4.EXPORTED_SYMBOLS)
 
@@ -88,6 +89,17 @@ def test_quant_validation(lib):
     assert q(FAKE, 0, FAKE, 3, FAKE, -1, 64, None) == E_SHAPE
     assert q(None, 0, FAKE, 3, FAKE, 4, 64, None) == E_NULL
     assert q(MISALIGNED, 0, FAKE, 3, FAKE, 4, 64, None) == E_ALIGN
+    assert q(None, 0, None, 3, None, 0, 64, None) == W4_OK        # M = 0: nothing to do
+
+
+def test_quant_per_tensor_validation(lib):
+    q = lib.w4_quant_act_per_tensor
+    assert q(FAKE, 7, FAKE, 3, FAKE, 4, 64, None) == E_DTYPE
+    assert q(FAKE, 0, FAKE, 5, FAKE, 4, 64, None) == E_DTYPE
+    assert q(FAKE, 0, FAKE, 3, FAKE, 4, 60, None) == E_SHAPE
+    assert q(FAKE, 0, FAKE, 3, FAKE, -1, 64, None) == E_SHAPE
+    assert q(FAKE, 0, None, 3, FAKE, 4, 64, None) == E_NULL
+    assert q(FAKE, 0, FAKE, 3, ctypes.c_void_p(0x10002), 4, 64, None) == E_ALIGN
     assert q(None, 0, None, 3, None, 0, 64, None) == W4_OK        # M = 0: nothing to do
 
 
