@@ -308,11 +308,43 @@ W4_API int w4a16_gemm_partials(const void* a, int a_dtype, const void* b_packed,
  *   "norm_exact_sum": 1 = w4_rmsnorm_quant_per_token always re-sums the squares
  *                  with error-free pair arithmetic (the path it otherwise takes
  *                  only when the fast sum cannot decide r); same results
+ *   "schedule_table": 1 (default) = consult the schedule table below; 0 = the
+ *                  heuristic alone
+ * When any of force_path, splitk, skinny_strips or tiled_bm is nonzero, those
+ * fields are forced and the schedule table is not consulted.
  * Returns W4_OK, or W4_E_UNSUPPORTED for an unknown key / W4_E_SHAPE for an
  * out-of-range value.
  * ------------------------------------------------------------------------- */
 W4_API int w4_set_option(const char* key, int64_t value);
 W4_API int64_t w4_get_option(const char* key);
+
+/* ---------------------------------------------------------------------------
+ * Schedule table.
+ *
+ * [Machete README] *Code generation*: each type pair carries a default
+ * heuristic that maps problem shapes to schedules (tile shapes and the like),
+ * since no one schedule suits every shape, and a caller may name the schedule
+ * instead.  Here a schedule is (path, K split, tile rows, strips per wave)
+ * and the table maps (activation dtype, grouping, N, K, M range) to one.  The
+ * GEMM entry points look a problem up in the run-time entries (newest first),
+ * then in the built-in entries (measured on MI355X for the benchmark shapes,
+ * kept only where they beat the heuristic), and otherwise use the heuristic.
+ * An entry whose schedule does not fit the problem is passed over.
+ *
+ * w4_schedule_add registers a run-time entry: problems with this a_dtype
+ * (W4_I8, W4_FP8_E4M3, W4_F16, W4_BF16), group_mode (0 = one group over K,
+ * 1 = group size 128), N, K and m_lo <= M <= m_hi take path (0 = heuristic,
+ * 1 = small-M, which needs m_hi <= 16, 2 = tiled), splitk (0 = heuristic,
+ * 1..64), tile_m (0, 64 or 128) and strips (0, 1 or 2).  This is also the
+ * per-shape override of the heuristic.  The workspace size the GEMM needs
+ * follows the schedule in force (w4_gemm_workspace_bytes and w4_gemm_plan
+ * consult the same table).  Errors: W4_E_DTYPE, W4_E_SHAPE.
+ * w4_schedule_clear removes every run-time entry.
+ * Both take a lock; calls racing with GEMM launches on other threads are safe.
+ * ------------------------------------------------------------------------- */
+W4_API int w4_schedule_add(int a_dtype, int group_mode, int64_t N, int64_t K, int64_t m_lo, int64_t m_hi,
+                           int path, int splitk, int tile_m, int strips);
+W4_API int w4_schedule_clear(void);
 
 /* The kernel the GEMM entry points would choose for this problem under the
  * current options, for logging and tests: *path (1 = small-M, 2 = tiled), its

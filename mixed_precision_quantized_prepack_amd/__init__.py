@@ -24,7 +24,8 @@ __all__ = [
     "LIB_PATH", "lib", "W4Error", "prepack_B", "prepack_B_from_exllama", "prepack_B_bytes", "quant_act_per_token",
     "quant_act_per_tensor", "rmsnorm_quant_per_token",
     "w4a8_gemm", "w4a16_gemm", "w4a8_gemm_partials", "w4a16_gemm_partials",
-    "gemm_workspace_bytes", "gemm_plan", "set_option", "get_option", "EXPORTED_SYMBOLS",
+    "gemm_workspace_bytes", "gemm_plan", "set_option", "get_option", "schedule_add", "schedule_clear",
+    "EXPORTED_SYMBOLS",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libw4.so")
@@ -66,6 +67,8 @@ _SIGNATURES = [
                                    _i64, _i64, _i64, _vp, _vp, _sz, _vp]),
     ("w4_set_option", _int, [ctypes.c_char_p, _i64]),
     ("w4_get_option", _i64, [ctypes.c_char_p]),
+    ("w4_schedule_add", _int, [_int, _int, _i64, _i64, _i64, _i64, _int, _int, _int, _int]),
+    ("w4_schedule_clear", _int, []),
     ("w4_gemm_plan", _int, [_i64, _i64, _i64, _i64, _int, ctypes.POINTER(_int),
                             ctypes.POINTER(_int), ctypes.POINTER(_int), ctypes.POINTER(_int)]),
 ]
@@ -242,6 +245,19 @@ def gemm_plan(M: int, N: int, K: int, group_size: int, a_dtype: int):
     _check("w4_gemm_plan", lib().w4_gemm_plan(M, N, K, group_size, a_dtype, ctypes.byref(p), ctypes.byref(s),
                                               ctypes.byref(tm), ctypes.byref(tn)))
     return p.value, s.value, tm.value, tn.value
+
+
+def schedule_add(a_dtype: int, grouped: bool, N: int, K: int, m_lo: int, m_hi: int, path: int = 0,
+                 splitk: int = 0, tile_m: int = 0, strips: int = 0) -> None:
+    """Register a schedule-table entry (include/w4.h): problems of this
+    activation dtype code, grouping, N, K and m_lo <= M <= m_hi take this
+    (path, splitk, tile_m, strips); 0 leaves a field to the heuristic."""
+    _check("w4_schedule_add", lib().w4_schedule_add(a_dtype, int(bool(grouped)), N, K, m_lo, m_hi, path, splitk,
+                                                    tile_m, strips))
+
+
+def schedule_clear() -> None:
+    _check("w4_schedule_clear", lib().w4_schedule_clear())
 
 
 def set_option(key: str, value: int):

@@ -8,7 +8,9 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
+#include <vector>
 
 #include "w4.h"
 #include "w4_internal.h"
@@ -24,6 +26,33 @@ std::atomic<int64_t> g_splitk{0};
 std::atomic<int64_t> g_norm_exact_sum{0};
 std::atomic<int64_t> g_skinny_strips{0};
 std::atomic<int64_t> g_tiled_bm{0};
+std::atomic<int64_t> g_schedule_table{1};
+
+// A kernel schedule: path, K split, tile rows (tiled kernel) and 16-column
+// strips per wave (small-M kernel); 0 leaves a field to the heuristic.
+struct Sched {
+  int64_t path = 0, splitk = 0, tile_m = 0, strips = 0;
+  bool any() const { return path || splitk || tile_m || strips; }
+};
+
+// Schedule table entry: problems of this activation type, grouping, N and K
+// with m_lo <= M <= m_hi take this schedule.
+struct SchedEntry {
+  int a_dtype, grouped;
+  int64_t N, K, m_lo, m_hi;
+  int path, splitk, tile_m, strips;
+};
+
+// Built-in entries, measured on MI355X by the package's autotune module for
+// the shapes of its benchmarks (only where they beat the heuristic); the last
+// entry is a sentinel.
+const SchedEntry kBuiltinSchedules[] = {
+#include "w4_schedule_table.inc"
+    {-1, 0, 0, 0, 0, 0, 0, 0, 0, 0},
+};
+
+std::mutex g_sched_mutex;
+std::vector<SchedEntry> g_sched_user;   // entries added at run time, searched first
 
 int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 int fail(int status, const char* fmt, ...) {
@@ -101,9 +130,10 @@ int check_group(int64_t group_size, int64_t K) {
 // Kernel choice.  Small M is bound by the weight stream and uses the skinny
 // kernel with enough K-splitting waves to keep ~16 waves per CU in flight;
 // larger M uses the tiled kernel, split along K while there are fewer tiles
-// than CUs.
-int make_plan(int64_t M, int64_t N, int64_t K, bool grouped, int op, GemmPlan* plan) {
-  const int64_t fp = g_force_path.load(), fs = g_splitk.load();
+// than CUs.  Fields of `forced` that are nonzero replace the heuristic's
+// choice (and must fit the problem).
+int plan_with(int64_t M, int64_t N, int64_t K, bool grouped, int op, const Sched& forced, GemmPlan* plan) {
+  const int64_t fp = forced.path, fs = forced.splitk;
   const int64_t KB = K / 128;
   const int cu = cu_count();
   plan->path = fp ? (int)fp : (M <= 16 ? PATH_SKINNY : PATH_TILED);
@@ -111,7 +141,7 @@ int make_plan(int64_t M, int64_t N, int64_t K, bool grouped, int op, GemmPlan* p
   // strips of 16 columns per wave of the small-M kernel: two strips share
   // one activation fragment.  Grouped problems take two only when the
   // fragment is worth sharing (M >= 8) and N leaves enough workgroups.
-  const int64_t fns = g_skinny_strips.load();
+  const int64_t fns = forced.strips;
   const bool two = N % 32 == 0 && (!grouped || (M >= 8 && N >= 8192));
   int64_t ns = fns ? fns : (two ? 2 : 1);
   const int64_t groups = grouped ? KB : 1;
@@ -153,7 +183,7 @@ int make_plan(int64_t M, int64_t N, int64_t K, bool grouped, int op, GemmPlan* p
     // per channel: two workgroups per CU; grouped and fp8, whose tall tile
     // is 128 x 128: one), 64 x 256 tiles otherwise
     const bool byte = op == OP_I8 || op == OP_FP8;
-    const int64_t fbm = g_tiled_bm.load();
+    const int64_t fbm = forced.tile_m;
     if (byte) {
       int tall_bm, tall_bn;
       tiled_tile(op, grouped, 1, &tall_bm, &tall_bn);
@@ -171,11 +201,17 @@ int make_plan(int64_t M, int64_t N, int64_t K, bool grouped, int op, GemmPlan* p
       // K splits: the fewest that give two workgroups per CU, or one per CU
       // when there are very few tiles (each split adds an M x N fp32 slot
       // that the reduce reads back, which outweighs the second workgroup
-      // there)
+      // there).  Grouped int8 keeps the VALU busy with its per-group fold,
+      // so a second workgroup per CU gains nothing: the most splits that
+      // still fit one workgroup per CU.
       const int64_t tiles = ((M + plan->bm - 1) / plan->bm) * ((N + plan->bn - 1) / plan->bn);
-      const int64_t target = tiles < cu / 2 ? cu : 2LL * cu;
       s = 1;
-      while (tiles * s < target && s * 2 <= 8) s *= 2;
+      if (op == OP_I8 && grouped) {
+        while (tiles * s * 2 <= cu && s * 2 <= 16) s *= 2;
+      } else {
+        const int64_t target = tiles < cu / 2 ? cu : 2LL * cu;
+        while (tiles * s < target && s * 2 <= 8) s *= 2;
+      }
       while (s > 1 && KB / s < 4) s /= 2;
     }
     if (s < 1 || s > 64 || s > KB)
@@ -183,6 +219,45 @@ int make_plan(int64_t M, int64_t N, int64_t K, bool grouped, int op, GemmPlan* p
     plan->splitk = (int)s;
   }
   return W4_OK;
+}
+
+bool schedule_matches(const SchedEntry& e, int op, bool grouped, int64_t M, int64_t N, int64_t K) {
+  return op_of(e.a_dtype) == op && (e.grouped != 0) == grouped && e.N == N && e.K == K && e.m_lo <= M &&
+         M <= e.m_hi;
+}
+
+// Run-time entries first, then the built-in ones.
+bool lookup_schedule(int op, bool grouped, int64_t M, int64_t N, int64_t K, Sched* out) {
+  {
+    std::lock_guard<std::mutex> lock(g_sched_mutex);
+    for (const SchedEntry& e : g_sched_user)
+      if (schedule_matches(e, op, grouped, M, N, K)) {
+        *out = Sched{e.path, e.splitk, e.tile_m, e.strips};
+        return true;
+      }
+  }
+  for (const SchedEntry& e : kBuiltinSchedules) {
+    if (e.a_dtype < 0) break;
+    if (schedule_matches(e, op, grouped, M, N, K)) {
+      *out = Sched{e.path, e.splitk, e.tile_m, e.strips};
+      return true;
+    }
+  }
+  return false;
+}
+
+// The options, when any is set, force their fields.  Otherwise a matching
+// schedule-table entry (run-time entries first, then the built-in ones) is
+// taken if it fits the problem, and the heuristic decides the rest.
+int make_plan(int64_t M, int64_t N, int64_t K, bool grouped, int op, GemmPlan* plan) {
+  const Sched opts{g_force_path.load(), g_splitk.load(), g_tiled_bm.load(), g_skinny_strips.load()};
+  if (opts.any()) return plan_with(M, N, K, grouped, op, opts, plan);
+  if (g_schedule_table.load()) {
+    Sched t;
+    if (lookup_schedule(op, grouped, M, N, K, &t) && plan_with(M, N, K, grouped, op, t, plan) == W4_OK)
+      return W4_OK;
+  }
+  return plan_with(M, N, K, grouped, op, Sched{}, plan);
 }
 
 size_t workspace_for(const GemmPlan& plan, int64_t M, int64_t N) {
@@ -511,6 +586,11 @@ int w4_set_option(const char* key, int64_t value) {
     g_norm_exact_sum.store(value);
     return ok();
   }
+  if (!strcmp(key, "schedule_table")) {
+    if (value != 0 && value != 1) return fail(W4_E_SHAPE, "schedule_table must be 0 or 1");
+    g_schedule_table.store(value);
+    return ok();
+  }
   return fail(W4_E_UNSUPPORTED, "unknown option '%s'", key);
 }
 
@@ -521,7 +601,32 @@ int64_t w4_get_option(const char* key) {
   if (!strcmp(key, "skinny_strips")) return g_skinny_strips.load();
   if (!strcmp(key, "tiled_bm")) return g_tiled_bm.load();
   if (!strcmp(key, "norm_exact_sum")) return g_norm_exact_sum.load();
+  if (!strcmp(key, "schedule_table")) return g_schedule_table.load();
   return -1;
+}
+
+int w4_schedule_add(int a_dtype, int group_mode, int64_t N, int64_t K, int64_t m_lo, int64_t m_hi, int path,
+                    int splitk, int tile_m, int strips) {
+  if (op_of(a_dtype) < 0) return fail(W4_E_DTYPE, "unknown a_dtype");
+  if (group_mode != 0 && group_mode != 1) return fail(W4_E_SHAPE, "group_mode must be 0 or 1");
+  if (N <= 0 || K <= 0 || m_lo < 0 || m_hi < m_lo)
+    return fail(W4_E_SHAPE, "need N > 0, K > 0, 0 <= m_lo <= m_hi");
+  if (path < 0 || path > 2) return fail(W4_E_SHAPE, "path must be 0, 1 or 2");
+  if (splitk < 0 || splitk > 64) return fail(W4_E_SHAPE, "splitk must be in [0, 64]");
+  if (tile_m != 0 && tile_m != 64 && tile_m != 128) return fail(W4_E_SHAPE, "tile_m must be 0, 64 or 128");
+  if (strips < 0 || strips > 2) return fail(W4_E_SHAPE, "strips must be 0, 1 or 2");
+  if (path == 1 && m_hi > 16) return fail(W4_E_SHAPE, "the small-M kernel handles M <= 16");
+  std::lock_guard<std::mutex> lock(g_sched_mutex);
+  // a later entry for the same problems replaces an earlier one
+  g_sched_user.insert(g_sched_user.begin(),
+                      SchedEntry{a_dtype, group_mode, N, K, m_lo, m_hi, path, splitk, tile_m, strips});
+  return ok();
+}
+
+int w4_schedule_clear(void) {
+  std::lock_guard<std::mutex> lock(g_sched_mutex);
+  g_sched_user.clear();
+  return ok();
 }
 
 }  // extern "C"

@@ -11,6 +11,7 @@ import re
 import pytest
 
 import mixed_precision_quantized_prepack_amd as w4
+from tests.schedule_table import builtin_schedule_entries
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "w4.h")
@@ -163,9 +164,20 @@ def test_partials_window_validation(lib):
     assert f(FAKE, 3, FAKE, 0, 128, 4, 32, 256, 0, 4, 0, 32, None, None, 0, None) == E_NULL
 
 
-def test_plan_choices(lib):
-    """Kernel choice and K split for the int8 per-channel 8192x21760 sweep on a
-    256-CU part (the CU count the library assumes without a device)."""
+@pytest.fixture
+def heuristic_only(lib):
+    """The heuristic alone: the schedule table switched off."""
+    w4.set_option("schedule_table", 0)
+    try:
+        yield
+    finally:
+        w4.set_option("schedule_table", 1)
+
+
+def test_plan_choices(lib, heuristic_only):
+    """Kernel choice and K split of the heuristic for the int8 per-channel
+    8192x21760 sweep on a 256-CU part (the CU count the library assumes
+    without a device)."""
     plans = {M: w4.gemm_plan(M, 8192, 21760, -1, w4.I8) for M in (1, 16, 64, 128, 256, 512, 1024, 4096)}
     assert plans[1][0] == plans[16][0] == 1                      # small-M kernel
     assert plans[1][3] == 32                                     # two 16-column strips per wave
@@ -175,6 +187,11 @@ def test_plan_choices(lib):
     assert w4.gemm_plan(1, 22016, 4096, 128, w4.I8)[3] == 16
     assert w4.gemm_plan(16, 22016, 4096, 128, w4.I8)[3] == 32
     assert w4.gemm_plan(16, 4096, 11008, 128, w4.I8)[3] == 16
+    # grouped int8 K splits: the most that keep one workgroup per CU (at least 4 K blocks each)
+    assert w4.gemm_plan(64, 12288, 4096, 128, w4.I8)[1] == 4          # 48 tiles
+    assert w4.gemm_plan(128, 22016, 4096, 128, w4.I8)[1] == 1         # 172 tiles
+    assert w4.gemm_plan(32, 4096, 11008, 128, w4.I8)[1] == 16         # 16 tiles, 86 K blocks
+    assert w4.gemm_plan(32, 4096, 4096, 128, w4.I8)[1] == 8           # 32 K blocks
     # grouped int8 and fp8: 128 x 128 tiles once there is one per CU, else 64 x 256
     assert w4.gemm_plan(1024, 22016, 4096, 128, w4.I8)[2:] == (128, 128)
     assert w4.gemm_plan(128, 22016, 4096, 128, w4.I8)[2:] == (64, 256)
@@ -190,7 +207,7 @@ def test_plan_choices(lib):
         w4.set_option("force_path", 0)
 
 
-def test_options_and_plans(lib):
+def test_options_and_plans(lib, heuristic_only):
     try:
         assert lib.w4_set_option(b"nonsense", 1) == E_UNSUP
         assert lib.w4_set_option(b"force_path", 5) == E_SHAPE
@@ -221,3 +238,67 @@ def test_binding_refuses_cpu_tensors(lib):
     x = torch.zeros((4, 64), dtype=torch.float16)
     with pytest.raises(ValueError):
         w4.quant_act_per_token(x)
+
+
+def test_schedule_add_validation(lib):
+    f = lib.w4_schedule_add
+    assert f(9, 0, 8192, 21760, 1, 16, 1, 2, 0, 0) == E_DTYPE
+    assert f(3, 2, 8192, 21760, 1, 16, 1, 2, 0, 0) == E_SHAPE         # group mode
+    assert f(3, 0, 8192, 21760, 17, 16, 2, 2, 0, 0) == E_SHAPE        # m_hi < m_lo
+    assert f(3, 0, 8192, 21760, 1, 64, 1, 2, 0, 0) == E_SHAPE         # small-M kernel above M = 16
+    assert f(3, 0, 8192, 21760, 1, 16, 3, 2, 0, 0) == E_SHAPE
+    assert f(3, 0, 8192, 21760, 1, 16, 2, 65, 0, 0) == E_SHAPE
+    assert f(3, 0, 8192, 21760, 1, 16, 2, 2, 96, 0) == E_SHAPE
+    assert f(3, 0, 8192, 21760, 1, 16, 1, 2, 0, 3) == E_SHAPE
+
+
+def test_schedule_table_lookup(lib):
+    try:
+        w4.schedule_clear()
+        base = {M: w4.gemm_plan(M, 8192, 21760, -1, w4.I8) for M in (8, 16, 17, 64)}
+        w4.schedule_add(w4.I8, False, 8192, 21760, 9, 16, path=2, splitk=4, tile_m=64)
+        assert w4.gemm_plan(16, 8192, 21760, -1, w4.I8) == (2, 4, 64, 256)
+        assert w4.gemm_plan(9, 8192, 21760, -1, w4.I8)[:2] == (2, 4)
+        assert w4.gemm_workspace_bytes(16, 8192, 21760, -1, w4.I8) == 4 * 16 * 8192 * 4
+        # outside the M range, another N or grouping, or another dtype: unchanged
+        assert w4.gemm_plan(8, 8192, 21760, -1, w4.I8) == base[8]
+        assert w4.gemm_plan(17, 8192, 21760, -1, w4.I8) == base[17]
+        assert w4.gemm_plan(16, 8192, 21760, -1, w4.FP8_E4M3)[0] == 1
+        # a newer entry for the same problems wins; fields left at 0 go to the heuristic
+        w4.schedule_add(w4.I8, False, 8192, 21760, 16, 16, path=1, splitk=0, strips=1)
+        p16 = w4.gemm_plan(16, 8192, 21760, -1, w4.I8)
+        assert p16[0] == 1 and p16[3] == 16
+        # the options force their fields and skip the table
+        w4.set_option("splitk", 2)
+        assert w4.gemm_plan(9, 8192, 21760, -1, w4.I8)[:2] == (1, 2)
+        w4.set_option("splitk", 0)
+        # schedule_table = 0: heuristic alone
+        w4.set_option("schedule_table", 0)
+        assert w4.gemm_plan(16, 8192, 21760, -1, w4.I8) == base[16]
+        w4.set_option("schedule_table", 1)
+        # an entry that does not fit the problem (K split above K/128) is passed over
+        w4.schedule_add(w4.I8, False, 8192, 21760, 64, 64, path=2, splitk=64)
+        assert w4.gemm_plan(64, 8192, 21760, -1, w4.I8)[1] <= 21760 // 128
+        w4.schedule_add(w4.I8, True, 4096, 256, 64, 64, path=2, splitk=8)
+        assert w4.gemm_plan(64, 4096, 256, 128, w4.I8)[1] <= 2
+        w4.schedule_clear()
+        assert {M: w4.gemm_plan(M, 8192, 21760, -1, w4.I8) for M in (8, 16, 17, 64)} == base
+    finally:
+        w4.set_option("splitk", 0)
+        w4.set_option("schedule_table", 1)
+        w4.schedule_clear()
+
+
+def test_builtin_schedule_entries_fit_their_problems(lib):
+    """Every built-in entry is taken at both ends of its M range (none is
+    passed over for not fitting)."""
+    w4.schedule_clear()
+    for a_dtype, grouped, N, K, m_lo, m_hi, path, splitk, tile_m, strips in builtin_schedule_entries():
+        gs = 128 if grouped else -1
+        for M in (m_lo, m_hi):
+            p = w4.gemm_plan(M, N, K, gs, a_dtype)
+            assert p[0] == path and (splitk == 0 or p[1] == splitk), (N, K, M)
+            if path == 2 and tile_m:
+                assert p[2] == tile_m, (N, K, M)
+            if path == 1 and strips:
+                assert p[3] == 16 * strips, (N, K, M)
