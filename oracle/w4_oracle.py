@@ -354,19 +354,41 @@ def _exact_int_matmul(A: np.ndarray, B: np.ndarray) -> np.ndarray:
     return np.rint(A.astype(np.float64) @ B.astype(np.float64).T).astype(np.int64)
 
 
+def zero_point_weights(w_logical: np.ndarray, K: int, zeros: np.ndarray, group_size: int) -> np.ndarray:
+    """Asymmetric weights: w[n, k] = u[n, k] - z[n, k // group_size] (int64).
+
+    u is the raw 4-bit code (0..15) and z the integer zero-point of the
+    weight's group; [Marlin W4A8 PR] review (symmetric quantisation only is
+    named as a limit of QQQ), with the zero-point convention of the W4A16 API
+    page (raw zero-points, subtracted before the scale).
+    """
+    u = nibbles(w_logical, K)
+    z = np.asarray(zeros, dtype=np.int64).reshape(u.shape[0], -1)
+    assert z.shape[1] * group_size == K
+    return u - np.repeat(z, group_size, axis=1)
+
+
 def w4a8_group_partials(codes: np.ndarray, q_dtype: str, w_logical: np.ndarray, K: int,
-                        wtype: str, group_size: int, rows=None, cols=None) -> np.ndarray:
+                        wtype: str, group_size: int, rows=None, cols=None,
+                        zeros: Optional[np.ndarray] = None) -> np.ndarray:
     """P[g, m, n] = sum_{k in group g} A_int[m, k] * w[n, k]   (int64, exact).
 
     A_int is the int8 code (int8 activations) or 512 * fp8 value (fp8
     activations), so for fp8 the partial's value is P * 2**-9.  ``rows`` /
-    ``cols`` restrict the computation to a sub-matrix of the output.
+    ``cols`` restrict the computation to a sub-matrix of the output.  With
+    ``zeros`` ([N, G] integers) the weights are the asymmetric u - z (wtype
+    must be "uint4").
     """
     gs = K if group_size in (-1, K) else group_size
     assert K % gs == 0
     A = activation_integers(codes if rows is None else codes[rows], q_dtype)
     wl = w_logical if cols is None else w_logical[cols]
-    W = weight_values(wl, K, wtype)
+    if zeros is None:
+        W = weight_values(wl, K, wtype)
+    else:
+        assert wtype == "uint4"
+        z = np.asarray(zeros).reshape(w_logical.shape[0], -1)
+        W = zero_point_weights(wl, K, z if cols is None else z[cols], gs)
     G = K // gs
     P = np.empty((G, A.shape[0], W.shape[0]), dtype=np.int64)
     for g in range(G):
@@ -389,11 +411,12 @@ def w4a8_gemm(codes: np.ndarray, q_dtype: str, a_scales: np.ndarray,
               w_logical: np.ndarray, K: int, wtype: str,
               w_scales: np.ndarray, s_dtype: str, group_size: int,
               out_dtype: str, bias_bits: Optional[np.ndarray] = None,
-              rows=None, cols=None) -> dict:
+              rows=None, cols=None, zeros: Optional[np.ndarray] = None) -> dict:
     """W4A8 GEMM:  out[m, n] = RNE_out( s_a[m] * sum_g s_w[n, g] * P[g, m, n] * unit
                                          + bias[n] )
 
-    P are the exact integer partials above; unit = 1 (int8) or 2**-9 (fp8).
+    P are the exact integer partials above (with ``zeros``: of the asymmetric
+    weights u - z); unit = 1 (int8) or 2**-9 (fp8).
     Per-channel scales are [N] (one group spanning K).  All arithmetic after
     the stored inputs is float64 and the result is rounded once.
 
@@ -405,10 +428,14 @@ def w4a8_gemm(codes: np.ndarray, q_dtype: str, a_scales: np.ndarray,
     """
     gs = K if group_size in (-1, K) else group_size
     G = K // gs
-    P = w4a8_group_partials(codes, q_dtype, w_logical, K, wtype, gs, rows, cols)
+    P = w4a8_group_partials(codes, q_dtype, w_logical, K, wtype, gs, rows, cols, zeros)
     A = activation_integers(codes if rows is None else codes[rows], q_dtype)
     wl = w_logical if cols is None else w_logical[cols]
-    Wabs = np.abs(weight_values(wl, K, wtype))
+    if zeros is None:
+        Wabs = np.abs(weight_values(wl, K, wtype))
+    else:
+        z = np.asarray(zeros).reshape(w_logical.shape[0], -1)
+        Wabs = np.abs(zero_point_weights(wl, K, z if cols is None else z[cols], gs))
     sw = _scales_f64(w_scales, s_dtype)
     sw = sw.reshape(sw.shape[0], -1)
     if cols is not None:
