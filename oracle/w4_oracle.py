@@ -428,7 +428,8 @@ def w4a8_gemm(codes: np.ndarray, q_dtype: str, a_scales: np.ndarray,
     """
     gs = K if group_size in (-1, K) else group_size
     G = K // gs
-    P = w4a8_group_partials(codes, q_dtype, w_logical, K, wtype, gs, rows, cols, zeros)
+    P = (w4a8_group_partials(codes, q_dtype, w_logical, K, wtype, gs, rows, cols) if zeros is None else
+         w4a8_group_partials(codes, q_dtype, w_logical, K, wtype, gs, rows, cols, zeros=zeros))
     A = activation_integers(codes if rows is None else codes[rows], q_dtype)
     wl = w_logical if cols is None else w_logical[cols]
     if zeros is None:
