@@ -243,6 +243,31 @@ W4_API int w4a8_gemm(const void* aq, int a_dtype, const float* a_scales, const v
               void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Asymmetric W4A8 GEMM (weights with zero-points).
+ *
+ * "support W4A8 Marlin kernel", limitations comment: QQQ's W4A8 handles
+ * symmetric weights only.  This entry point takes raw uint4 codes u with an
+ * integer zero-point per (column, group), as the W4A16 API page does for
+ * W4A16 (raw zero-points, subtracted before the scale):
+ *
+ *   out[m,n] = RNE_out( s_a[m] * sum_g s_w[n,g] * sum_{k in g} a[m,k] * (u[n,k] - z[n,g])
+ *                       + bias[n] )
+ *
+ * with int8 activation codes a.  The inner sums are exact (int32).
+ *
+ * zeros   : device, [N][K/group_size] (per channel: [N]) of z_dtype (W4_F16,
+ *           W4_BF16 or W4_F32), integer values 0..15.
+ * b_packed: PB-v1 bytes of the raw codes (w4_prepack_B, W4_OPERAND_I8).
+ * Other arguments as w4a8_gemm with a_dtype W4_I8.  The workspace is the
+ * one w4_gemm_workspace_bytes(M, N, K, group_size, W4_I8) reports.  Per
+ * channel needs K <= 65536.  Errors as w4a8_gemm.
+ * ------------------------------------------------------------------------- */
+W4_API int w4a8_gemm_zp(const void* aq, const float* a_scales, const void* b_packed, const void* b_scales,
+                        int s_dtype, const void* zeros, int z_dtype, int64_t group_size, const void* bias,
+                        void* out, int out_dtype, int64_t M, int64_t N, int64_t K, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
  * W4A16 GEMM.
  *
  * Follows the "...mixed_precision.rdna_hybrid_w4a16" API page

@@ -23,7 +23,7 @@ from typing import Optional
 __all__ = [
     "LIB_PATH", "lib", "W4Error", "prepack_B", "prepack_B_from_exllama", "prepack_B_bytes", "quant_act_per_token",
     "quant_act_per_tensor", "rmsnorm_quant_per_token",
-    "w4a8_gemm", "w4a16_gemm", "w4a8_gemm_partials", "w4a16_gemm_partials",
+    "w4a8_gemm", "w4a8_gemm_zp", "w4a16_gemm", "w4a8_gemm_partials", "w4a16_gemm_partials",
     "gemm_workspace_bytes", "gemm_plan", "set_option", "get_option", "schedule_add", "schedule_clear",
     "EXPORTED_SYMBOLS",
 ]
@@ -59,6 +59,8 @@ _SIGNATURES = [
     ("w4_gemm_workspace_bytes", _sz, [_i64, _i64, _i64, _i64, _int]),
     ("w4a8_gemm", _int, [_vp, _int, _vp, _vp, _int, _vp, _int, _i64, _vp, _vp, _int,
                          _i64, _i64, _i64, _vp, _sz, _vp]),
+    ("w4a8_gemm_zp", _int, [_vp, _vp, _vp, _vp, _int, _vp, _int, _i64, _vp, _vp, _int,
+                            _i64, _i64, _i64, _vp, _sz, _vp]),
     ("w4a16_gemm", _int, [_vp, _int, _vp, _int, _vp, _vp, _i64, _vp, _vp, _i64, _i64, _i64,
                           _vp, _sz, _vp]),
     ("w4a8_gemm_partials", _int, [_vp, _int, _vp, _int, _i64, _i64, _i64, _i64, _i64, _i64,
@@ -284,6 +286,27 @@ def w4a8_gemm(aq, a_scales, b_packed, b_scales, group_size: int, out_dtype, wtyp
         _dev_ptr(aq, "aq"), a_dt, _dev_ptr(a_scales, "a_scales"), _dev_ptr(b_packed, "b_packed"),
         WTYPES[wtype], _dev_ptr(b_scales, "b_scales"), _dtype_code(b_scales.dtype), group_size,
         _dev_ptr(bias, "bias"), _dev_ptr(out, "out"), o_dt, M, N, K, wsp, wsb, _stream(aq)))
+    return out
+
+
+def w4a8_gemm_zp(aq, a_scales, b_packed, b_scales, zeros, group_size: int, out_dtype, bias=None, out=None,
+                 workspace=None):
+    """Asymmetric W4A8 GEMM (include/w4.h): aq [M, K] int8, a_scales [M] fp32,
+    b_packed PB-v1 (I8 operand) of raw uint4 codes, b_scales and zeros
+    [N] or [N, K/G] (zeros: integers 0..15 in fp16 / bf16 / fp32)."""
+    torch = _torch()
+    M, K = aq.shape
+    N = b_scales.shape[0]
+    if aq.dtype != torch.int8:
+        raise ValueError("aq must be int8 codes")
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=aq.device)
+    wsp, wsb = _workspace(workspace, gemm_workspace_bytes(M, N, K, group_size, I8), aq.device)
+    _check("w4a8_gemm_zp", lib().w4a8_gemm_zp(
+        _dev_ptr(aq, "aq"), _dev_ptr(a_scales, "a_scales"), _dev_ptr(b_packed, "b_packed"),
+        _dev_ptr(b_scales, "b_scales"), _dtype_code(b_scales.dtype), _dev_ptr(zeros, "zeros"),
+        _dtype_code(zeros.dtype), group_size, _dev_ptr(bias, "bias"), _dev_ptr(out, "out"),
+        _dtype_code(out_dtype), M, N, K, wsp, wsb, _stream(aq)))
     return out
 
 

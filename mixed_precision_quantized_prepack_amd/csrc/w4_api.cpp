@@ -131,13 +131,15 @@ int check_group(int64_t group_size, int64_t K) {
 // kernel with enough K-splitting waves to keep ~16 waves per CU in flight;
 // larger M uses the tiled kernel, split along K while there are fewer tiles
 // than CUs.  Fields of `forced` that are nonzero replace the heuristic's
-// choice (and must fit the problem).
-int plan_with(int64_t M, int64_t N, int64_t K, bool grouped, int op, const Sched& forced, GemmPlan* plan) {
+// choice (and must fit the problem).  zp: asymmetric int8, whose small-M
+// kernel keeps a second (zero-point) table.
+int plan_with(int64_t M, int64_t N, int64_t K, bool grouped, int op, const Sched& forced, GemmPlan* plan,
+              bool zp = false) {
   const int64_t fp = forced.path, fs = forced.splitk;
   const int64_t KB = K / 128;
   const int cu = cu_count();
   plan->path = fp ? (int)fp : (M <= 16 ? PATH_SKINNY : PATH_TILED);
-  tiled_tile(op, grouped, 0, &plan->bm, &plan->bn);
+  tiled_tile(op, grouped, 0, &plan->bm, &plan->bn, zp);
   // strips of 16 columns per wave of the small-M kernel: two strips share
   // one activation fragment.  Grouped problems take two only when the
   // fragment is worth sharing (M >= 8) and N leaves enough workgroups.
@@ -145,14 +147,18 @@ int plan_with(int64_t M, int64_t N, int64_t K, bool grouped, int op, const Sched
   const bool two = N % 32 == 0 && (!grouped || (M >= 8 && N >= 8192));
   int64_t ns = fns ? fns : (two ? 2 : 1);
   const int64_t groups = grouped ? KB : 1;
-  if (plan->path == PATH_SKINNY && skinny_table_bytes(op, grouped, groups, (int)ns) > kSkinnyTableMax) {
+  bool one_split = false;
+  if (plan->path == PATH_SKINNY && skinny_table_bytes(op, grouped, groups, (int)ns, zp) > kSkinnyTableMax) {
     // the scale / zero-point tables would not fit the small-M kernel's LDS
-    if (!fns && ns == 2 && skinny_table_bytes(op, grouped, groups, 1) <= kSkinnyTableMax) {
+    if (!fns && ns == 2 && skinny_table_bytes(op, grouped, groups, 1, zp) <= kSkinnyTableMax) {
       ns = 1;
     } else if (fp || fns) {
       return fail(W4_E_UNSUPPORTED, "the small-M kernel's LDS tables do not fit K=%lld", (long long)K);
     } else {
       plan->path = PATH_TILED;
+      // where only the zero-point table tips the balance, the symmetric plan
+      // (whose workspace size callers query) has none: no K split either
+      one_split = zp && skinny_table_bytes(op, grouped, groups, 1) <= kSkinnyTableMax;
     }
   }
   if (plan->path == PATH_SKINNY) {
@@ -186,17 +192,19 @@ int plan_with(int64_t M, int64_t N, int64_t K, bool grouped, int op, const Sched
     const int64_t fbm = forced.tile_m;
     if (byte) {
       int tall_bm, tall_bn;
-      tiled_tile(op, grouped, 1, &tall_bm, &tall_bn);
+      tiled_tile(op, grouped, 1, &tall_bm, &tall_bn, zp);
       const int64_t tall_tiles = ((M + tall_bm - 1) / tall_bm) * ((N + tall_bn - 1) / tall_bn);
       const int64_t need = (op == OP_I8 && !grouped) ? 2LL * cu : (int64_t)cu;
       const bool tall = fbm ? fbm == 128 : tall_tiles >= need;
-      tiled_tile(op, grouped, tall ? 1 : 0, &plan->bm, &plan->bn);
+      tiled_tile(op, grouped, tall ? 1 : 0, &plan->bm, &plan->bn, zp);
     } else if (fbm && fbm != plan->bm) {
       return fail(W4_E_SHAPE, "tiled_bm=%lld is not available for this problem", (long long)fbm);
     }
     int64_t s;
     if (fs) {
       s = fs;
+    } else if (one_split) {
+      s = 1;
     } else {
       // K splits: the fewest that give two workgroups per CU, or one per CU
       // when there are very few tiles (each split adds an M x N fp32 slot
@@ -249,15 +257,15 @@ bool lookup_schedule(int op, bool grouped, int64_t M, int64_t N, int64_t K, Sche
 // The options, when any is set, force their fields.  Otherwise a matching
 // schedule-table entry (run-time entries first, then the built-in ones) is
 // taken if it fits the problem, and the heuristic decides the rest.
-int make_plan(int64_t M, int64_t N, int64_t K, bool grouped, int op, GemmPlan* plan) {
+int make_plan(int64_t M, int64_t N, int64_t K, bool grouped, int op, GemmPlan* plan, bool zp = false) {
   const Sched opts{g_force_path.load(), g_splitk.load(), g_tiled_bm.load(), g_skinny_strips.load()};
-  if (opts.any()) return plan_with(M, N, K, grouped, op, opts, plan);
+  if (opts.any()) return plan_with(M, N, K, grouped, op, opts, plan, zp);
   if (g_schedule_table.load()) {
     Sched t;
-    if (lookup_schedule(op, grouped, M, N, K, &t) && plan_with(M, N, K, grouped, op, t, plan) == W4_OK)
+    if (lookup_schedule(op, grouped, M, N, K, &t) && plan_with(M, N, K, grouped, op, t, plan, zp) == W4_OK)
       return W4_OK;
   }
-  return plan_with(M, N, K, grouped, op, Sched{}, plan);
+  return plan_with(M, N, K, grouped, op, Sched{}, plan, zp);
 }
 
 size_t workspace_for(const GemmPlan& plan, int64_t M, int64_t N) {
@@ -265,11 +273,11 @@ size_t workspace_for(const GemmPlan& plan, int64_t M, int64_t N) {
   return (size_t)plan.splitk * (size_t)M * (size_t)N * 4u;
 }
 
-// Shared front end of the four GEMM entry points.
+// Shared front end of the GEMM entry points.
 int run_gemm(GemmArgs& args, int op, bool grouped, bool flip, void* workspace, size_t workspace_bytes,
-             void* stream) {
+             void* stream, bool zp = false) {
   GemmPlan plan;
-  if (int st = make_plan(args.M, args.N, args.K, grouped, op, &plan)) return st;
+  if (int st = make_plan(args.M, args.N, args.K, grouped, op, &plan, zp)) return st;
   const size_t need = workspace_for(plan, args.M, args.N);
   if (need) {
     if (!workspace || workspace_bytes < need)
@@ -279,7 +287,7 @@ int run_gemm(GemmArgs& args, int op, bool grouped, bool flip, void* workspace, s
   }
   args.ws = workspace;
   if (args.M == 0) return ok();
-  hipError_t e = launch_gemm(args, op, grouped, flip, plan, (hipStream_t)stream);
+  hipError_t e = launch_gemm(args, op, grouped, flip, zp, plan, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "GEMM launch");
   return ok();
 }
@@ -455,8 +463,46 @@ int w4a8_gemm(const void* aq, int a_dtype, const float* a_scales, const void* b_
   args.G = (int)(K / g);
   args.s_dtype = s_dtype;
   args.out_dtype = out_dtype;
+  args.z_dtype = W4_F16;
   args.mode = MODE_OUTPUT;
   return run_gemm(args, op_of(a_dtype), g != K, wtype == W4_UINT4B8, workspace, workspace_bytes, stream);
+}
+
+int w4a8_gemm_zp(const void* aq, const float* a_scales, const void* b_packed, const void* b_scales, int s_dtype,
+                 const void* zeros, int z_dtype, int64_t group_size, const void* bias, void* out, int out_dtype,
+                 int64_t M, int64_t N, int64_t K, void* workspace, size_t workspace_bytes, void* stream) {
+  if (int st = validate_w4a8(aq, W4_I8, b_packed, W4_UINT4B8, group_size, M, N, K)) return st;
+  if (s_dtype != W4_F32 && s_dtype != W4_F16 && s_dtype != W4_BF16)
+    return fail(W4_E_DTYPE, "s_dtype must be W4_F32, W4_F16 or W4_BF16");
+  if (z_dtype != W4_F32 && z_dtype != W4_F16 && z_dtype != W4_BF16)
+    return fail(W4_E_DTYPE, "z_dtype must be W4_F32, W4_F16 or W4_BF16");
+  if (out_dtype != W4_F16 && out_dtype != W4_BF16) return fail(W4_E_DTYPE, "out_dtype must be W4_F16 or W4_BF16");
+  const int64_t g = resolve_group(group_size, K);
+  // 16 sum(a (u - z)) in int32 over a whole-K group: |.| <= 16 * 127 * 15 * K
+  if (g == K && K > 65536) return fail(W4_E_SHAPE, "per-channel zero-points need K <= 65536 (int32 range)");
+  if (!b_scales || !zeros || (M > 0 && (!a_scales || !out)))
+    return fail(W4_E_NULL, "a_scales, b_scales, zeros and out are required");
+  if (!aligned(out, 16) || !aligned(a_scales, 4) || !aligned(b_scales, s_dtype == W4_F32 ? 4 : 2) ||
+      !aligned(zeros, z_dtype == W4_F32 ? 4 : 2) || !aligned(bias, 2))
+    return fail(W4_E_ALIGN, "out must be 16-byte aligned; scales, zeros and bias naturally aligned");
+  GemmArgs args{};
+  args.a = aq;
+  args.a_scales = a_scales;
+  args.b = static_cast<const uint32_t*>(b_packed);
+  args.s = b_scales;
+  args.z = zeros;
+  args.bias = bias;
+  args.out = out;
+  args.M = M;
+  args.N = N;
+  args.K = K;
+  args.G = (int)(K / g);
+  args.s_dtype = s_dtype;
+  args.out_dtype = out_dtype;
+  args.z_dtype = z_dtype;
+  args.mode = MODE_OUTPUT;
+  // raw uint4 codes: the int8 operand holds 16 (u - 8), the kernels subtract (z - 8) sum(a)
+  return run_gemm(args, OP_I8, g != K, true, workspace, workspace_bytes, stream, true);
 }
 
 static int validate_w4a16(const void* a, int a_dtype, const void* b_packed, int wtype, const void* zeros,
@@ -494,6 +540,7 @@ int w4a16_gemm(const void* a, int a_dtype, const void* b_packed, int wtype, cons
   args.G = (int)(K / g);
   args.s_dtype = a_dtype;
   args.out_dtype = a_dtype;
+  args.z_dtype = a_dtype;
   args.mode = MODE_OUTPUT;
   return run_gemm(args, op_of(a_dtype), g != K, false, workspace, workspace_bytes, stream);
 }
@@ -551,6 +598,7 @@ int w4a16_gemm_partials(const void* a, int a_dtype, const void* b_packed, int wt
   args.G = (int)(K / g);
   args.s_dtype = a_dtype;
   args.out_dtype = a_dtype;
+  args.z_dtype = a_dtype;
   args.mode = MODE_PARTIALS;
   args.m0 = m0;
   args.m1 = m1;

@@ -112,6 +112,16 @@ __device__ __forceinline__ void ones_mma(const u32x4* a, f32x4& ones) {
   for (int kw = 0; kw < 4; ++kw) ones = mma_bf16(one, a[kw], ones);
 }
 
+// Asymmetric int8 W4A8: the operand holds 16 (u - 8) (the uint4b8
+// expansion of the raw code u), so each group also needs 16 * sum(a), times
+// z - 8, to reach 16 * sum(a (u - z)) exactly.  A weight operand of 16s gives
+// that sum in every D row.
+__device__ __forceinline__ void ones_mma_i8(const u32x4* a, i32x4& ones) {
+  const u32x4 sixteen{0x10101010u, 0x10101010u, 0x10101010u, 0x10101010u};
+  ones = mma_i8(sixteen, a[0], ones);
+  ones = mma_i8(sixteen, a[1], ones);
+}
+
 // The group (or whole-K) dot product of one D element.
 template <int OP>
 __device__ __forceinline__ float partial_value(typename OpTraits<OP>::Acc acc, f32x4 ones, float zc,
@@ -129,7 +139,7 @@ __device__ __forceinline__ int32_t int_partial(typename OpTraits<OP>::Acc acc, i
 }
 
 __device__ __forceinline__ float zero_point(const GemmArgs& p, int64_t n, int g) {
-  return p.z ? load_as_f32(p.z, p.out_dtype, n * p.G + g) : 8.0f;
+  return p.z ? load_as_f32(p.z, p.z_dtype, n * p.G + g) : 8.0f;
 }
 
 __device__ __forceinline__ void store_out(const GemmArgs& p, int64_t m, int64_t n, float v) {
@@ -245,7 +255,7 @@ constexpr int waitcnt_vm_lgkm0(int vm) { return (vm & 15) | ((vm >> 4) << 14) | 
 // its D rows for a K block with one 16-byte LDS read, instead of a 64-lane
 // gather from memory per block (which costs the address pipeline as much as
 // the block's weights).  The table's size is set at launch.
-template <int OP, bool GROUPED, bool FLIP, int NS, bool PARTIALS>
+template <int OP, bool GROUPED, bool FLIP, int NS, bool PARTIALS, bool ZP>
 __global__ __launch_bounds__(64 * skinny_max_waves(OP, GROUPED)) void w4_gemm_skinny(GemmArgs p, int S) {
   using Acc = typename OpTraits<OP>::Acc;
   constexpr int EB = OpTraits<OP>::kElemBytes;
@@ -260,7 +270,8 @@ __global__ __launch_bounds__(64 * skinny_max_waves(OP, GROUPED)) void w4_gemm_sk
   const int r = lane & 15;
   const int kq = lane >> 4;
   constexpr bool partials = PARTIALS;  // verification mode: store group partials
-  const int zdt = p.out_dtype;                    // W4A16: zero-points in the activation dtype
+  const int zdt = p.z_dtype;                      // zero-point storage dtype
+  static_assert(!ZP || (OP == OP_I8 && FLIP), "zero-points: int8 operand from raw uint4 codes");
 
   const __amdgpu_buffer_rsrc_t rw =
       make_rsrc(reinterpret_cast<const uint8_t*>(p.b) + nb0 * KB * 1024, (int64_t)NS * KB * 1024);
@@ -270,12 +281,13 @@ __global__ __launch_bounds__(64 * skinny_max_waves(OP, GROUPED)) void w4_gemm_sk
   // (a product, not a branch: a branch here would wait for the kernel
   // arguments before anything else is issued)
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.s, (int64_t)(p.s != nullptr) * p.N * p.G * sbytes);
-  const __amdgpu_buffer_rsrc_t rz = make_rsrc(p.z, p.z ? p.N * p.G * 2 : 0);
+  const __amdgpu_buffer_rsrc_t rz = make_rsrc(p.z, p.z ? p.N * p.G * (zdt == W4_F32 ? 4 : 2) : 0);
   const uint32_t w_lane = (uint32_t)lane * 16;
   const uint32_t a_lane = (uint32_t)((r * p.K + kq * 32) * EB);
 
   Acc acc[NS];
   f32x4 ones = {};
+  i32x4 ones_i = {};   // asymmetric int8: 16 * sum(a)
   f32x4 tot[NS];
 #pragma unroll
   for (int j = 0; j < NS; ++j) {
@@ -305,7 +317,7 @@ __global__ __launch_bounds__(64 * skinny_max_waves(OP, GROUPED)) void w4_gemm_sk
     }
   }
   uint32_t zpc[NS][4];
-  if constexpr (OP == OP_BF16 && !GROUPED) {
+  if constexpr ((OP == OP_BF16 || ZP) && !GROUPED) {
 #pragma unroll
     for (int j = 0; j < NS; ++j)
 #pragma unroll
@@ -316,8 +328,9 @@ __global__ __launch_bounds__(64 * skinny_max_waves(OP, GROUPED)) void w4_gemm_sk
   u32x4 wv[2][U][NS];
   u32x4 av[2][U][AV];
   // LDS tables: tsc = group scales (grouped), tz = 128 + z (grouped bf16
-  // W4A16) or z (grouped fp16 W4A16), each [NS][G][16] fp32.
-  constexpr bool kTab = skinny_tables(OP, GROUPED) > 0;
+  // W4A16), z (grouped fp16 W4A16) or z - 8 (grouped asymmetric int8), each
+  // [NS][G][16] fp32.
+  constexpr bool kTab = skinny_tables(OP, GROUPED, ZP) > 0;
   extern __shared__ __attribute__((aligned(16))) float skinny_tab[];
   // (each table is followed by a 16-float pad that takes the stores of
   // staging slots past its end)
@@ -354,6 +367,7 @@ __global__ __launch_bounds__(64 * skinny_max_waves(OP, GROUPED)) void w4_gemm_sk
       const int k = wave + (kb + u) * S;
       const int g = GROUPED ? k : 0;
       if constexpr (OP == OP_BF16) ones_mma(av[buf][u], ones);
+      if constexpr (ZP) ones_mma_i8(av[buf][u], ones_i);
 #pragma unroll
       for (int j = 0; j < NS; ++j) {
         f16x2 nz = {};
@@ -375,14 +389,18 @@ __global__ __launch_bounds__(64 * skinny_max_waves(OP, GROUPED)) void w4_gemm_sk
             const int slot = (j * p.G + g) * 16 + 4 * kq;
             const f32x4 sv = *reinterpret_cast<const f32x4*>(&tsc[slot]);
             f32x4 zc = {};
-            if constexpr (OP == OP_BF16) zc = *reinterpret_cast<const f32x4*>(&tz[slot]);
+            if constexpr (OP == OP_BF16 || ZP) zc = *reinterpret_cast<const f32x4*>(&tz[slot]);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              const float pv = partial_value<OP>(acc[j], ones, zc[i], i);
+              // asymmetric int8: 16 * sum(a (u - z)), exact
+              int32_t ia = 0;
+              if constexpr (OP == OP_I8) ia = ZP ? acc[j][i] - (int32_t)zc[i] * ones_i[i] : acc[j][i];
+              const float pv = ZP ? (float)ia * 0.0625f : partial_value<OP>(acc[j], ones, zc[i], i);
               if (partials) {
-                if (in_window(p, r, n_d + i)) store_partial<OP>(p, g, r, n_d + i, pv, int_partial<OP>(acc[j], i));
+                if (in_window(p, r, n_d + i))
+                  store_partial<OP>(p, g, r, n_d + i, pv, ZP ? ia >> 4 : int_partial<OP>(acc[j], i));
               } else {
-                const float pf = (OP == OP_I8) ? (float)acc[j][i] : pv;
+                const float pf = (OP == OP_I8) ? (float)ia : pv;
                 tot[j][i] = fmaf(pf, sv[i], tot[j][i]);
               }
             }
@@ -391,6 +409,7 @@ __global__ __launch_bounds__(64 * skinny_max_waves(OP, GROUPED)) void w4_gemm_sk
 #pragma unroll
         for (int j = 0; j < NS; ++j) acc[j] = Acc{};
         ones = f32x4{};
+        ones_i = i32x4{};
       }
     }
   };
@@ -415,7 +434,7 @@ __global__ __launch_bounds__(64 * skinny_max_waves(OP, GROUPED)) void w4_gemm_sk
       const int g = g0 + gfirst + t * gstep;
       const uint32_t idx = (uint32_t)((nb0 * 16 + srow) * G + g);
       if constexpr (GROUPED) tws[t] = load_word(rs, p.s_dtype, idx, g < G && !partials);
-      if constexpr (OP == OP_BF16 || OP == OP_F16) twz[t] = load_word(rz, zdt, idx, g < G && p.z);
+      if constexpr (OP == OP_BF16 || OP == OP_F16 || ZP) twz[t] = load_word(rz, zdt, idx, g < G && p.z);
     }
   };
   auto stage_store = [&](int g0) {
@@ -431,6 +450,7 @@ __global__ __launch_bounds__(64 * skinny_max_waves(OP, GROUPED)) void w4_gemm_sk
       }
       if constexpr (OP == OP_BF16) tz[slot] = 128.0f + (p.z ? word_to_f32(twz[t], zdt, idx) : 8.0f);
       if constexpr (OP == OP_F16) tz[slot] = p.z ? word_to_f32(twz[t], zdt, idx) : 8.0f;
+      if constexpr (ZP) tz[slot] = (p.z ? word_to_f32(twz[t], zdt, idx) : 8.0f) - 8.0f;
     }
   };
   if constexpr (kTab) {
@@ -494,6 +514,9 @@ __global__ __launch_bounds__(64 * skinny_max_waves(OP, GROUPED)) void w4_gemm_sk
       uint32_t bits;
       if constexpr (GROUPED) {
         bits = __float_as_uint(tot[j][i]);
+      } else if constexpr (ZP) {
+        const int32_t zc = (int32_t)(p.z ? word_to_f32(zpc[j][i], zdt, (uint32_t)(n_d + i) * p.G) : 8.0f) - 8;
+        bits = (uint32_t)(acc[j][i] - zc * ones_i[i]);
       } else if constexpr (OP == OP_I8) {
         bits = (uint32_t)acc[j][i];
       } else {
@@ -631,7 +654,7 @@ __device__ __forceinline__ void stage_barrier() {
   asm volatile("" ::: "memory");
 }
 
-template <int OP, bool GROUPED, bool FLIP, int NT, int MT, bool SPLIT, bool PARTIALS>
+template <int OP, bool GROUPED, bool FLIP, int NT, int MT, bool SPLIT, bool PARTIALS, bool ZP>
 __global__ __launch_bounds__(256, 2) void w4_gemm_tiled(GemmArgs p, int splitk) {
   using Acc = typename OpTraits<OP>::Acc;
   constexpr int EB = OpTraits<OP>::kElemBytes;
@@ -651,7 +674,8 @@ __global__ __launch_bounds__(256, 2) void w4_gemm_tiled(GemmArgs p, int splitk) 
   // loads of later stages.
   constexpr bool kFold = GROUPED && !PARTIALS;
   constexpr int BNW = 4 * NT * 16;   // columns of the workgroup
-  constexpr int kTables = kFold ? (OP == OP_BF16 ? 2 : 1) : 0;
+  constexpr int kTables = kFold ? ((OP == OP_BF16 || ZP) ? 2 : 1) : 0;
+  static_assert(!ZP || (OP == OP_I8 && FLIP), "zero-points: int8 operand from raw uint4 codes");
   __shared__ __attribute__((aligned(1024))) uint8_t lds[3 * STAGE + kTables * 2 * BNW * 4];
   float* const gsc = reinterpret_cast<float*>(lds + 3 * STAGE);   // [2][BNW]
   float* const gzc = gsc + 2 * BNW;                               // [2][BNW]
@@ -683,8 +707,8 @@ __global__ __launch_bounds__(256, 2) void w4_gemm_tiled(GemmArgs p, int splitk) 
   // (a product, not a branch: a branch here would wait for the kernel
   // arguments before anything else is issued)
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.s, (int64_t)(p.s != nullptr) * p.N * p.G * sbytes);
-  const __amdgpu_buffer_rsrc_t rz = make_rsrc(p.z, p.z ? p.N * p.G * 2 : 0);
-  const int zdt = p.out_dtype;  // W4A16: zero-points in the activation dtype
+  const int zdt = p.z_dtype;    // zero-point storage dtype
+  const __amdgpu_buffer_rsrc_t rz = make_rsrc(p.z, p.z ? p.N * p.G * (zdt == W4_F32 ? 4 : 2) : 0);
 
   // Load j of this wave fills tile rows [(4 j + wave) RPL, +RPL); lane l
   // writes LDS bytes [16 l, 16 l + 16) of that range, i.e. row l / CPR, slot
@@ -722,7 +746,7 @@ __global__ __launch_bounds__(256, 2) void w4_gemm_tiled(GemmArgs p, int splitk) 
     if constexpr (GROUPED) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
-        if constexpr (PARTIALS && OP == OP_BF16) {
+        if constexpr (PARTIALS && (OP == OP_BF16 || ZP)) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const uint32_t n = (uint32_t)((nb_base + nt) * 16 + 4 * kq + i);
@@ -747,6 +771,7 @@ __global__ __launch_bounds__(256, 2) void w4_gemm_tiled(GemmArgs p, int splitk) 
   Acc acc[NT][MT];
   f32x4 tot[NT][MT];
   f32x4 ones[MT];
+  i32x4 onesi[MT];   // asymmetric int8: 16 * sum(a) of the tile rows
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
@@ -755,7 +780,10 @@ __global__ __launch_bounds__(256, 2) void w4_gemm_tiled(GemmArgs p, int splitk) 
       tot[nt][mt] = f32x4{};
     }
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) ones[mt] = f32x4{};
+  for (int mt = 0; mt < MT; ++mt) {
+    ones[mt] = f32x4{};
+    onesi[mt] = i32x4{};
+  }
 
   // LDS offset of this lane's fragment chunk j in rows r (+ 16 mt).
   int frag_off[AV];
@@ -775,7 +803,7 @@ __global__ __launch_bounds__(256, 2) void w4_gemm_tiled(GemmArgs p, int splitk) 
     if constexpr (kFold) {
       const uint32_t idx = col_n * (uint32_t)p.G + (uint32_t)kb;
       col_sw = load_word(rs, p.s_dtype, idx, kb < kb1 && col_n < (uint32_t)p.N);
-      if constexpr (OP == OP_BF16) col_zw = load_word(rz, zdt, idx, kb < kb1 && p.z && col_n < (uint32_t)p.N);
+      if constexpr (OP == OP_BF16 || ZP) col_zw = load_word(rz, zdt, idx, kb < kb1 && p.z && col_n < (uint32_t)p.N);
     }
   };
   auto store_col = [&](int kb) {
@@ -786,6 +814,7 @@ __global__ __launch_bounds__(256, 2) void w4_gemm_tiled(GemmArgs p, int splitk) 
       if constexpr (OP == OP_I8) sv *= 0.0625f;
       gsc[slot * BNW + col] = sv;
       if constexpr (OP == OP_BF16) gzc[slot * BNW + col] = 128.0f + (p.z ? word_to_f32(col_zw, zdt, idx) : 8.0f);
+      if constexpr (ZP) gzc[slot * BNW + col] = (p.z ? word_to_f32(col_zw, zdt, idx) : 8.0f) - 8.0f;
     }
   };
 
@@ -833,7 +862,7 @@ __global__ __launch_bounds__(256, 2) void w4_gemm_tiled(GemmArgs p, int splitk) 
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         scv[nt] = *reinterpret_cast<const f32x4*>(&gsc[slot * BNW + (wave * NT + nt) * 16 + 4 * kq]);
-        if constexpr (OP == OP_BF16)
+        if constexpr (OP == OP_BF16 || ZP)
           zcv[nt] = *reinterpret_cast<const f32x4*>(&gzc[slot * BNW + (wave * NT + nt) * 16 + 4 * kq]);
       }
       // Row mt's MFMAs start from zero; row mt - 1 is folded while they run.
@@ -841,7 +870,9 @@ __global__ __launch_bounds__(256, 2) void w4_gemm_tiled(GemmArgs p, int splitk) 
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           float pv;
-          if constexpr (OP == OP_I8)
+          if constexpr (ZP)
+            pv = (float)(acc[nt][mt][i] - (int32_t)zcv[nt][i] * onesi[mt][i]);
+          else if constexpr (OP == OP_I8)
             pv = (float)acc[nt][mt][i];
           else if constexpr (OP == OP_BF16)
             pv = fmaf(-zcv[nt][i], ones[mt][i], acc[nt][mt][i]);
@@ -866,6 +897,11 @@ __global__ __launch_bounds__(256, 2) void w4_gemm_tiled(GemmArgs p, int splitk) 
             ones_mma(af[mt], o);
             ones[mt] = o;
           }
+          if (nt == NT - 1 && ZP) {
+            i32x4 o = i32x4{};
+            ones_mma_i8(af[mt], o);
+            onesi[mt] = o;
+          }
           if (mt > 0) fold_block(nt, mt - 1);
           __builtin_amdgcn_sched_barrier(0);
         }
@@ -878,10 +914,11 @@ __global__ __launch_bounds__(256, 2) void w4_gemm_tiled(GemmArgs p, int splitk) 
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) block_mma<OP>(e[nt], af[mt], acc[nt][mt]);
         if constexpr (OP == OP_BF16) ones_mma(af[mt], ones[mt]);
+        if constexpr (ZP) ones_mma_i8(af[mt], onesi[mt]);
       }
       // Issue order: the fragment reads of tile row mt + 2 go out with the
       // MFMAs of row mt, so each read has two rows of MFMAs to land.
-      constexpr int kMfmaPerRow = NT * kMfmaPerBlock<OP> + (OP == OP_BF16 ? 4 : 0);
+      constexpr int kMfmaPerRow = NT * kMfmaPerBlock<OP> + (OP == OP_BF16 ? 4 : 0) + (ZP ? 2 : 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 2 * AV, 0);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
@@ -898,22 +935,28 @@ __global__ __launch_bounds__(256, 2) void w4_gemm_tiled(GemmArgs p, int splitk) 
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const uint32_t idx = (uint32_t)(n_d + i) * p.G + kb;
-          zc[i] = (OP == OP_BF16) ? 128.0f + (p.z ? word_to_f32(x.zd[nt][i], zdt, idx) : 8.0f) : 0.0f;
+          const float z = p.z ? word_to_f32(x.zd[nt][i], zdt, idx) : 8.0f;
+          zc[i] = (OP == OP_BF16) ? 128.0f + z : (ZP ? z - 8.0f : 0.0f);
         }
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
           const int64_t m = m_base + mt * 16 + r;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float pv = partial_value<OP>(acc[nt][mt], ones[mt], zc[i], i);
+            int32_t ia = 0;
+            if constexpr (ZP) ia = acc[nt][mt][i] - (int32_t)zc[i] * onesi[mt][i];
+            const float pv = ZP ? (float)ia * 0.0625f : partial_value<OP>(acc[nt][mt], ones[mt], zc[i], i);
             if (m < p.M && n_d < p.N && in_window(p, m, n_d + i))
-              store_partial<OP>(p, kb, m, n_d + i, pv, int_partial<OP>(acc[nt][mt], i));
+              store_partial<OP>(p, kb, m, n_d + i, pv, ZP ? ia >> 4 : int_partial<OP>(acc[nt][mt], i));
           }
           acc[nt][mt] = Acc{};
         }
       }
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) ones[mt] = f32x4{};
+      for (int mt = 0; mt < MT; ++mt) {
+        ones[mt] = f32x4{};
+        onesi[mt] = i32x4{};
+      }
     }
   };
 
@@ -974,6 +1017,10 @@ __global__ __launch_bounds__(256, 2) void w4_gemm_tiled(GemmArgs p, int splitk) 
 #pragma unroll
       for (int i = 0; i < 4; ++i) zc[i] = 128.0f + zero_point(p, n_d + i, 0);
     }
+    if constexpr (ZP && !GROUPED) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) zc[i] = zero_point(p, n_d + i, 0) - 8.0f;
+    }
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       const int64_t m = m_base + mt * 16 + r;
@@ -983,6 +1030,8 @@ __global__ __launch_bounds__(256, 2) void w4_gemm_tiled(GemmArgs p, int splitk) 
       for (int i = 0; i < 4; ++i) {
         if constexpr (GROUPED)
           bits[i] = __float_as_uint(tot[nt][mt][i]);
+        else if constexpr (ZP)
+          bits[i] = (uint32_t)(acc[nt][mt][i] - (int32_t)zc[i] * onesi[mt][i]);
         else if constexpr (OP == OP_I8)
           bits[i] = (uint32_t)acc[nt][mt][i];
         else
@@ -1074,12 +1123,13 @@ __global__ __launch_bounds__(256) void w4_splitk_reduce(GemmArgs p, int splitk) 
 // ===========================================================================
 // Host-side launchers.
 // ===========================================================================
-void tiled_tile(int op, bool grouped, int tall, int* bm, int* bn) {
+void tiled_tile(int op, bool grouped, int tall, int* bm, int* bn, bool zp) {
   // 8-bit operands: 64 x 256, or the tall tile, 128 x 256 for int8 per
-  // channel and 128 x 128 otherwise (2 n-blocks per wave: grouped and fp8
-  // waves spend more VALU per weight block, which 8 tile rows amortise)
+  // channel and 128 x 128 otherwise (2 n-blocks per wave: grouped, fp8 and
+  // zero-point waves spend more VALU (or registers) per weight block, which 8
+  // tile rows amortise)
   if (op == OP_I8 || op == OP_FP8) {
-    const bool wide = op == OP_I8 && !grouped;
+    const bool wide = op == OP_I8 && !grouped && !zp;
     *bm = tall ? 128 : 64;
     *bn = (tall && !wide) ? 128 : 256;
   } else {
@@ -1088,7 +1138,7 @@ void tiled_tile(int op, bool grouped, int tall, int* bm, int* bn) {
   }
 }
 
-template <int OP, bool GROUPED, bool FLIP>
+template <int OP, bool GROUPED, bool FLIP, bool ZP = false>
 static hipError_t launch_typed(const GemmArgs& args, const GemmPlan& plan, hipStream_t stream) {
   if (plan.path == PATH_SKINNY) {
     // S waves split K; at least 4 NS waves are launched so that every output
@@ -1098,17 +1148,17 @@ static hipError_t launch_typed(const GemmArgs& args, const GemmPlan& plan, hipSt
     const unsigned threads = 64u * (unsigned)(S > 4 * ns ? S : 4 * ns);
     const dim3 grid((unsigned)(args.N / plan.bn));
     const bool part = args.mode == MODE_PARTIALS;
-    const size_t tab = (size_t)skinny_table_bytes(OP, GROUPED, args.G, ns);   // checked by the plan
+    const size_t tab = (size_t)skinny_table_bytes(OP, GROUPED, args.G, ns, ZP);   // checked by the plan
     if (ns == 2) {
       if (part)
-        hipLaunchKernelGGL((w4_gemm_skinny<OP, GROUPED, FLIP, 2, true>), grid, dim3(threads), tab, stream, args, S);
+        hipLaunchKernelGGL((w4_gemm_skinny<OP, GROUPED, FLIP, 2, true, ZP>), grid, dim3(threads), tab, stream, args, S);
       else
-        hipLaunchKernelGGL((w4_gemm_skinny<OP, GROUPED, FLIP, 2, false>), grid, dim3(threads), tab, stream, args, S);
+        hipLaunchKernelGGL((w4_gemm_skinny<OP, GROUPED, FLIP, 2, false, ZP>), grid, dim3(threads), tab, stream, args, S);
     } else {
       if (part)
-        hipLaunchKernelGGL((w4_gemm_skinny<OP, GROUPED, FLIP, 1, true>), grid, dim3(threads), tab, stream, args, S);
+        hipLaunchKernelGGL((w4_gemm_skinny<OP, GROUPED, FLIP, 1, true, ZP>), grid, dim3(threads), tab, stream, args, S);
       else
-        hipLaunchKernelGGL((w4_gemm_skinny<OP, GROUPED, FLIP, 1, false>), grid, dim3(threads), tab, stream, args, S);
+        hipLaunchKernelGGL((w4_gemm_skinny<OP, GROUPED, FLIP, 1, false, ZP>), grid, dim3(threads), tab, stream, args, S);
     }
     return hipGetLastError();
   }
@@ -1133,24 +1183,28 @@ static hipError_t launch_typed(const GemmArgs& args, const GemmPlan& plan, hipSt
     const bool part = args.mode == MODE_PARTIALS;
     if (plan.splitk > 1) {
       if (part)
-        hipLaunchKernelGGL((w4_gemm_tiled<OP, GROUPED, FLIP, NT, MT, true, true>), grid, dim3(256), 0, stream,
+        hipLaunchKernelGGL((w4_gemm_tiled<OP, GROUPED, FLIP, NT, MT, true, true, ZP>), grid, dim3(256), 0, stream,
                            args, plan.splitk);
       else
-        hipLaunchKernelGGL((w4_gemm_tiled<OP, GROUPED, FLIP, NT, MT, true, false>), grid, dim3(256), 0, stream,
+        hipLaunchKernelGGL((w4_gemm_tiled<OP, GROUPED, FLIP, NT, MT, true, false, ZP>), grid, dim3(256), 0, stream,
                            args, plan.splitk);
     } else {
       if (part)
-        hipLaunchKernelGGL((w4_gemm_tiled<OP, GROUPED, FLIP, NT, MT, false, true>), grid, dim3(256), 0, stream,
+        hipLaunchKernelGGL((w4_gemm_tiled<OP, GROUPED, FLIP, NT, MT, false, true, ZP>), grid, dim3(256), 0, stream,
                            args, 1);
       else
-        hipLaunchKernelGGL((w4_gemm_tiled<OP, GROUPED, FLIP, NT, MT, false, false>), grid, dim3(256), 0, stream,
+        hipLaunchKernelGGL((w4_gemm_tiled<OP, GROUPED, FLIP, NT, MT, false, false, ZP>), grid, dim3(256), 0, stream,
                            args, 1);
     }
   };
   if constexpr (kByte) {
-    if (plan.bm == 128 && plan.bn == 256)
-      launch(std::integral_constant<int, 8>{}, std::integral_constant<int, 4>{});
-    else if (plan.bm == 128)
+    if (plan.bm == 128 && plan.bn == 256) {
+      // the 128 x 256 tile exists for symmetric int8 per channel only
+      if constexpr (OP == OP_I8 && !GROUPED && !ZP)
+        launch(std::integral_constant<int, 8>{}, std::integral_constant<int, 4>{});
+      else
+        return hipErrorInvalidValue;
+    } else if (plan.bm == 128)
       launch(std::integral_constant<int, 8>{}, std::integral_constant<int, 2>{});
     else
       launch(std::integral_constant<int, 4>{}, std::integral_constant<int, 4>{});
@@ -1160,8 +1214,13 @@ static hipError_t launch_typed(const GemmArgs& args, const GemmPlan& plan, hipSt
   return finish();
 }
 
-hipError_t launch_gemm(const GemmArgs& args, int op, bool grouped, bool flip, const GemmPlan& plan,
+hipError_t launch_gemm(const GemmArgs& args, int op, bool grouped, bool flip, bool zp, const GemmPlan& plan,
                        hipStream_t stream) {
+  if (zp) {   // asymmetric int8 W4A8 (the API admits no other combination)
+    if (op != OP_I8 || !flip) return hipErrorInvalidValue;
+    return grouped ? launch_typed<OP_I8, true, true, true>(args, plan, stream)
+                   : launch_typed<OP_I8, false, true, true>(args, plan, stream);
+  }
 #define W4_DISPATCH(OPV)                                                          \
   if (grouped)                                                                    \
     return flip ? launch_typed<OPV, true, true>(args, plan, stream)               \

@@ -18,7 +18,7 @@ struct GemmArgs {
   const float* a_scales;   // [M] per-token scales (W4A8) or nullptr (W4A16)
   const uint32_t* b;       // PB-v1 words
   const void* s;           // weight scales: [N] (per channel) or [N][G]
-  const void* z;           // W4A16 zero-points [N][G] or nullptr (z = 8)
+  const void* z;           // zero-points [N][G] (W4A16, asymmetric W4A8) or nullptr (z = 8)
   const void* bias;        // [N] in out dtype, or nullptr
   void* out;               // [M][N]
   void* ws;                // split-K slots [splitk][M][N] of 4-byte values
@@ -27,6 +27,7 @@ struct GemmArgs {
   int G;                   // K / group_size
   int s_dtype;             // W4_F32 / W4_F16 / W4_BF16
   int out_dtype;           // W4_F16 / W4_BF16
+  int z_dtype;             // zero-point storage: W4_F16 / W4_BF16 / W4_F32
   int mode;                // Mode
   int64_t m0, m1, n0, n1;  // partials window
 };
@@ -42,11 +43,12 @@ constexpr int skinny_max_waves(int op, bool grouped) {
 // LDS tables of the small-M kernel (grouped problems only): group scales,
 // and for W4A16 the zero-point terms, each [strips][groups][16] fp32
 // followed by a 16-float pad.
-constexpr int skinny_tables(int op, bool grouped) {
-  return grouped ? ((op == OP_BF16 || op == OP_F16) ? 2 : 1) : 0;
+// (asymmetric int8 W4A8 also keeps a zero-point table).
+constexpr int skinny_tables(int op, bool grouped, bool zp = false) {
+  return grouped ? ((op == OP_BF16 || op == OP_F16 || zp) ? 2 : 1) : 0;
 }
-inline int64_t skinny_table_bytes(int op, bool grouped, int64_t groups, int strips) {
-  return (int64_t)skinny_tables(op, grouped) * (strips * groups * 16 + 16) * 4;
+inline int64_t skinny_table_bytes(int op, bool grouped, int64_t groups, int strips, bool zp = false) {
+  return (int64_t)skinny_tables(op, grouped, zp) * (strips * groups * 16 + 16) * 4;
 }
 // Largest table the small-M kernel stages; larger problems use the tiled kernel.
 constexpr int64_t kSkinnyTableMax = 48 * 1024;
@@ -58,7 +60,7 @@ struct GemmPlan {
 };
 
 // Block tile of the tiled kernel for an operand class / grouping.
-void tiled_tile(int op, bool grouped, int tall, int* bm, int* bn);
+void tiled_tile(int op, bool grouped, int tall, int* bm, int* bn, bool zp = false);
 
 hipError_t launch_prepack(const void* w_in, void* w_packed, int64_t N, int64_t K, int operand, bool exllama,
                           hipStream_t stream);
@@ -68,7 +70,8 @@ hipError_t launch_quant_per_tensor(const void* x, int x_dtype, void* xq, int q_d
                                    int64_t K, hipStream_t stream);
 hipError_t launch_rmsnorm_quant(const void* x, int x_dtype, const void* gamma, float eps, void* xq, int q_dtype,
                                 float* scales, int64_t M, int64_t K, int exact_sum, hipStream_t stream);
-hipError_t launch_gemm(const GemmArgs& args, int op, bool grouped, bool flip, const GemmPlan& plan,
+// zp: asymmetric int8 W4A8 (op OP_I8, flip set: raw uint4 codes, zero-points in args.z).
+hipError_t launch_gemm(const GemmArgs& args, int op, bool grouped, bool flip, bool zp, const GemmPlan& plan,
                        hipStream_t stream);
 
 }  // namespace w4

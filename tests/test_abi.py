@@ -157,6 +157,25 @@ def test_w4a16_validation(lib):
     assert call(M=0) == W4_OK
 
 
+def test_w4a8_zp_validation(lib):
+    f = lib.w4a8_gemm_zp
+
+    def call(aq=FAKE, sa=FAKE, b=FAKE, bs=FAKE, s_dtype=1, z=FAKE, z_dtype=0, gs=128, out=FAKE, out_dtype=0,
+             M=4, N=32, K=256):
+        return f(aq, sa, b, bs, s_dtype, z, z_dtype, gs, None, out, out_dtype, M, N, K, None, 0, None)
+    assert call(z=None) == E_NULL
+    assert call(sa=None) == E_NULL
+    assert call(z_dtype=3) == E_DTYPE
+    assert call(s_dtype=4) == E_DTYPE
+    assert call(out_dtype=2) == E_DTYPE
+    assert call(gs=64) == E_GROUP
+    assert call(N=40) == E_SHAPE
+    assert call(gs=-1, K=65536 + 128) == E_SHAPE           # per-channel int32 range
+    assert call(z=ctypes.c_void_p(0x10001)) == E_ALIGN
+    assert call(z=ctypes.c_void_p(0x10002), z_dtype=2) == E_ALIGN
+    assert call(M=0) == W4_OK
+
+
 def test_partials_window_validation(lib):
     f = lib.w4a8_gemm_partials
     assert f(FAKE, 3, FAKE, 0, 128, 4, 32, 256, 0, 5, 0, 32, FAKE, None, 0, None) == E_SHAPE
