@@ -439,6 +439,29 @@ def main(argv=None) -> int:
         row["hbm_frac"] = round(row["rmsnorm_quant_GBps"] / HBM_PEAK_GBPS, 4)
         norm_quant.append(row)
 
+    # ---- asymmetric W4A8 (zero-points; the same codes read as raw uint4)
+    # next to the symmetric GEMM, REPS launches back to back per M
+    zeros = torch.randint(0, 16, (N,), generator=torch.Generator().manual_seed(7)).to(torch.float16).to(dev)
+    zp_rows = []
+    for i, M in enumerate(Ms):
+        if M not in (min(Ms), 16, 256, max(Ms)):
+            continue
+        row = {"M": M}
+        for name, fn in (("symmetric_us", lambda r: w4.w4a8_gemm(aq[M], sa[M], packed[r % copies], scales, -1,
+                                                                 torch.float16, out=out[M], workspace=ws)),
+                         ("zero_point_us", lambda r: w4.w4a8_gemm_zp(aq[M], sa[M], packed[r % copies], scales,
+                                                                     zeros, -1, torch.float16, out=out[M],
+                                                                     workspace=ws))):
+            fn(i)
+            e0, e1 = mk(), mk()
+            e0.record()
+            for r in range(REPS):
+                fn(i + r)
+            e1.record()
+            torch.cuda.synchronize()
+            row[name] = round(e0.elapsed_time(e1) * 1e3 / REPS, 2)
+        zp_rows.append(row)
+
     # ---- per-M figures ----------------------------------------------------
     per_m = []
     total_ops = 0.0
@@ -499,6 +522,7 @@ def main(argv=None) -> int:
         "roofline": roofline,
         "roofline_small_m": roofline_small,
         "rmsnorm_quant": norm_quant,
+        "w4a8_zero_point": zp_rows,
         "prepack": {"median_us": round(prepack_us[len(prepack_us) // 2], 2),
                     "GBps_read_plus_write": round(N * K / (prepack_us[len(prepack_us) // 2] * 1e-6) / 1e9, 1)},
         "prepack_from_exllama": {"median_us": round(import_us[len(import_us) // 2], 2),
