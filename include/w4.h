@@ -54,7 +54,7 @@ typedef enum w4_status {
   W4_E_SHAPE = 2,       /* a size is negative or violates N%16, K%128, ...   */
   W4_E_DTYPE = 3,       /* unsupported dtype / wtype / operand combination   */
   W4_E_ALIGN = 4,       /* a device pointer is not 16-byte aligned           */
-  W4_E_GROUP = 5,       /* group_size not in {K, -1, 128} or does not divide K */
+  W4_E_GROUP = 5,       /* group_size not in {K, -1, 128} (W4A16 also 64, 32) or does not divide K */
   W4_E_WORKSPACE = 6,   /* workspace missing or smaller than required        */
   W4_E_UNSUPPORTED = 7, /* valid request outside what this version implements */
   W4_E_HIP = 8          /* the HIP runtime returned an error                 */
@@ -284,7 +284,10 @@ W4_API int w4a8_gemm_zp(const void* aq, const float* a_scales, const void* b_pac
  * scales    : device, [N][K/group_size] of a_dtype.
  * zeros     : device, [N][K/group_size] of a_dtype, integer values 0..15, or
  *             NULL for z = 8.
- * group_size: K, -1 (= K) or 128.
+ * group_size: K, -1 (= K), 128, 64 or 32.  Groups smaller than the kernels'
+ *             128-deep K block follow the W4A16 API page's kernel, which
+ *             narrows its K tile to the group size: each block then holds 2
+ *             or 4 groups, each with its own scale and zero-point.
  * bias      : device, [N] of a_dtype, or NULL.
  * out       : device, [M][N] of a_dtype.
  * workspace : as for w4a8_gemm.

@@ -119,10 +119,12 @@ int check_shape(int64_t M, int64_t N, int64_t K) {
   return W4_OK;
 }
 
-int check_group(int64_t group_size, int64_t K) {
+// W4A16 (small_ok) also takes groups of 64 and 32.
+int check_group(int64_t group_size, int64_t K, bool small_ok = false) {
   const int64_t g = resolve_group(group_size, K);
-  if (g != K && g != 128)
-    return fail(W4_E_GROUP, "group_size=%lld: supported values are K, -1 and 128", (long long)group_size);
+  if (g != K && g != 128 && !(small_ok && (g == 64 || g == 32)))
+    return fail(W4_E_GROUP, "group_size=%lld: supported values are K, -1 and 128%s", (long long)group_size,
+                small_ok ? ", 64, 32" : "");
   if (K % g) return fail(W4_E_GROUP, "group_size=%lld does not divide K=%lld", (long long)g, (long long)K);
   return W4_OK;
 }
@@ -134,7 +136,7 @@ int check_group(int64_t group_size, int64_t K) {
 // choice (and must fit the problem).  zp: asymmetric int8, whose small-M
 // kernel keeps a second (zero-point) table.
 int plan_with(int64_t M, int64_t N, int64_t K, bool grouped, int op, const Sched& forced, GemmPlan* plan,
-              bool zp = false) {
+              bool zp = false, int sg = 1) {
   const int64_t fp = forced.path, fs = forced.splitk;
   const int64_t KB = K / 128;
   const int cu = cu_count();
@@ -146,7 +148,7 @@ int plan_with(int64_t M, int64_t N, int64_t K, bool grouped, int op, const Sched
   const int64_t fns = forced.strips;
   const bool two = N % 32 == 0 && (!grouped || (M >= 8 && N >= 8192));
   int64_t ns = fns ? fns : (two ? 2 : 1);
-  const int64_t groups = grouped ? KB : 1;
+  const int64_t groups = grouped ? KB * sg : 1;   // sg groups per 128-deep block
   bool one_split = false;
   if (plan->path == PATH_SKINNY && skinny_table_bytes(op, grouped, groups, (int)ns, zp) > kSkinnyTableMax) {
     // the scale / zero-point tables would not fit the small-M kernel's LDS
@@ -257,15 +259,23 @@ bool lookup_schedule(int op, bool grouped, int64_t M, int64_t N, int64_t K, Sche
 // The options, when any is set, force their fields.  Otherwise a matching
 // schedule-table entry (run-time entries first, then the built-in ones) is
 // taken if it fits the problem, and the heuristic decides the rest.
-int make_plan(int64_t M, int64_t N, int64_t K, bool grouped, int op, GemmPlan* plan, bool zp = false) {
+int make_plan(int64_t M, int64_t N, int64_t K, bool grouped, int op, GemmPlan* plan, bool zp = false,
+              int sg = 1) {
   const Sched opts{g_force_path.load(), g_splitk.load(), g_tiled_bm.load(), g_skinny_strips.load()};
-  if (opts.any()) return plan_with(M, N, K, grouped, op, opts, plan, zp);
-  if (g_schedule_table.load()) {
+  if (opts.any()) return plan_with(M, N, K, grouped, op, opts, plan, zp, sg);
+  // the table's entries were measured with groups of 128
+  if (g_schedule_table.load() && sg == 1) {
     Sched t;
     if (lookup_schedule(op, grouped, M, N, K, &t) && plan_with(M, N, K, grouped, op, t, plan, zp) == W4_OK)
       return W4_OK;
   }
-  return plan_with(M, N, K, grouped, op, Sched{}, plan, zp);
+  return plan_with(M, N, K, grouped, op, Sched{}, plan, zp, sg);
+}
+
+// Groups per 128-deep block (1 for 128 and per channel, 2 or 4 for 64 or 32).
+int subgroups(int64_t group_size, int64_t K) {
+  const int64_t g = resolve_group(group_size, K);
+  return (g == 64 || g == 32) && g != K ? (int)(128 / g) : 1;
 }
 
 size_t workspace_for(const GemmPlan& plan, int64_t M, int64_t N) {
@@ -277,7 +287,8 @@ size_t workspace_for(const GemmPlan& plan, int64_t M, int64_t N) {
 int run_gemm(GemmArgs& args, int op, bool grouped, bool flip, void* workspace, size_t workspace_bytes,
              void* stream, bool zp = false) {
   GemmPlan plan;
-  if (int st = make_plan(args.M, args.N, args.K, grouped, op, &plan, zp)) return st;
+  const int sg = grouped ? (int)(128 * (int64_t)args.G / args.K) : 1;
+  if (int st = make_plan(args.M, args.N, args.K, grouped, op, &plan, zp, sg)) return st;
   const size_t need = workspace_for(plan, args.M, args.N);
   if (need) {
     if (!workspace || workspace_bytes < need)
@@ -400,10 +411,11 @@ int w4_rmsnorm_quant_per_token(const void* x, int x_dtype, const void* gamma, fl
 
 size_t w4_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t group_size, int a_dtype) {
   const int op = op_of(a_dtype);
-  if (op < 0 || check_shape(M, N, K) || check_group(group_size, K)) return 0;
+  const bool w4a16 = op == OP_F16 || op == OP_BF16;
+  if (op < 0 || check_shape(M, N, K) || check_group(group_size, K, w4a16)) return 0;
   GemmPlan plan;
   const bool grouped = resolve_group(group_size, K) != K;
-  if (make_plan(M, N, K, grouped, op, &plan)) return 0;
+  if (make_plan(M, N, K, grouped, op, &plan, false, subgroups(group_size, K))) return 0;
   return workspace_for(plan, M, N);
 }
 
@@ -412,9 +424,10 @@ int w4_gemm_plan(int64_t M, int64_t N, int64_t K, int64_t group_size, int a_dtyp
   const int op = op_of(a_dtype);
   if (op < 0) return fail(W4_E_DTYPE, "unknown a_dtype");
   if (int st = check_shape(M, N, K)) return st;
-  if (int st = check_group(group_size, K)) return st;
+  if (int st = check_group(group_size, K, op == OP_F16 || op == OP_BF16)) return st;
   GemmPlan plan;
-  if (int st = make_plan(M, N, K, resolve_group(group_size, K) != K, op, &plan)) return st;
+  if (int st = make_plan(M, N, K, resolve_group(group_size, K) != K, op, &plan, false, subgroups(group_size, K)))
+    return st;
   if (path) *path = plan.path;
   if (splitk) *splitk = plan.splitk;
   if (tile_m) *tile_m = plan.path == PATH_SKINNY ? 16 : plan.bm;
@@ -512,7 +525,7 @@ static int validate_w4a16(const void* a, int a_dtype, const void* b_packed, int 
     return fail(W4_E_DTYPE, "W4A16 weights are W4_UINT4 or W4_UINT4B8");
   if (wtype == W4_UINT4B8 && zeros) return fail(W4_E_DTYPE, "W4_UINT4B8 weights take no zero-points");
   if (int st = check_shape(M, N, K)) return st;
-  if (int st = check_group(group_size, K)) return st;
+  if (int st = check_group(group_size, K, true)) return st;
   if (!b_packed || (M > 0 && !a)) return fail(W4_E_NULL, "a and b_packed are required");
   if (!aligned(a, 16) || !aligned(b_packed, 16)) return fail(W4_E_ALIGN, "a and b_packed must be 16-byte aligned");
   if (!aligned(zeros, 2)) return fail(W4_E_ALIGN, "zeros must be 2-byte aligned");

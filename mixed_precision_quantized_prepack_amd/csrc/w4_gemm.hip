@@ -122,6 +122,29 @@ __device__ __forceinline__ void ones_mma_i8(const u32x4* a, i32x4& ones) {
   ones = mma_i8(sixteen, a[1], ones);
 }
 
+// Groups smaller than a 128-deep block (W4A16, group size 64 or 32: SG = 2 or
+// 4 sub-groups per block).  Lane group kq of an MFMA operand holds the k in
+// [32 kq, 32 kq + 32) of the block, so the lanes of sub-group sg are those
+// with kq / (4 / SG) == sg; an operand with the other lanes zeroed gives that
+// sub-group's dot product.
+template <int SG>
+__device__ __forceinline__ int lane_subgroup(int kq) { return kq / (4 / SG); }
+
+template <int N>
+__device__ __forceinline__ void mask_words(const uint32_t* e, bool keep, uint32_t* out) {
+#pragma unroll
+  for (int t = 0; t < N; ++t) out[t] = keep ? e[t] : 0u;
+}
+
+// bf16 ones-operand restricted to the lanes that keep it: the activation sum
+// of one sub-group.
+__device__ __forceinline__ void ones_mma_masked(const u32x4* a, bool keep, f32x4& ones) {
+  const uint32_t v = keep ? 0x3F803F80u : 0u;
+  const u32x4 one{v, v, v, v};
+#pragma unroll
+  for (int kw = 0; kw < 4; ++kw) ones = mma_bf16(one, a[kw], ones);
+}
+
 // The group (or whole-K) dot product of one D element.
 template <int OP>
 __device__ __forceinline__ float partial_value(typename OpTraits<OP>::Acc acc, f32x4 ones, float zc,
@@ -255,7 +278,7 @@ constexpr int waitcnt_vm_lgkm0(int vm) { return (vm & 15) | ((vm >> 4) << 14) | 
 // its D rows for a K block with one 16-byte LDS read, instead of a 64-lane
 // gather from memory per block (which costs the address pipeline as much as
 // the block's weights).  The table's size is set at launch.
-template <int OP, bool GROUPED, bool FLIP, int NS, bool PARTIALS, bool ZP>
+template <int OP, bool GROUPED, bool FLIP, int NS, bool PARTIALS, bool ZP, int SG>
 __global__ __launch_bounds__(64 * skinny_max_waves(OP, GROUPED)) void w4_gemm_skinny(GemmArgs p, int S) {
   using Acc = typename OpTraits<OP>::Acc;
   constexpr int EB = OpTraits<OP>::kElemBytes;
@@ -272,6 +295,7 @@ __global__ __launch_bounds__(64 * skinny_max_waves(OP, GROUPED)) void w4_gemm_sk
   constexpr bool partials = PARTIALS;  // verification mode: store group partials
   const int zdt = p.z_dtype;                      // zero-point storage dtype
   static_assert(!ZP || (OP == OP_I8 && FLIP), "zero-points: int8 operand from raw uint4 codes");
+  static_assert(SG == 1 || (GROUPED && (OP == OP_F16 || OP == OP_BF16)), "sub-groups: grouped W4A16 only");
 
   const __amdgpu_buffer_rsrc_t rw =
       make_rsrc(reinterpret_cast<const uint8_t*>(p.b) + nb0 * KB * 1024, (int64_t)NS * KB * 1024);
@@ -365,6 +389,54 @@ __global__ __launch_bounds__(64 * skinny_max_waves(OP, GROUPED)) void w4_gemm_sk
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int k = wave + (kb + u) * S;
+      if constexpr (SG > 1) {
+        // groups of 64 or 32: each sub-group's dot products come from MFMAs
+        // on the weight words of its lanes only, and are folded at once
+        const int sgl = lane_subgroup<SG>(kq);
+        f32x4 os[SG];
+#pragma unroll
+        for (int sg = 0; sg < SG; ++sg) {
+          os[sg] = f32x4{};
+          if constexpr (OP == OP_BF16) ones_mma_masked(av[buf][u], sgl == sg, os[sg]);
+        }
+#pragma unroll
+        for (int j = 0; j < NS; ++j) {
+          f16x2 nz = {};
+          if constexpr (OP == OP_F16) {
+            // the zero-point of the group this lane's weights belong to
+            const float z = k < KB ? tz[(j * p.G + k * SG + sgl) * 16 + r] : 8.0f;
+            const _Float16 h = (_Float16)(-(1024.0f + z));
+            nz = f16x2{h, h};
+          }
+          uint32_t e[16];
+          expand_weights<OP, FLIP>(wv[buf][u][j], nz, e);
+          const int64_t n_d = (nb0 + j) * 16 + 4 * kq;
+#pragma unroll
+          for (int sg = 0; sg < SG; ++sg) {
+            uint32_t es[16];
+            mask_words<16>(e, sgl == sg, es);
+            Acc t = Acc{};
+            block_mma<OP>(es, av[buf][u], t);
+            if (k < KB) {
+              const int g = k * SG + sg;
+              const int slot = (j * p.G + g) * 16 + 4 * kq;
+              const f32x4 sv = *reinterpret_cast<const f32x4*>(&tsc[slot]);
+              f32x4 zc = {};
+              if constexpr (OP == OP_BF16) zc = *reinterpret_cast<const f32x4*>(&tz[slot]);
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const float pv = partial_value<OP>(t, os[sg], zc[i], i);
+                if (partials) {
+                  if (in_window(p, r, n_d + i)) store_partial<OP>(p, g, r, n_d + i, pv, 0);
+                } else {
+                  tot[j][i] = fmaf(pv, sv[i], tot[j][i]);
+                }
+              }
+            }
+          }
+        }
+        continue;
+      }
       const int g = GROUPED ? k : 0;
       if constexpr (OP == OP_BF16) ones_mma(av[buf][u], ones);
       if constexpr (ZP) ones_mma_i8(av[buf][u], ones_i);
@@ -654,7 +726,7 @@ __device__ __forceinline__ void stage_barrier() {
   asm volatile("" ::: "memory");
 }
 
-template <int OP, bool GROUPED, bool FLIP, int NT, int MT, bool SPLIT, bool PARTIALS, bool ZP>
+template <int OP, bool GROUPED, bool FLIP, int NT, int MT, bool SPLIT, bool PARTIALS, bool ZP, int SG>
 __global__ __launch_bounds__(256, 2) void w4_gemm_tiled(GemmArgs p, int splitk) {
   using Acc = typename OpTraits<OP>::Acc;
   constexpr int EB = OpTraits<OP>::kElemBytes;
@@ -676,9 +748,10 @@ __global__ __launch_bounds__(256, 2) void w4_gemm_tiled(GemmArgs p, int splitk) 
   constexpr int BNW = 4 * NT * 16;   // columns of the workgroup
   constexpr int kTables = kFold ? ((OP == OP_BF16 || ZP) ? 2 : 1) : 0;
   static_assert(!ZP || (OP == OP_I8 && FLIP), "zero-points: int8 operand from raw uint4 codes");
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[3 * STAGE + kTables * 2 * BNW * 4];
-  float* const gsc = reinterpret_cast<float*>(lds + 3 * STAGE);   // [2][BNW]
-  float* const gzc = gsc + 2 * BNW;                               // [2][BNW]
+  static_assert(SG == 1 || (GROUPED && (OP == OP_F16 || OP == OP_BF16)), "sub-groups: grouped W4A16 only");
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[3 * STAGE + kTables * 2 * SG * BNW * 4];
+  float* const gsc = reinterpret_cast<float*>(lds + 3 * STAGE);   // [2][SG][BNW]
+  float* const gzc = gsc + 2 * SG * BNW;                          // [2][SG][BNW]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -754,7 +827,8 @@ __global__ __launch_bounds__(256, 2) void w4_gemm_tiled(GemmArgs p, int splitk) 
           }
         }
         if constexpr (OP == OP_F16)
-          x.wz[nt] = load_word(rz, zdt, (uint32_t)(((nb_base + nt) * 16 + r) * p.G + kb), kb < kb1 && p.z);
+          x.wz[nt] = load_word(rz, zdt, (uint32_t)(((nb_base + nt) * 16 + r) * p.G + kb * SG + lane_subgroup<SG>(kq)),
+                               kb < kb1 && p.z);
       }
     }
   };
@@ -798,23 +872,34 @@ __global__ __launch_bounds__(256, 2) void w4_gemm_tiled(GemmArgs p, int splitk) 
   // LDS read per n-block.  int8 scales carry the 1/16 of the 16 w operand.
   const int col = tid % BNW;
   const uint32_t col_n = (uint32_t)((int64_t)by * BNW + col);
-  uint32_t col_sw = 0, col_zw = 0;   // raw words of the column for the step being prefetched
+  // raw words of the column for the step being prefetched (SG groups per step)
+  uint32_t col_sw[SG], col_zw[SG];
+#pragma unroll
+  for (int sg = 0; sg < SG; ++sg) col_sw[sg] = col_zw[sg] = 0;
   auto load_col = [&](int kb) {
     if constexpr (kFold) {
-      const uint32_t idx = col_n * (uint32_t)p.G + (uint32_t)kb;
-      col_sw = load_word(rs, p.s_dtype, idx, kb < kb1 && col_n < (uint32_t)p.N);
-      if constexpr (OP == OP_BF16 || ZP) col_zw = load_word(rz, zdt, idx, kb < kb1 && p.z && col_n < (uint32_t)p.N);
+#pragma unroll
+      for (int sg = 0; sg < SG; ++sg) {
+        const uint32_t idx = col_n * (uint32_t)p.G + (uint32_t)(kb * SG + sg);
+        col_sw[sg] = load_word(rs, p.s_dtype, idx, kb < kb1 && col_n < (uint32_t)p.N);
+        if constexpr (OP == OP_BF16 || ZP)
+          col_zw[sg] = load_word(rz, zdt, idx, kb < kb1 && p.z && col_n < (uint32_t)p.N);
+      }
     }
   };
   auto store_col = [&](int kb) {
     if constexpr (kFold) {
-      const uint32_t idx = col_n * (uint32_t)p.G + (uint32_t)kb;
       const int slot = (kb - kb0) & 1;
-      float sv = word_to_f32(col_sw, p.s_dtype, idx);
-      if constexpr (OP == OP_I8) sv *= 0.0625f;
-      gsc[slot * BNW + col] = sv;
-      if constexpr (OP == OP_BF16) gzc[slot * BNW + col] = 128.0f + (p.z ? word_to_f32(col_zw, zdt, idx) : 8.0f);
-      if constexpr (ZP) gzc[slot * BNW + col] = (p.z ? word_to_f32(col_zw, zdt, idx) : 8.0f) - 8.0f;
+#pragma unroll
+      for (int sg = 0; sg < SG; ++sg) {
+        const uint32_t idx = col_n * (uint32_t)p.G + (uint32_t)(kb * SG + sg);
+        const int at = (slot * SG + sg) * BNW + col;
+        float sv = word_to_f32(col_sw[sg], p.s_dtype, idx);
+        if constexpr (OP == OP_I8) sv *= 0.0625f;
+        gsc[at] = sv;
+        if constexpr (OP == OP_BF16) gzc[at] = 128.0f + (p.z ? word_to_f32(col_zw[sg], zdt, idx) : 8.0f);
+        if constexpr (ZP) gzc[at] = (p.z ? word_to_f32(col_zw[sg], zdt, idx) : 8.0f) - 8.0f;
+      }
     }
   };
 
@@ -832,7 +917,7 @@ __global__ __launch_bounds__(256, 2) void w4_gemm_tiled(GemmArgs p, int splitk) 
       f16x2 nz = {};
       if constexpr (OP == OP_F16) {
         if constexpr (GROUPED) {
-          const uint32_t zi = (uint32_t)(((nb_base + nt) * 16 + r) * p.G + kb);
+          const uint32_t zi = (uint32_t)(((nb_base + nt) * 16 + r) * p.G + kb * SG + lane_subgroup<SG>(kq));
           const _Float16 h = (_Float16)(-(1024.0f + (p.z ? word_to_f32(x.wz[nt], zdt, zi) : 8.0f)));
           nz = f16x2{h, h};
         } else {
@@ -855,7 +940,52 @@ __global__ __launch_bounds__(256, 2) void w4_gemm_tiled(GemmArgs p, int splitk) 
 #pragma unroll
       for (int j = 0; j < AV; ++j)
         af[mt][j] = *reinterpret_cast<const u32x4*>(src + mt * 16 * ROWB + frag_off[j]);
-    if constexpr (kFold) {
+    if constexpr (SG > 1) {
+      // groups of 64 or 32: per sub-group, MFMAs on the weight words of its
+      // lanes only, folded (or stored) at once
+      const int sgl = lane_subgroup<SG>(kq);
+      const int slot = (kb - kb0) & 1;
+      // sub-group outermost: only its masked weight words are live
+#pragma unroll
+      for (int sg = 0; sg < SG; ++sg) {
+        const int g = kb * SG + sg;
+        uint32_t es[NT][16];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          mask_words<16>(e[nt], sgl == sg, es[nt]);
+          pin_words<16>(es[nt]);
+        }
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          f32x4 os = {};
+          if constexpr (OP == OP_BF16) ones_mma_masked(af[mt], sgl == sg, os);
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) {
+            const int64_t n_d = (nb_base + nt) * 16 + 4 * kq;
+            Acc t = Acc{};
+            block_mma<OP>(es[nt], af[mt], t);
+            if constexpr (PARTIALS) {
+              const int64_t m = m_base + mt * 16 + r;
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                if (m < p.M && n_d < p.N && in_window(p, m, n_d + i)) {
+                  const float zc = (OP == OP_BF16) ? 128.0f + zero_point(p, n_d + i, g) : 0.0f;
+                  store_partial<OP>(p, g, m, n_d + i, partial_value<OP>(t, os, zc, i), 0);
+                }
+              }
+            } else {
+              const int at = (slot * SG + sg) * BNW + (wave * NT + nt) * 16 + 4 * kq;
+              const f32x4 sv = *reinterpret_cast<const f32x4*>(&gsc[at]);
+              f32x4 zc = {};
+              if constexpr (OP == OP_BF16) zc = *reinterpret_cast<const f32x4*>(&gzc[at]);
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                tot[nt][mt][i] = fmaf(partial_value<OP>(t, os, zc[i], i), sv[i], tot[nt][mt][i]);
+            }
+          }
+        }
+      }
+    } else if constexpr (kFold) {
       // This group's scales (and bf16 128 + z terms) for the lane's D rows.
       const int slot = (kb - kb0) & 1;
       f32x4 scv[NT], zcv[NT];
@@ -926,7 +1056,7 @@ __global__ __launch_bounds__(256, 2) void w4_gemm_tiled(GemmArgs p, int splitk) 
         if (mt + 2 < MT) __builtin_amdgcn_sched_group_barrier(0x100, AV, 0);
       }
     }
-    if constexpr (GROUPED && PARTIALS) {
+    if constexpr (GROUPED && PARTIALS && SG == 1) {
       // verification mode: store each group's dot products
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
@@ -1138,7 +1268,7 @@ void tiled_tile(int op, bool grouped, int tall, int* bm, int* bn, bool zp) {
   }
 }
 
-template <int OP, bool GROUPED, bool FLIP, bool ZP = false>
+template <int OP, bool GROUPED, bool FLIP, bool ZP = false, int SG = 1>
 static hipError_t launch_typed(const GemmArgs& args, const GemmPlan& plan, hipStream_t stream) {
   if (plan.path == PATH_SKINNY) {
     // S waves split K; at least 4 NS waves are launched so that every output
@@ -1151,14 +1281,14 @@ static hipError_t launch_typed(const GemmArgs& args, const GemmPlan& plan, hipSt
     const size_t tab = (size_t)skinny_table_bytes(OP, GROUPED, args.G, ns, ZP);   // checked by the plan
     if (ns == 2) {
       if (part)
-        hipLaunchKernelGGL((w4_gemm_skinny<OP, GROUPED, FLIP, 2, true, ZP>), grid, dim3(threads), tab, stream, args, S);
+        hipLaunchKernelGGL((w4_gemm_skinny<OP, GROUPED, FLIP, 2, true, ZP, SG>), grid, dim3(threads), tab, stream, args, S);
       else
-        hipLaunchKernelGGL((w4_gemm_skinny<OP, GROUPED, FLIP, 2, false, ZP>), grid, dim3(threads), tab, stream, args, S);
+        hipLaunchKernelGGL((w4_gemm_skinny<OP, GROUPED, FLIP, 2, false, ZP, SG>), grid, dim3(threads), tab, stream, args, S);
     } else {
       if (part)
-        hipLaunchKernelGGL((w4_gemm_skinny<OP, GROUPED, FLIP, 1, true, ZP>), grid, dim3(threads), tab, stream, args, S);
+        hipLaunchKernelGGL((w4_gemm_skinny<OP, GROUPED, FLIP, 1, true, ZP, SG>), grid, dim3(threads), tab, stream, args, S);
       else
-        hipLaunchKernelGGL((w4_gemm_skinny<OP, GROUPED, FLIP, 1, false, ZP>), grid, dim3(threads), tab, stream, args, S);
+        hipLaunchKernelGGL((w4_gemm_skinny<OP, GROUPED, FLIP, 1, false, ZP, SG>), grid, dim3(threads), tab, stream, args, S);
     }
     return hipGetLastError();
   }
@@ -1183,17 +1313,17 @@ static hipError_t launch_typed(const GemmArgs& args, const GemmPlan& plan, hipSt
     const bool part = args.mode == MODE_PARTIALS;
     if (plan.splitk > 1) {
       if (part)
-        hipLaunchKernelGGL((w4_gemm_tiled<OP, GROUPED, FLIP, NT, MT, true, true, ZP>), grid, dim3(256), 0, stream,
+        hipLaunchKernelGGL((w4_gemm_tiled<OP, GROUPED, FLIP, NT, MT, true, true, ZP, SG>), grid, dim3(256), 0, stream,
                            args, plan.splitk);
       else
-        hipLaunchKernelGGL((w4_gemm_tiled<OP, GROUPED, FLIP, NT, MT, true, false, ZP>), grid, dim3(256), 0, stream,
+        hipLaunchKernelGGL((w4_gemm_tiled<OP, GROUPED, FLIP, NT, MT, true, false, ZP, SG>), grid, dim3(256), 0, stream,
                            args, plan.splitk);
     } else {
       if (part)
-        hipLaunchKernelGGL((w4_gemm_tiled<OP, GROUPED, FLIP, NT, MT, false, true, ZP>), grid, dim3(256), 0, stream,
+        hipLaunchKernelGGL((w4_gemm_tiled<OP, GROUPED, FLIP, NT, MT, false, true, ZP, SG>), grid, dim3(256), 0, stream,
                            args, 1);
       else
-        hipLaunchKernelGGL((w4_gemm_tiled<OP, GROUPED, FLIP, NT, MT, false, false, ZP>), grid, dim3(256), 0, stream,
+        hipLaunchKernelGGL((w4_gemm_tiled<OP, GROUPED, FLIP, NT, MT, false, false, ZP, SG>), grid, dim3(256), 0, stream,
                            args, 1);
     }
   };
@@ -1231,11 +1361,20 @@ hipError_t launch_gemm(const GemmArgs& args, int op, bool grouped, bool flip, bo
     case OP_I8: W4_DISPATCH(OP_I8)
     case OP_FP8: W4_DISPATCH(OP_FP8)
     case OP_F16:
-      return grouped ? launch_typed<OP_F16, true, false>(args, plan, stream)
-                     : launch_typed<OP_F16, false, false>(args, plan, stream);
-    default:
-      return grouped ? launch_typed<OP_BF16, true, false>(args, plan, stream)
-                     : launch_typed<OP_BF16, false, false>(args, plan, stream);
+    default: {
+      // W4A16 groups of 128, 64 or 32: 1, 2 or 4 groups per 128-deep block
+      const int64_t sg = grouped ? 128 * (int64_t)args.G / args.K : 1;
+      if (op == OP_F16) {
+        if (!grouped) return launch_typed<OP_F16, false, false>(args, plan, stream);
+        return sg == 4 ? launch_typed<OP_F16, true, false, false, 4>(args, plan, stream)
+               : sg == 2 ? launch_typed<OP_F16, true, false, false, 2>(args, plan, stream)
+                         : launch_typed<OP_F16, true, false>(args, plan, stream);
+      }
+      if (!grouped) return launch_typed<OP_BF16, false, false>(args, plan, stream);
+      return sg == 4 ? launch_typed<OP_BF16, true, false, false, 4>(args, plan, stream)
+             : sg == 2 ? launch_typed<OP_BF16, true, false, false, 2>(args, plan, stream)
+                       : launch_typed<OP_BF16, true, false>(args, plan, stream);
+    }
   }
 #undef W4_DISPATCH
 }

@@ -142,6 +142,7 @@ def test_w4a8_validation(lib):
     assert _w4a8(lib, out=MISALIGNED) == E_ALIGN
     assert _w4a8(lib, K=131072 + 128, gs=-1) == E_SHAPE  # int32 range of per-channel int8
     assert _w4a8(lib, M=0) == W4_OK
+    assert _w4a8(lib, gs=32) == E_GROUP                 # groups of 64 / 32: W4A16 only
 
 
 def test_w4a16_validation(lib):
@@ -151,7 +152,9 @@ def test_w4a16_validation(lib):
     assert call(wtype=0) == E_DTYPE
     assert call(wtype=2) == E_DTYPE                      # uint4b8 takes no zero-points
     assert call(s=None) == E_NULL
-    assert call(gs=32) == E_GROUP
+    assert call(gs=48) == E_GROUP
+    assert call(gs=16) == E_GROUP
+    assert call(gs=64, K=320) == E_SHAPE                 # K % 128
     assert call(N=8) == E_SHAPE
     assert call(z=ctypes.c_void_p(0x10001)) == E_ALIGN
     assert call(M=0) == W4_OK
