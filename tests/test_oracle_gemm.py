@@ -190,6 +190,21 @@ def test_w4a16_outputs_match_exact_rationals(M, N, K, bias):
     assert np.array_equal(r["out"], want)
 
 
+@pytest.mark.parametrize("gs", [64, 32])
+def test_w4a16_small_groups_match_exact_rationals(gs):
+    """Groups of 64 and 32 (the W4A16 API page's kernel narrows its K tile to
+    the group size): scales and zero-points [N, K/gs], exact rationals."""
+    c = _case("w4a16_bf16_g128_4096x4096", 2, N=16, K=256, with_bias=True)
+    g = torch.Generator().manual_seed(gs)
+    G = 256 // gs
+    c.w_scales = (torch.rand((16, G), generator=g) * 0.015 + 0.005).to(torch.bfloat16)
+    c.zeros = torch.randint(0, 16, (16, G), generator=g).to(torch.bfloat16)
+    want, ex = _exact_w4a16(c, gs)
+    r = _oracle_w4a16(c, gs)
+    assert np.allclose(r["exact"], ex, rtol=1e-12, atol=1e-12)
+    assert np.array_equal(r["out"], want)
+
+
 # ---------------------------------------------------------------------------
 # Invariants.
 # ---------------------------------------------------------------------------
