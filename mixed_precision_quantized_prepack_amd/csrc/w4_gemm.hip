@@ -1338,6 +1338,10 @@ static hipError_t launch_typed(const GemmArgs& args, const GemmPlan& plan, hipSt
       launch(std::integral_constant<int, 8>{}, std::integral_constant<int, 2>{});
     else
       launch(std::integral_constant<int, 4>{}, std::integral_constant<int, 4>{});
+  } else if constexpr (SG == 4) {
+    // groups of 32: four sub-group passes per block; 32-row tiles keep the
+    // activation fragments and totals in registers
+    launch(std::integral_constant<int, 2>{}, std::integral_constant<int, 2>{});
   } else {
     launch(std::integral_constant<int, 4>{}, std::integral_constant<int, 2>{});
   }
