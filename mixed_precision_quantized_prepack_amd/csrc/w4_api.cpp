@@ -143,10 +143,12 @@ int plan_with(int64_t M, int64_t N, int64_t K, bool grouped, int op, const Sched
   plan->path = fp ? (int)fp : (M <= 16 ? PATH_SKINNY : PATH_TILED);
   tiled_tile(op, grouped, 0, &plan->bm, &plan->bn, zp);
   // strips of 16 columns per wave of the small-M kernel: two strips share
-  // one activation fragment.  Grouped problems take two only when the
-  // fragment is worth sharing (M >= 8) and N leaves enough workgroups.
+  // one activation fragment.  Grouped problems take two when N leaves enough
+  // workgroups and either the fragment is worth sharing (M >= 8) or the
+  // strips are long (K >= 8192) or many (N >= 16384): a wave then keeps
+  // twice the weight bytes in flight.
   const int64_t fns = forced.strips;
-  const bool two = N % 32 == 0 && (!grouped || (M >= 8 && N >= 8192));
+  const bool two = N % 32 == 0 && (!grouped || N >= 16384 || (N >= 8192 && (M >= 8 || KB >= 64)));
   int64_t ns = fns ? fns : (two ? 2 : 1);
   const int64_t groups = grouped ? KB * sg : 1;   // sg groups per 128-deep block
   bool one_split = false;

@@ -205,8 +205,12 @@ def test_plan_choices(lib, heuristic_only):
     assert plans[1][3] == 32                                     # two 16-column strips per wave
     assert [plans[M][1] for M in (64, 128, 256, 512, 1024)] == [8, 4, 4, 2, 1]
     assert plans[4096][1:] == (1, 128, 256)                      # one 128 x 256 tile per workgroup
-    # grouped small M: one strip below M = 8, two from there when N >= 8192
-    assert w4.gemm_plan(1, 22016, 4096, 128, w4.I8)[3] == 16
+    # grouped small M: two strips from M = 8 when N >= 8192, at any M when
+    # N >= 16384 or (N >= 8192 and K >= 8192), else one
+    assert w4.gemm_plan(1, 12288, 4096, 128, w4.I8)[3] == 16
+    assert w4.gemm_plan(8, 12288, 4096, 128, w4.I8)[3] == 32
+    assert w4.gemm_plan(1, 22016, 4096, 128, w4.I8)[3] == 32
+    assert w4.gemm_plan(1, 8192, 8192, 128, w4.BF16)[:2] == (1, 8) and w4.gemm_plan(1, 8192, 8192, 128, w4.BF16)[3] == 32
     assert w4.gemm_plan(16, 22016, 4096, 128, w4.I8)[3] == 32
     assert w4.gemm_plan(16, 4096, 11008, 128, w4.I8)[3] == 16
     # grouped int8 K splits: the most that keep one workgroup per CU (at least 4 K blocks each)
