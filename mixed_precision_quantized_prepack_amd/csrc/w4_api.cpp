@@ -175,13 +175,14 @@ int plan_with(int64_t M, int64_t N, int64_t K, bool grouped, int op, const Sched
     if (fs) {
       s = fs;
     } else {
-      // ~16 resident waves per CU, each with at least 8 K blocks (shorter
-      // waves spend most of their time waiting for their first loads)
+      // ~16 resident waves per CU, each with at least 8 weight blocks (K
+      // blocks times strips; shorter waves spend most of their time waiting
+      // for their first loads)
       const int64_t groups = N / (16 * ns);
       const int64_t want = (16 * cu + groups - 1) / groups;
       s = 1;
       while (s < want && s < 8) s *= 2;
-      while (s > 1 && KB / s < 8) s /= 2;
+      while (s > 1 && KB * ns / s < 8) s /= 2;
     }
     const int smax = skinny_max_waves(op, grouped);
     if (s < 1 || s > smax || s > KB)

@@ -209,6 +209,7 @@ def test_plan_choices(lib, heuristic_only):
     # N >= 16384 or (N >= 8192 and K >= 8192), else one
     assert w4.gemm_plan(1, 12288, 4096, 128, w4.I8)[3] == 16
     assert w4.gemm_plan(8, 12288, 4096, 128, w4.I8)[3] == 32
+    assert w4.gemm_plan(1, 22016, 4096, 128, w4.I8)[:2] == (1, 8)  # 4 K blocks x 2 strips per wave
     assert w4.gemm_plan(1, 22016, 4096, 128, w4.I8)[3] == 32
     assert w4.gemm_plan(1, 8192, 8192, 128, w4.BF16)[:2] == (1, 8) and w4.gemm_plan(1, 8192, 8192, 128, w4.BF16)[3] == 32
     assert w4.gemm_plan(16, 22016, 4096, 128, w4.I8)[3] == 32
