@@ -101,77 +101,14 @@ hipError_t launch_prepack(const void* w_in, void* w_packed, int64_t N, int64_t K
 // 16-byte chunks (8 elements) of the row in registers, so the row is read from
 // HBM once: pass 1 takes the absolute maximum, a wave reduction plus an LDS
 // exchange gives the row maximum, pass 2 forms the quotients and stores the
-// codes.  Longer rows re-read their tail in pass 2.
+// codes.  Longer rows re-read their tail in pass 2.  The chunk coder
+// (elem, chunk_absmax, div_rn, quant_chunk) is in w4_device.h.
 //
-// Quotients x / s must be the correctly rounded fp32 division.  They are
-// formed from one correctly rounded reciprocal per row, y = RN(1/s):
-// q = RN(x * y), the exact residual r = fma(-q, s, x), and RN(q + r * y), which
-// equals RN(x / s) by Markstein's theorem (y within half an ulp of 1/s, q
-// within one ulp of x/s, r exact; no overflow or underflow).  Rows whose scale
-// is too small for that (bf16 inputs near the bottom of the exponent range)
-// use the plain division.
-// ---------------------------------------------------------------------------
 // Chunks a thread keeps in registers: the launch picks the smallest of
 // 4, 8 or 12 that covers the row (a chunk slot past the row still costs an
 // address-pipeline pass, which matters when few rows share a CU), and at
 // most 4 in 1024-thread workgroups.
 constexpr int kMaxChunks = 12;
-
-template <int XT>
-__device__ __forceinline__ float elem(const uint4& v, int j) {
-  const uint32_t w = (j < 2) ? v.x : (j < 4) ? v.y : (j < 6) ? v.z : v.w;
-  const uint32_t b = (j & 1) ? (w >> 16) : (w & 0xFFFFu);
-  return XT == W4_F16 ? f16_bits_to_f32(b) : bf16_bits_to_f32(b);
-}
-
-template <int XT>
-__device__ __forceinline__ float chunk_absmax(float m, const uint4& v) {
-#pragma unroll
-  for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(elem<XT>(v, j)));
-  return m;
-}
-
-// correctly rounded x / s given y = RN(1 / s) (see above).  The sum q + r*y
-// of a zero quotient is +0 even for x = -0, so the sign is taken from x (with
-// s > 0 the quotient always has the sign of x).
-__device__ __forceinline__ float div_rn(float x, float s, float y) {
-  const float q = x * y;
-  const float r = fmaf(-q, s, x);
-  return copysignf(fmaf(r, y, q), x);
-}
-
-template <int XT, int QT, bool FAST>
-__device__ __forceinline__ uint2 quant_chunk(const uint4& v, float s, float y) {
-  uint32_t out[2];
-  if (QT == W4_I8) {
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      uint32_t word = 0;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float x = elem<XT>(v, 4 * h + j);
-        float q = rintf(FAST ? div_rn(x, s, y) : x / s);
-        q = fminf(fmaxf(q, -127.0f), 127.0f);
-        word |= ((uint32_t)(int)q & 0xFFu) << (8 * j);
-      }
-      out[h] = word;
-    }
-  } else {
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      float q[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float x = elem<XT>(v, 4 * h + j);
-        q[j] = fminf(fmaxf(FAST ? div_rn(x, s, y) : x / s, -448.0f), 448.0f);
-      }
-      int word = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
-      word = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], word, true);
-      out[h] = (uint32_t)word;
-    }
-  }
-  return make_uint2(out[0], out[1]);
-}
 
 // ---------------------------------------------------------------------------
 // Fused RMSNorm.  "[ Kernel ] Enable Dynamic Per Token fp8", review
