@@ -243,6 +243,28 @@ W4_API int w4a8_gemm(const void* aq, int a_dtype, const float* a_scales, const v
               void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * W4A8 GEMM with the per-token quantisation fused into the small-M kernel.
+ *
+ * "[ Kernel ] Enable Dynamic Per Token fp8", review discussion: per-token
+ * scales make it easy to fuse the quantisation with its neighbours.  Returns
+ * what w4_quant_act_per_token followed by w4a8_gemm returns (the same codes,
+ * scales and output bits), in one launch: every workgroup of the small-M
+ * kernel quantises the M rows into its LDS before its main loop.
+ *
+ * x           : device, [M][K] of x_dtype (W4_F16 or W4_BF16), finite values.
+ * q_dtype     : W4_I8 or W4_FP8_E4M3 (the activation codes).
+ * a_scales_out: device, [M] fp32, receives the per-token scales, or NULL.
+ * Other arguments as w4a8_gemm.  Supported where the problem takes the
+ * small-M kernel (M <= 16) and the M*K codes fit its LDS (M*K + tables below
+ * about 32 KiB); otherwise W4_E_UNSUPPORTED, and the two calls are the way.
+ * No workspace.  Errors as w4a8_gemm, plus W4_E_UNSUPPORTED.
+ * ------------------------------------------------------------------------- */
+W4_API int w4a8_gemm_quant_fused(const void* x, int x_dtype, int q_dtype, const void* b_packed, int wtype,
+                                 const void* b_scales, int s_dtype, int64_t group_size, const void* bias,
+                                 void* out, int out_dtype, int64_t M, int64_t N, int64_t K, float* a_scales_out,
+                                 void* stream);
+
+/* ---------------------------------------------------------------------------
  * Asymmetric W4A8 GEMM (weights with zero-points).
  *
  * "support W4A8 Marlin kernel", limitations comment: QQQ's W4A8 handles

@@ -484,6 +484,53 @@ int w4a8_gemm(const void* aq, int a_dtype, const float* a_scales, const void* b_
   return run_gemm(args, op_of(a_dtype), g != K, wtype == W4_UINT4B8, workspace, workspace_bytes, stream);
 }
 
+int w4a8_gemm_quant_fused(const void* x, int x_dtype, int q_dtype, const void* b_packed, int wtype,
+                          const void* b_scales, int s_dtype, int64_t group_size, const void* bias, void* out,
+                          int out_dtype, int64_t M, int64_t N, int64_t K, float* a_scales_out, void* stream) {
+  if (x_dtype != W4_F16 && x_dtype != W4_BF16) return fail(W4_E_DTYPE, "x_dtype must be W4_F16 or W4_BF16");
+  if (q_dtype != W4_I8 && q_dtype != W4_FP8_E4M3) return fail(W4_E_DTYPE, "q_dtype must be W4_I8 or W4_FP8_E4M3");
+  if (int st = validate_w4a8(x, q_dtype, b_packed, wtype, group_size, M, N, K)) return st;
+  if (s_dtype != W4_F32 && s_dtype != W4_F16 && s_dtype != W4_BF16)
+    return fail(W4_E_DTYPE, "s_dtype must be W4_F32, W4_F16 or W4_BF16");
+  if (out_dtype != W4_F16 && out_dtype != W4_BF16) return fail(W4_E_DTYPE, "out_dtype must be W4_F16 or W4_BF16");
+  if (!b_scales || (M > 0 && !out)) return fail(W4_E_NULL, "b_scales and out are required");
+  if (!aligned(out, 16) || !aligned(b_scales, s_dtype == W4_F32 ? 4 : 2) || !aligned(bias, 2) ||
+      !aligned(a_scales_out, 4))
+    return fail(W4_E_ALIGN, "out must be 16-byte aligned; scales and bias naturally aligned");
+  if (M == 0) return ok();
+  const int64_t g = resolve_group(group_size, K);
+  const bool grouped = g != K;
+  const int op = op_of(q_dtype);
+  GemmPlan plan;
+  if (int st = make_plan(M, N, K, grouped, op, &plan)) return st;
+  const int ns = plan.bn / 16;
+  // the codes stay in the small-M kernel's LDS next to its tables
+  const int64_t lds = skinny_table_bytes(op, grouped, K / g, ns) + M * K + 32 + skinny_static_lds(op, grouped, ns);
+  if (plan.path != PATH_SKINNY || lds > 65536)
+    return fail(W4_E_UNSUPPORTED,
+                "fused quantisation needs the small-M kernel with M*K codes in LDS (M=%lld K=%lld): "
+                "use w4_quant_act_per_token and w4a8_gemm", (long long)M, (long long)K);
+  GemmArgs args{};
+  args.x = x;
+  args.x_dtype = x_dtype;
+  args.a_scales_out = a_scales_out;
+  args.b = static_cast<const uint32_t*>(b_packed);
+  args.s = b_scales;
+  args.bias = bias;
+  args.out = out;
+  args.M = M;
+  args.N = N;
+  args.K = K;
+  args.G = (int)(K / g);
+  args.s_dtype = s_dtype;
+  args.out_dtype = out_dtype;
+  args.z_dtype = W4_F16;
+  args.mode = MODE_OUTPUT;
+  hipError_t e = launch_gemm(args, op, grouped, wtype == W4_UINT4B8, false, plan, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "fused GEMM launch");
+  return ok();
+}
+
 int w4a8_gemm_zp(const void* aq, const float* a_scales, const void* b_packed, const void* b_scales, int s_dtype,
                  const void* zeros, int z_dtype, int64_t group_size, const void* bias, void* out, int out_dtype,
                  int64_t M, int64_t N, int64_t K, void* workspace, size_t workspace_bytes, void* stream) {

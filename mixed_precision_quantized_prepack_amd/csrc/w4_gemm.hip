@@ -278,7 +278,7 @@ constexpr int waitcnt_vm_lgkm0(int vm) { return (vm & 15) | ((vm >> 4) << 14) | 
 // its D rows for a K block with one 16-byte LDS read, instead of a 64-lane
 // gather from memory per block (which costs the address pipeline as much as
 // the block's weights).  The table's size is set at launch.
-template <int OP, bool GROUPED, bool FLIP, int NS, bool PARTIALS, bool ZP, int SG>
+template <int OP, bool GROUPED, bool FLIP, int NS, bool PARTIALS, bool ZP, int SG, bool QA>
 __global__ __launch_bounds__(64 * skinny_max_waves(OP, GROUPED)) void w4_gemm_skinny(GemmArgs p, int S) {
   using Acc = typename OpTraits<OP>::Acc;
   constexpr int EB = OpTraits<OP>::kElemBytes;
@@ -296,10 +296,12 @@ __global__ __launch_bounds__(64 * skinny_max_waves(OP, GROUPED)) void w4_gemm_sk
   const int zdt = p.z_dtype;                      // zero-point storage dtype
   static_assert(!ZP || (OP == OP_I8 && FLIP), "zero-points: int8 operand from raw uint4 codes");
   static_assert(SG == 1 || (GROUPED && (OP == OP_F16 || OP == OP_BF16)), "sub-groups: grouped W4A16 only");
+  static_assert(!QA || ((OP == OP_I8 || OP == OP_FP8) && !PARTIALS && !ZP && SG == 1),
+                "fused quantisation: W4A8 outputs only");
 
   const __amdgpu_buffer_rsrc_t rw =
       make_rsrc(reinterpret_cast<const uint8_t*>(p.b) + nb0 * KB * 1024, (int64_t)NS * KB * 1024);
-  const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a, p.M * p.K * EB);
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a, QA ? 0 : p.M * p.K * EB);
   const int sbytes = p.s_dtype == W4_F32 ? 4 : 2;
   // scales are absent (null) in the partials entry points: an empty buffer
   // (a product, not a branch: a branch here would wait for the kernel
@@ -360,6 +362,72 @@ __global__ __launch_bounds__(64 * skinny_max_waves(OP, GROUPED)) void w4_gemm_sk
   // staging slots past its end)
   float* const tsc = skinny_tab;
   float* const tz = skinny_tab + (GROUPED ? NS * p.G * 16 + 16 : 0);
+  // fused quantisation: the codes [M][K] (row-major, as the quantiser writes
+  // them) after the tables, then a 32-byte zero pad that rows past M and
+  // blocks past K read
+  uint8_t* const qcodes =
+      reinterpret_cast<uint8_t*>(skinny_tab) + skinny_tables(OP, GROUPED, ZP) * (NS * p.G * 16 + 16) * 4;
+  const uint32_t qpad = (uint32_t)(p.M * p.K);
+  __shared__ uint32_t qa_max[QA ? 16 : 1];
+  __shared__ float qa_s[QA ? 16 : 1];
+  if constexpr (QA) {
+    // Per-token quantisation of the M rows into LDS (the same codes and
+    // scales as the quantisation kernel): per row, the workgroup's threads
+    // take 16-byte chunks, a wave maximum and an LDS maximum give the row's
+    // absolute maximum, then the chunks are coded (re-read from L2 when the
+    // row spans more than one round of chunks).
+    constexpr int QC = 8;   // chunks per thread per round
+    const int T = (int)blockDim.x;
+    const int nch = (int)(p.K >> 3);
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(p.x, p.M * p.K * 2);
+    constexpr int QT = OP == OP_I8 ? W4_I8 : W4_FP8_E4M3;
+    const float qmax = OP == OP_I8 ? 127.0f : 448.0f;
+    const bool f16 = p.x_dtype == W4_F16;
+    if (threadIdx.x < 16) qa_max[threadIdx.x] = 0u;
+    if (threadIdx.x < 8) reinterpret_cast<uint32_t*>(qcodes + qpad)[threadIdx.x] = 0u;
+    __syncthreads();
+    auto load_round = [&](int m, int c0, uint4* v) {
+#pragma unroll
+      for (int i = 0; i < QC; ++i) {
+        const int c = c0 + (int)threadIdx.x + i * T;
+        const u32x4 w = buffer_load16(rx, c < nch ? (uint32_t)((m * p.K + c * 8) * 2) : kOutOfRange);
+        v[i] = make_uint4(w.x, w.y, w.z, w.w);
+      }
+    };
+    for (int m = 0; m < p.M; ++m) {
+      uint4 v[QC];
+      float amax = 0.0f;
+      for (int c0 = 0; c0 < nch; c0 += QC * T) {
+        load_round(m, c0, v);
+#pragma unroll
+        for (int i = 0; i < QC; ++i) amax = f16 ? chunk_absmax<W4_F16>(amax, v[i]) : chunk_absmax<W4_BF16>(amax, v[i]);
+      }
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+      if (lane == 0) atomicMax(&qa_max[m], __float_as_uint(amax));   // amax >= 0: integer order
+      __syncthreads();
+      const float s = __uint_as_float(qa_max[m]) / qmax;
+      const float y = 1.0f / s;
+      if (threadIdx.x == 0) qa_s[m] = s;
+      if (threadIdx.x == 0 && blockIdx.x == 0 && p.a_scales_out) p.a_scales_out[m] = s;
+      for (int c0 = 0; c0 < nch; c0 += QC * T) {
+        if (nch > QC * T) load_round(m, c0, v);   // one round: the chunks are still in registers
+#pragma unroll
+        for (int i = 0; i < QC; ++i) {
+          const int c = c0 + (int)threadIdx.x + i * T;
+          uint2 q = make_uint2(0u, 0u);
+          if (s != 0.0f) {
+            if (s >= 0x1p-100f)
+              q = f16 ? quant_chunk<W4_F16, QT, true>(v[i], s, y) : quant_chunk<W4_BF16, QT, true>(v[i], s, y);
+            else
+              q = f16 ? quant_chunk<W4_F16, QT, false>(v[i], s, y) : quant_chunk<W4_BF16, QT, false>(v[i], s, y);
+          }
+          if (c < nch) *reinterpret_cast<uint2*>(qcodes + (uint32_t)(m * p.K + c * 8)) = q;
+        }
+      }
+    }
+    __syncthreads();
+  }
 
   auto load_batch = [&](int buf, int kb) {   // kb: this wave's batch index in blocks of S
 #pragma unroll
@@ -371,8 +439,13 @@ __global__ __launch_bounds__(64 * skinny_max_waves(OP, GROUPED)) void w4_gemm_sk
         wv[buf][u][j] = __builtin_amdgcn_raw_buffer_load_b128(
             rw, (int)(in ? (uint32_t)((j * KB + k) * 1024) + w_lane : kOutOfRange), 0, W4_SKINNY_WPOLICY);
 #pragma unroll
-      for (int a = 0; a < AV; ++a)
-        av[buf][u][a] = buffer_load16(ra, in ? a_lane + (uint32_t)(k * 128 * EB + 16 * a) : kOutOfRange);
+      for (int a = 0; a < AV; ++a) {
+        if constexpr (QA)
+          av[buf][u][a] = *reinterpret_cast<const u32x4*>(
+              qcodes + (in && r < p.M ? a_lane + (uint32_t)(k * 128 + 16 * a) : qpad));
+        else
+          av[buf][u][a] = buffer_load16(ra, in ? a_lane + (uint32_t)(k * 128 * EB + 16 * a) : kOutOfRange);
+      }
     }
   };
   auto compute_batch = [&](int buf, int kb, bool pin) {
@@ -623,7 +696,10 @@ __global__ __launch_bounds__(64 * skinny_max_waves(OP, GROUPED)) void w4_gemm_sk
         const float sn = word_to_f32(ep_s, p.s_dtype, (uint32_t)ep_n);
         v = (OP == OP_I8) ? (float)iv * (sn * 0.0625f) : fv * sn;
       }
-      if (p.a_scales) v *= __uint_as_float(ep_a);
+      if constexpr (QA)
+        v *= qa_s[ep_m];
+      else if (p.a_scales)
+        v *= __uint_as_float(ep_a);
       if (p.bias) v += word_to_f32(ep_b, p.out_dtype, (uint32_t)ep_n);
       store_out(p, ep_m, ep_n, v);
     }
@@ -1279,19 +1355,35 @@ static hipError_t launch_typed(const GemmArgs& args, const GemmPlan& plan, hipSt
     const dim3 grid((unsigned)(args.N / plan.bn));
     const bool part = args.mode == MODE_PARTIALS;
     const size_t tab = (size_t)skinny_table_bytes(OP, GROUPED, args.G, ns, ZP);   // checked by the plan
+    if (args.x) {
+      // fused quantisation: the codes and their pad follow the tables
+      if constexpr ((OP == OP_I8 || OP == OP_FP8) && !ZP && SG == 1) {
+        const size_t lds = tab + (size_t)(args.M * args.K) + 32;
+        if (ns == 2)
+          hipLaunchKernelGGL((w4_gemm_skinny<OP, GROUPED, FLIP, 2, false, false, 1, true>), grid, dim3(threads), lds,
+                             stream, args, S);
+        else
+          hipLaunchKernelGGL((w4_gemm_skinny<OP, GROUPED, FLIP, 1, false, false, 1, true>), grid, dim3(threads), lds,
+                             stream, args, S);
+        return hipGetLastError();
+      } else {
+        return hipErrorInvalidValue;
+      }
+    }
     if (ns == 2) {
       if (part)
-        hipLaunchKernelGGL((w4_gemm_skinny<OP, GROUPED, FLIP, 2, true, ZP, SG>), grid, dim3(threads), tab, stream, args, S);
+        hipLaunchKernelGGL((w4_gemm_skinny<OP, GROUPED, FLIP, 2, true, ZP, SG, false>), grid, dim3(threads), tab, stream, args, S);
       else
-        hipLaunchKernelGGL((w4_gemm_skinny<OP, GROUPED, FLIP, 2, false, ZP, SG>), grid, dim3(threads), tab, stream, args, S);
+        hipLaunchKernelGGL((w4_gemm_skinny<OP, GROUPED, FLIP, 2, false, ZP, SG, false>), grid, dim3(threads), tab, stream, args, S);
     } else {
       if (part)
-        hipLaunchKernelGGL((w4_gemm_skinny<OP, GROUPED, FLIP, 1, true, ZP, SG>), grid, dim3(threads), tab, stream, args, S);
+        hipLaunchKernelGGL((w4_gemm_skinny<OP, GROUPED, FLIP, 1, true, ZP, SG, false>), grid, dim3(threads), tab, stream, args, S);
       else
-        hipLaunchKernelGGL((w4_gemm_skinny<OP, GROUPED, FLIP, 1, false, ZP, SG>), grid, dim3(threads), tab, stream, args, S);
+        hipLaunchKernelGGL((w4_gemm_skinny<OP, GROUPED, FLIP, 1, false, ZP, SG, false>), grid, dim3(threads), tab, stream, args, S);
     }
     return hipGetLastError();
   }
+  if (args.x) return hipErrorInvalidValue;   // the fused quantisation exists in the small-M kernel only
   constexpr bool kByte = (OP == OP_I8 || OP == OP_FP8);
   auto finish = [&]() -> hipError_t {
     hipError_t e = hipGetLastError();

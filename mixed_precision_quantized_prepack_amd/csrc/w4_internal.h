@@ -28,6 +28,12 @@ struct GemmArgs {
   int s_dtype;             // W4_F32 / W4_F16 / W4_BF16
   int out_dtype;           // W4_F16 / W4_BF16
   int z_dtype;             // zero-point storage: W4_F16 / W4_BF16 / W4_F32
+  // fused per-token quantisation (small-M kernel): x holds the fp16 / bf16
+  // activations [M][K] (a is unused); the per-token scales go to
+  // a_scales_out when it is not null
+  const void* x;
+  int x_dtype;
+  float* a_scales_out;
   int mode;                // Mode
   int64_t m0, m1, n0, n1;  // partials window
 };
@@ -70,7 +76,14 @@ hipError_t launch_quant_per_tensor(const void* x, int x_dtype, void* xq, int q_d
                                    int64_t K, hipStream_t stream);
 hipError_t launch_rmsnorm_quant(const void* x, int x_dtype, const void* gamma, float eps, void* xq, int q_dtype,
                                 float* scales, int64_t M, int64_t K, int exact_sum, hipStream_t stream);
+// Bytes of LDS the small-M kernel declares statically (its wave-order
+// reduction buffer and the fused quantiser's row maxima and scales).
+constexpr int64_t skinny_static_lds(int op, bool grouped, int strips) {
+  return (int64_t)skinny_max_waves(op, grouped) * strips * 64 * 4 * 4 + 2 * 16 * 4;
+}
+
 // zp: asymmetric int8 W4A8 (op OP_I8, flip set: raw uint4 codes, zero-points in args.z).
+// The fused quantisation (args.x set) takes the small-M kernel (plan.path == PATH_SKINNY).
 hipError_t launch_gemm(const GemmArgs& args, int op, bool grouped, bool flip, bool zp, const GemmPlan& plan,
                        hipStream_t stream);
 

@@ -160,6 +160,25 @@ def test_w4a16_validation(lib):
     assert call(M=0) == W4_OK
 
 
+def test_w4a8_quant_fused_validation(lib):
+    f = lib.w4a8_gemm_quant_fused
+
+    def call(x=FAKE, x_dtype=0, q_dtype=3, b=FAKE, wtype=0, bs=FAKE, s_dtype=2, gs=-1, out=FAKE, out_dtype=0,
+             M=1, N=32, K=256, so=None):
+        return f(x, x_dtype, q_dtype, b, wtype, bs, s_dtype, gs, None, out, out_dtype, M, N, K, so, None)
+    assert call(x_dtype=3) == E_DTYPE
+    assert call(q_dtype=0) == E_DTYPE
+    assert call(wtype=1) == E_DTYPE
+    assert call(b=None) == E_NULL
+    assert call(out=None) == E_NULL
+    assert call(x=MISALIGNED) == E_ALIGN
+    assert call(so=ctypes.c_void_p(0x10002)) == E_ALIGN
+    assert call(gs=64) == E_GROUP
+    assert call(M=17) == E_UNSUP                             # the tiled kernel: no fused quantisation
+    assert call(M=16, N=8192, K=21760) == E_UNSUP            # 16 x 21760 codes exceed the LDS
+    assert call(M=0) == W4_OK
+
+
 def test_w4a8_zp_validation(lib):
     f = lib.w4a8_gemm_zp
 
