@@ -370,34 +370,41 @@ __global__ __launch_bounds__(64 * skinny_max_waves(OP, GROUPED)) void w4_gemm_sk
   const uint32_t qpad = (uint32_t)(p.M * p.K);
   __shared__ uint32_t qa_max[QA ? 16 : 1];
   __shared__ float qa_s[QA ? 16 : 1];
-  if constexpr (QA) {
-    // Per-token quantisation of the M rows into LDS (the same codes and
-    // scales as the quantisation kernel): per row, the workgroup's threads
-    // take 16-byte chunks, a wave maximum and an LDS maximum give the row's
-    // absolute maximum, then the chunks are coded (re-read from L2 when the
-    // row spans more than one round of chunks).
+  // Fused quantisation: per-token quantisation of the M rows into LDS (the
+  // same codes and scales as the quantisation kernel).  The waves split into
+  // one group per row (rows past the groups' count loop): a group's threads
+  // take 16-byte chunks of its row, a wave maximum and an LDS maximum give
+  // the row's absolute maximum, then the chunks are coded (re-read from L2
+  // unless the group's one row fitted one round of chunks in registers).
+  auto quantise_rows = [&]() {
     constexpr int QC = 8;   // chunks per thread per round
-    const int T = (int)blockDim.x;
     const int nch = (int)(p.K >> 3);
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(p.x, p.M * p.K * 2);
     constexpr int QT = OP == OP_I8 ? W4_I8 : W4_FP8_E4M3;
     const float qmax = OP == OP_I8 ? 127.0f : 448.0f;
     const bool f16 = p.x_dtype == W4_F16;
+    const int nw = (int)(blockDim.x >> 6);
+    const int gw = nw >= p.M ? nw / (int)p.M : 1;    // waves per row
+    const int ngr = nw / gw;                          // rows in flight
+    const int grp = wave / gw;
+    const int Tr = gw * 64;
+    const int tr = (wave - grp * gw) * 64 + lane;     // thread within the row's group
+    const bool keep = p.M <= ngr && nch <= QC * Tr;
     if (threadIdx.x < 16) qa_max[threadIdx.x] = 0u;
     if (threadIdx.x < 8) reinterpret_cast<uint32_t*>(qcodes + qpad)[threadIdx.x] = 0u;
     __syncthreads();
     auto load_round = [&](int m, int c0, uint4* v) {
 #pragma unroll
       for (int i = 0; i < QC; ++i) {
-        const int c = c0 + (int)threadIdx.x + i * T;
+        const int c = c0 + tr + i * Tr;
         const u32x4 w = buffer_load16(rx, c < nch ? (uint32_t)((m * p.K + c * 8) * 2) : kOutOfRange);
         v[i] = make_uint4(w.x, w.y, w.z, w.w);
       }
     };
-    for (int m = 0; m < p.M; ++m) {
-      uint4 v[QC];
+    uint4 v[QC];
+    for (int m = grp; grp < ngr && m < p.M; m += ngr) {
       float amax = 0.0f;
-      for (int c0 = 0; c0 < nch; c0 += QC * T) {
+      for (int c0 = 0; c0 < nch; c0 += QC * Tr) {
         load_round(m, c0, v);
 #pragma unroll
         for (int i = 0; i < QC; ++i) amax = f16 ? chunk_absmax<W4_F16>(amax, v[i]) : chunk_absmax<W4_BF16>(amax, v[i]);
@@ -405,16 +412,20 @@ __global__ __launch_bounds__(64 * skinny_max_waves(OP, GROUPED)) void w4_gemm_sk
 #pragma unroll
       for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
       if (lane == 0) atomicMax(&qa_max[m], __float_as_uint(amax));   // amax >= 0: integer order
-      __syncthreads();
+    }
+    __syncthreads();
+    for (int m = grp; grp < ngr && m < p.M; m += ngr) {
       const float s = __uint_as_float(qa_max[m]) / qmax;
       const float y = 1.0f / s;
-      if (threadIdx.x == 0) qa_s[m] = s;
-      if (threadIdx.x == 0 && blockIdx.x == 0 && p.a_scales_out) p.a_scales_out[m] = s;
-      for (int c0 = 0; c0 < nch; c0 += QC * T) {
-        if (nch > QC * T) load_round(m, c0, v);   // one round: the chunks are still in registers
+      if (tr == 0) {
+        qa_s[m] = s;
+        if (blockIdx.x == 0 && p.a_scales_out) p.a_scales_out[m] = s;
+      }
+      for (int c0 = 0; c0 < nch; c0 += QC * Tr) {
+        if (!keep) load_round(m, c0, v);
 #pragma unroll
         for (int i = 0; i < QC; ++i) {
-          const int c = c0 + (int)threadIdx.x + i * T;
+          const int c = c0 + tr + i * Tr;
           uint2 q = make_uint2(0u, 0u);
           if (s != 0.0f) {
             if (s >= 0x1p-100f)
@@ -427,7 +438,7 @@ __global__ __launch_bounds__(64 * skinny_max_waves(OP, GROUPED)) void w4_gemm_sk
       }
     }
     __syncthreads();
-  }
+  };
 
   auto load_batch = [&](int buf, int kb) {   // kb: this wave's batch index in blocks of S
 #pragma unroll
@@ -598,6 +609,10 @@ __global__ __launch_bounds__(64 * skinny_max_waves(OP, GROUPED)) void w4_gemm_sk
       if constexpr (ZP) tz[slot] = (p.z ? word_to_f32(twz[t], zdt, idx) : 8.0f) - 8.0f;
     }
   };
+  // fused quantisation: the codes are in LDS before any batch is issued
+  // (issuing the first batches' weights before the quantisation measured
+  // slower: the quantisation's loads then wait for them)
+  if constexpr (QA) quantise_rows();
   if constexpr (kTab) {
     stage_load(0);
     asm volatile("" ::: "memory");
