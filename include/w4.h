@@ -12,13 +12,22 @@
  *           fp16/bf16 activations ("...mixed_precision.rdna_hybrid_w4a16"
  *           API page, triton_w4a16_skinny_fmt_gemm docstring).
  *
+ * Entry points: w4_prepack_B (and w4_prepack_B_from_exllama), the activation
+ * quantisers (w4_quant_act_per_token, w4_quant_act_per_tensor,
+ * w4_rmsnorm_quant_per_token), the GEMMs (w4a8_gemm, w4a8_gemm_zp,
+ * w4a8_gemm_quant_fused, w4a16_gemm), their verification variants
+ * (w4a8_gemm_partials, w4a16_gemm_partials), and the planning helpers
+ * (w4_gemm_workspace_bytes, w4_gemm_plan, w4_schedule_add / _clear,
+ * w4_set_option / w4_get_option).
+ *
  * General conventions (every entry point):
  *   - All pointers named as device pointers must point to device memory of
  *     the current HIP device; all arrays are dense and row-major.  Every device
  *     pointer must be 16-byte aligned.
  *   - The caller owns every buffer.  The library never allocates, frees or
  *     synchronises; it keeps no per-call state and may be called concurrently
- *     from several threads (on distinct output/workspace buffers).
+ *     from several threads (on distinct output/workspace buffers).  The
+ *     tuning options and the run-time schedule entries are process-wide.
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *     Work is enqueued on it and the call returns without waiting.
  *   - Arguments are validated on the host before anything is enqueued.  On a
