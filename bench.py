@@ -270,7 +270,7 @@ def main(argv=None) -> int:
     if args.summarize:
         return summarize(*args.summarize)
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: the kernels run on a single MI355X and this build has no "
+        print(f"bench.py measures one GPU: the library runs on a single MI355X and has no "
               f"multi-GPU path (asked for --gpus {args.gpus}).", file=sys.stderr)
         return 2
     Ms = tuple(int(x) for x in args.ms.split(","))
