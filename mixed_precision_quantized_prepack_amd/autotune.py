@@ -167,7 +167,7 @@ def tune(shapes, buckets, trials: int, margin: float, log=print):
             h_us = best.pop(None)
             c_best = min(best, key=best.get) if best else None
             b_us = best[c_best] if c_best else h_us
-            keep = c_best is not None and b_us < h_us * (1.0 - margin)
+            keep = c_best is not None and b_us < h_us * (1.0 - margin) and not same_schedule(heur, c_best)
             row = {"shape": name, "a_dtype": a_dtype, "grouped": grouped, "N": N, "K": K, "m_lo": lo,
                    "m_hi": hi, "M": M, "heuristic": list(heur), "heuristic_us": round(h_us, 2),
                    "best": list(c_best) if c_best else None, "best_us": round(b_us, 2), "keep": keep,
@@ -181,13 +181,23 @@ def tune(shapes, buckets, trials: int, margin: float, log=print):
     return results
 
 
+def same_schedule(plan, cand) -> bool:
+    """Whether a candidate (path, splitk, tile_m, strips) is the plan
+    (path, splitk, tile_m, tile_n) itself: then a faster timing is noise."""
+    path, split, tm, tn = plan
+    cp, cs, ctm, cst = cand
+    if cp != path or cs != split:
+        return False
+    return ctm == tm if path == 2 else cst * 16 == tn
+
+
 def write_table(results, path: str = TABLE_PATH) -> int:
     lines = ["// Schedule table: {a_dtype, grouped, N, K, m_lo, m_hi, path, splitk, tile_m, strips}.",
              "// Written by mixed_precision_quantized_prepack_amd/autotune.py from MI355X measurements;",
              "// each entry beat the heuristic's schedule at m_hi (timings in the comment)."]
     n = 0
     for r in results:
-        if not r["keep"]:
+        if not r["keep"] or same_schedule(r["heuristic"], r["best"]):
             continue
         p, s, tm, st = r["best"]
         lines.append(f"    {{{DTYPE_NAMES[r['a_dtype']]}, {int(r['grouped'])}, {r['N']}, {r['K']}, {r['m_lo']}, "

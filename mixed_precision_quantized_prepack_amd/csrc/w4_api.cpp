@@ -191,16 +191,18 @@ int plan_with(int64_t M, int64_t N, int64_t K, bool grouped, int op, const Sched
     plan->splitk = (int)s;
   } else {
     // 8-bit operands: 128-row tiles when there are enough of them (int8
-    // per channel: two workgroups per CU; grouped and fp8, whose tall tile
-    // is 128 x 128: one), 64 x 256 tiles otherwise
+    // per channel: two workgroups per CU; grouped int8, whose tall tile is
+    // 128 x 128: one; grouped fp8: half a workgroup per CU once M fills the
+    // 128 rows), 64 x 256 tiles otherwise
     const bool byte = op == OP_I8 || op == OP_FP8;
+    const bool fp8g = op == OP_FP8 && grouped;
     const int64_t fbm = forced.tile_m;
     if (byte) {
       int tall_bm, tall_bn;
       tiled_tile(op, grouped, 1, &tall_bm, &tall_bn, zp);
       const int64_t tall_tiles = ((M + tall_bm - 1) / tall_bm) * ((N + tall_bn - 1) / tall_bn);
       const int64_t need = (op == OP_I8 && !grouped) ? 2LL * cu : (int64_t)cu;
-      const bool tall = fbm ? fbm == 128 : tall_tiles >= need;
+      const bool tall = fbm ? fbm == 128 : (fp8g ? M >= 128 && 2 * tall_tiles >= cu : tall_tiles >= need);
       tiled_tile(op, grouped, tall ? 1 : 0, &plan->bm, &plan->bn, zp);
     } else if (fbm && fbm != plan->bm) {
       return fail(W4_E_SHAPE, "tiled_bm=%lld is not available for this problem", (long long)fbm);
@@ -216,11 +218,14 @@ int plan_with(int64_t M, int64_t N, int64_t K, bool grouped, int op, const Sched
       // that the reduce reads back, which outweighs the second workgroup
       // there).  Grouped int8 keeps the VALU busy with its per-group fold,
       // so a second workgroup per CU gains nothing: the most splits that
-      // still fit one workgroup per CU.
+      // still fit one workgroup per CU.  Grouped fp8 (lookup expansion and
+      // fold): the most that fit two.
       const int64_t tiles = ((M + plan->bm - 1) / plan->bm) * ((N + plan->bn - 1) / plan->bn);
       s = 1;
       if (op == OP_I8 && grouped) {
         while (tiles * s * 2 <= cu && s * 2 <= 16) s *= 2;
+      } else if (fp8g) {
+        while (tiles * s * 2 <= 2LL * cu && s * 2 <= 16) s *= 2;
       } else {
         const int64_t target = tiles < cu / 2 ? cu : 2LL * cu;
         while (tiles * s < target && s * 2 <= 8) s *= 2;

@@ -243,6 +243,11 @@ def test_plan_choices(lib, heuristic_only):
     assert w4.gemm_plan(128, 22016, 4096, 128, w4.I8)[2:] == (64, 256)
     assert w4.gemm_plan(8192, 28672, 8192, 128, w4.FP8_E4M3)[1:] == (1, 128, 128)
     assert w4.gemm_plan(32, 28672, 8192, 128, w4.FP8_E4M3)[2:] == (64, 256)
+    # grouped fp8: the tall tile from M = 128 (half a workgroup per CU), the
+    # most K splits that fit two workgroups per CU
+    assert w4.gemm_plan(128, 28672, 8192, 128, w4.FP8_E4M3)[1:] == (2, 128, 128)
+    assert w4.gemm_plan(256, 28672, 8192, 128, w4.FP8_E4M3)[1:] == (1, 128, 128)
+    assert w4.gemm_plan(64, 28672, 8192, 128, w4.FP8_E4M3)[1:] == (4, 64, 256)
     # a grouped K whose LDS scale table would not fit the small-M kernel: tiled
     assert w4.gemm_plan(1, 8192, 131072, 128, w4.I8)[0] == 2
     try:
