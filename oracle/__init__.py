@@ -11,5 +11,5 @@ from .w4_oracle import (  # noqa: F401
     prepack_B_from_exllama,
     quant_act_per_token, quant_act_per_tensor, rmsnorm_rows, rmsnorm_quant_per_token, activation_integers, w4a8_group_partials, w4a8_gemm,
     zero_point_weights,
-    w4a16_gemm, w4a16_group_partials,
+    w4a16_gemm, w4a16_gemm_prescaled_zeros, w4a16_group_partials,
 )

@@ -506,6 +506,44 @@ def w4a16_gemm(a_bits: np.ndarray, a_dtype: str, w_logical: np.ndarray, K: int, 
     return dict(out=F.round_and_encode(exact, a_dtype), exact=exact, mag=mag)
 
 
+def w4a16_gemm_prescaled_zeros(a_bits: np.ndarray, a_dtype: str, w_logical: np.ndarray, K: int,
+                               scales_bits: np.ndarray, zs_bits: np.ndarray, group_size: int,
+                               bias_bits: Optional[np.ndarray] = None, rows=None, cols=None) -> dict:
+    """W4A16 GEMM with pre-scaled zero-points (Machete README, *Overview*: the
+    dequantised weight is the code times its scale minus a zero term that
+    already carries the scale):
+
+        out[m, n] = RNE_a( sum_k a[m, k] * (u[n, k] * s[n, g(k)] - zs[n, g(k)]) + bias[n] )
+
+    u is the raw 4-bit code (0..15); s and zs are stored in the activation
+    dtype.  Sums in float64 (products of the stored values are exact).
+    """
+    gs = K if group_size in (-1, K) else group_size
+    G = K // gs
+    a = F.decode(a_bits if rows is None else a_bits[rows], a_dtype)
+    wl = w_logical if cols is None else w_logical[cols]
+    u = nibbles(wl, K).astype(np.float64)
+    s = F.decode(np.asarray(scales_bits).view(np.uint16), a_dtype).reshape(-1, G)
+    zs = F.decode(np.asarray(zs_bits).view(np.uint16), a_dtype).reshape(-1, G)
+    if cols is not None:
+        s, zs = s[cols], zs[cols]
+    acc = np.zeros((a.shape[0], u.shape[0]), dtype=np.float64)
+    mag = np.zeros_like(acc)
+    for g in range(G):
+        sl = slice(g * gs, (g + 1) * gs)
+        w = u[:, sl] * s[:, g:g + 1] - zs[:, g:g + 1]
+        acc += a[:, sl] @ w.T
+        mag += np.abs(a[:, sl]) @ np.abs(w).T
+    exact = acc
+    if bias_bits is not None:
+        b = F.decode(np.asarray(bias_bits).view(np.uint16), a_dtype)
+        if cols is not None:
+            b = b[cols]
+        exact = exact + b[None, :]
+        mag = mag + np.abs(b)[None, :]
+    return dict(out=F.round_and_encode(exact, a_dtype), exact=exact, mag=mag)
+
+
 def w4a16_group_partials(a_bits: np.ndarray, a_dtype: str, w_logical: np.ndarray, K: int,
                          wtype: str, zeros_bits: Optional[np.ndarray], group_size: int,
                          rows=None, cols=None) -> np.ndarray:
