@@ -15,7 +15,8 @@
  * Entry points: w4_prepack_B (and w4_prepack_B_from_exllama), the activation
  * quantisers (w4_quant_act_per_token, w4_quant_act_per_tensor,
  * w4_rmsnorm_quant_per_token), the GEMMs (w4a8_gemm, w4a8_gemm_zp,
- * w4a8_gemm_quant_fused, w4a16_gemm), their verification variants
+ * w4a8_gemm_quant_fused, w4a16_gemm, w4a16_gemm_prescaled_zeros), their
+ * verification variants
  * (w4a8_gemm_partials, w4a16_gemm_partials), and the planning helpers
  * (w4_gemm_workspace_bytes, w4_gemm_plan, w4_schedule_add / _clear,
  * w4_set_option / w4_get_option).
@@ -250,6 +251,27 @@ W4_API int w4a8_gemm(const void* aq, int a_dtype, const float* a_scales, const v
               int wtype, const void* b_scales, int s_dtype, int64_t group_size,
               const void* bias, void* out, int out_dtype, int64_t M, int64_t N, int64_t K,
               void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * W4A16 GEMM with pre-scaled zero-points.
+ *
+ * Machete README, "Overview": the dequantised weight is the code times its
+ * scale minus a zero term to which the scale is already applied (so that one
+ * FMA dequantises):
+ *
+ *   out[m,n] = RNE_a( sum_k a[m,k] * (c[n,k] * s[n,g] - zs[n,g]) + bias[n] )
+ *
+ * c are raw uint4 codes; s and zs [N][K/128] are in a_dtype (any values).
+ * The kernels take sum(a c) per group from the MFMAs and zs * sum(a) from a
+ * second MFMA with a ones-operand, both in fp32.
+ * group_size: 128 (K > 128).  Other arguments as w4a16_gemm (the workspace is
+ * the one w4_gemm_workspace_bytes reports for a_dtype and group size 128).
+ * Errors as w4a16_gemm.
+ * ------------------------------------------------------------------------- */
+W4_API int w4a16_gemm_prescaled_zeros(const void* a, int a_dtype, const void* b_packed, const void* scales,
+                                      const void* zeros_scaled, int64_t group_size, const void* bias, void* out,
+                                      int64_t M, int64_t N, int64_t K, void* workspace, size_t workspace_bytes,
+                                      void* stream);
 
 /* ---------------------------------------------------------------------------
  * W4A8 GEMM with the per-token quantisation fused into the small-M kernel.

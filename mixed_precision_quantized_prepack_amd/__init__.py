@@ -23,7 +23,7 @@ from typing import Optional
 __all__ = [
     "LIB_PATH", "lib", "W4Error", "prepack_B", "prepack_B_from_exllama", "prepack_B_bytes", "quant_act_per_token",
     "quant_act_per_tensor", "rmsnorm_quant_per_token",
-    "w4a8_gemm", "w4a8_gemm_quant_fused", "w4a8_gemm_zp", "w4a16_gemm", "w4a8_gemm_partials", "w4a16_gemm_partials",
+    "w4a8_gemm", "w4a8_gemm_quant_fused", "w4a8_gemm_zp", "w4a16_gemm", "w4a16_gemm_prescaled_zeros", "w4a8_gemm_partials", "w4a16_gemm_partials",
     "gemm_workspace_bytes", "gemm_plan", "set_option", "get_option", "schedule_add", "schedule_clear",
     "EXPORTED_SYMBOLS",
 ]
@@ -61,6 +61,8 @@ _SIGNATURES = [
                          _i64, _i64, _i64, _vp, _sz, _vp]),
     ("w4a8_gemm_quant_fused", _int, [_vp, _int, _int, _vp, _int, _vp, _int, _i64, _vp, _vp, _int,
                                      _i64, _i64, _i64, _vp, _vp]),
+    ("w4a16_gemm_prescaled_zeros", _int, [_vp, _int, _vp, _vp, _vp, _i64, _vp, _vp, _i64, _i64, _i64,
+                                          _vp, _sz, _vp]),
     ("w4a8_gemm_zp", _int, [_vp, _vp, _vp, _vp, _int, _vp, _int, _i64, _vp, _vp, _int,
                             _i64, _i64, _i64, _vp, _sz, _vp]),
     ("w4a16_gemm", _int, [_vp, _int, _vp, _int, _vp, _vp, _i64, _vp, _vp, _i64, _i64, _i64,
@@ -327,6 +329,24 @@ def w4a8_gemm_zp(aq, a_scales, b_packed, b_scales, zeros, group_size: int, out_d
         _dev_ptr(b_scales, "b_scales"), _dtype_code(b_scales.dtype), _dev_ptr(zeros, "zeros"),
         _dtype_code(zeros.dtype), group_size, _dev_ptr(bias, "bias"), _dev_ptr(out, "out"),
         _dtype_code(out_dtype), M, N, K, wsp, wsb, _stream(aq)))
+    return out
+
+
+def w4a16_gemm_prescaled_zeros(a, b_packed, scales, zeros_scaled, group_size: int = 128, bias=None, out=None,
+                               workspace=None):
+    """W4A16 GEMM with pre-scaled zero-points (include/w4.h): weight value
+    c * s - zs per group of 128; scales / zeros_scaled [N, K/128] in a's dtype."""
+    torch = _torch()
+    M, K = a.shape
+    N = scales.shape[0]
+    a_dt = _dtype_code(a.dtype)
+    if out is None:
+        out = torch.empty((M, N), dtype=a.dtype, device=a.device)
+    wsp, wsb = _workspace(workspace, gemm_workspace_bytes(M, N, K, group_size, a_dt), a.device)
+    _check("w4a16_gemm_prescaled_zeros", lib().w4a16_gemm_prescaled_zeros(
+        _dev_ptr(a, "a"), a_dt, _dev_ptr(b_packed, "b_packed"), _dev_ptr(scales, "scales"),
+        _dev_ptr(zeros_scaled, "zeros_scaled"), group_size, _dev_ptr(bias, "bias"), _dev_ptr(out, "out"),
+        M, N, K, wsp, wsb, _stream(a)))
     return out
 
 

@@ -613,6 +613,34 @@ int w4a16_gemm(const void* a, int a_dtype, const void* b_packed, int wtype, cons
   return run_gemm(args, op_of(a_dtype), g != K, false, workspace, workspace_bytes, stream);
 }
 
+int w4a16_gemm_prescaled_zeros(const void* a, int a_dtype, const void* b_packed, const void* scales,
+                               const void* zeros_scaled, int64_t group_size, const void* bias, void* out, int64_t M,
+                               int64_t N, int64_t K, void* workspace, size_t workspace_bytes, void* stream) {
+  if (int st = validate_w4a16(a, a_dtype, b_packed, W4_UINT4, zeros_scaled, group_size, M, N, K)) return st;
+  if (resolve_group(group_size, K) != 128 || K == 128)
+    return fail(W4_E_GROUP, "pre-scaled zero-points take groups of 128 (group_size=%lld)", (long long)group_size);
+  if (!scales || !zeros_scaled || (M > 0 && !out)) return fail(W4_E_NULL, "scales, zeros_scaled and out are required");
+  if (!aligned(out, 16) || !aligned(scales, 2) || !aligned(bias, 2))
+    return fail(W4_E_ALIGN, "out must be 16-byte aligned; scales and bias 2-byte aligned");
+  GemmArgs args{};
+  args.a = a;
+  args.b = static_cast<const uint32_t*>(b_packed);
+  args.s = scales;
+  args.z = zeros_scaled;
+  args.bias = bias;
+  args.out = out;
+  args.M = M;
+  args.N = N;
+  args.K = K;
+  args.G = (int)(K / 128);
+  args.s_dtype = a_dtype;
+  args.out_dtype = a_dtype;
+  args.z_dtype = a_dtype;
+  args.prescaled_zeros = true;
+  args.mode = MODE_OUTPUT;
+  return run_gemm(args, op_of(a_dtype), true, false, workspace, workspace_bytes, stream);
+}
+
 static int check_window(int64_t M, int64_t N, int64_t m0, int64_t m1, int64_t n0, int64_t n1) {
   if (m0 < 0 || m0 > m1 || m1 > M || n0 < 0 || n0 > n1 || n1 > N)
     return fail(W4_E_SHAPE, "window rows [%lld,%lld) cols [%lld,%lld) outside [0,%lld) x [0,%lld)",

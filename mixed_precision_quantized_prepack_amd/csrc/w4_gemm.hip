@@ -136,6 +136,20 @@ __device__ __forceinline__ void mask_words(const uint32_t* e, bool keep, uint32_
   for (int t = 0; t < N; ++t) out[t] = keep ? e[t] : 0u;
 }
 
+// W4A16 with pre-scaled zero-points: the operand holds the raw code (fp16:
+// 1024 + c - 1024; bf16: 128 + c), and each group subtracts zs * sum(a),
+// the activation sum again from a ones-operand.
+template <int OP>
+__device__ __forceinline__ void ones_mma_16(const u32x4* a, f32x4& ones) {
+  if constexpr (OP == OP_BF16) {
+    ones_mma(a, ones);
+  } else {
+    const u32x4 one{0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u};
+#pragma unroll
+    for (int kw = 0; kw < 4; ++kw) ones = mma_f16(one, a[kw], ones);
+  }
+}
+
 // bf16 ones-operand restricted to the lanes that keep it: the activation sum
 // of one sub-group.
 __device__ __forceinline__ void ones_mma_masked(const u32x4* a, bool keep, f32x4& ones) {
@@ -278,7 +292,7 @@ constexpr int waitcnt_vm_lgkm0(int vm) { return (vm & 15) | ((vm >> 4) << 14) | 
 // its D rows for a K block with one 16-byte LDS read, instead of a 64-lane
 // gather from memory per block (which costs the address pipeline as much as
 // the block's weights).  The table's size is set at launch.
-template <int OP, bool GROUPED, bool FLIP, int NS, bool PARTIALS, bool ZP, int SG, bool QA>
+template <int OP, bool GROUPED, bool FLIP, int NS, bool PARTIALS, bool ZP, int SG, bool QA, bool PZ = false>
 __global__ __launch_bounds__(64 * skinny_max_waves(OP, GROUPED)) void w4_gemm_skinny(GemmArgs p, int S) {
   using Acc = typename OpTraits<OP>::Acc;
   constexpr int EB = OpTraits<OP>::kElemBytes;
@@ -298,6 +312,8 @@ __global__ __launch_bounds__(64 * skinny_max_waves(OP, GROUPED)) void w4_gemm_sk
   static_assert(SG == 1 || (GROUPED && (OP == OP_F16 || OP == OP_BF16)), "sub-groups: grouped W4A16 only");
   static_assert(!QA || ((OP == OP_I8 || OP == OP_FP8) && !PARTIALS && !ZP && SG == 1),
                 "fused quantisation: W4A8 outputs only");
+  static_assert(!PZ || ((OP == OP_F16 || OP == OP_BF16) && GROUPED && !PARTIALS && SG == 1),
+                "pre-scaled zero-points: grouped W4A16 outputs only");
 
   const __amdgpu_buffer_rsrc_t rw =
       make_rsrc(reinterpret_cast<const uint8_t*>(p.b) + nb0 * KB * 1024, (int64_t)NS * KB * 1024);
@@ -522,13 +538,14 @@ __global__ __launch_bounds__(64 * skinny_max_waves(OP, GROUPED)) void w4_gemm_sk
         continue;
       }
       const int g = GROUPED ? k : 0;
-      if constexpr (OP == OP_BF16) ones_mma(av[buf][u], ones);
+      if constexpr (OP == OP_BF16 || PZ) ones_mma_16<OP>(av[buf][u], ones);
       if constexpr (ZP) ones_mma_i8(av[buf][u], ones_i);
 #pragma unroll
       for (int j = 0; j < NS; ++j) {
         f16x2 nz = {};
         if constexpr (OP == OP_F16) {
-          const float z = GROUPED ? (k < KB ? tz[(j * p.G + g) * 16 + r] : 8.0f) : zrow[j];
+          // pre-scaled zero-points: the raw code (its zero term comes with the fold)
+          const float z = PZ ? 0.0f : GROUPED ? (k < KB ? tz[(j * p.G + g) * 16 + r] : 8.0f) : zrow[j];
           const _Float16 h = (_Float16)(-(1024.0f + z));
           nz = f16x2{h, h};
         }
@@ -545,19 +562,23 @@ __global__ __launch_bounds__(64 * skinny_max_waves(OP, GROUPED)) void w4_gemm_sk
             const int slot = (j * p.G + g) * 16 + 4 * kq;
             const f32x4 sv = *reinterpret_cast<const f32x4*>(&tsc[slot]);
             f32x4 zc = {};
-            if constexpr (OP == OP_BF16 || ZP) zc = *reinterpret_cast<const f32x4*>(&tz[slot]);
+            if constexpr (OP == OP_BF16 || ZP || PZ) zc = *reinterpret_cast<const f32x4*>(&tz[slot]);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
               // asymmetric int8: 16 * sum(a (u - z)), exact
               int32_t ia = 0;
               if constexpr (OP == OP_I8) ia = ZP ? acc[j][i] - (int32_t)zc[i] * ones_i[i] : acc[j][i];
-              const float pv = ZP ? (float)ia * 0.0625f : partial_value<OP>(acc[j], ones, zc[i], i);
+              // pre-scaled zero-points: sum(a c) here (zc holds zs, taken below)
+              const float pv = ZP ? (float)ia * 0.0625f
+                               : PZ ? fmaf(OP == OP_BF16 ? -128.0f : 0.0f, ones[i], acc[j][i])
+                                    : partial_value<OP>(acc[j], ones, zc[i], i);
               if (partials) {
                 if (in_window(p, r, n_d + i))
                   store_partial<OP>(p, g, r, n_d + i, pv, ZP ? ia >> 4 : int_partial<OP>(acc[j], i));
               } else {
                 const float pf = (OP == OP_I8) ? (float)ia : pv;
                 tot[j][i] = fmaf(pf, sv[i], tot[j][i]);
+                if constexpr (PZ) tot[j][i] = fmaf(-zc[i], ones[i], tot[j][i]);
               }
             }
           }
@@ -604,8 +625,12 @@ __global__ __launch_bounds__(64 * skinny_max_waves(OP, GROUPED)) void w4_gemm_sk
         if constexpr (OP == OP_I8) sv *= 0.0625f;   // the operand holds 16 w
         tsc[slot] = sv;
       }
-      if constexpr (OP == OP_BF16) tz[slot] = 128.0f + (p.z ? word_to_f32(twz[t], zdt, idx) : 8.0f);
-      if constexpr (OP == OP_F16) tz[slot] = p.z ? word_to_f32(twz[t], zdt, idx) : 8.0f;
+      if constexpr (PZ)
+        tz[slot] = word_to_f32(twz[t], zdt, idx);   // zs, the pre-scaled zero term
+      else if constexpr (OP == OP_BF16)
+        tz[slot] = 128.0f + (p.z ? word_to_f32(twz[t], zdt, idx) : 8.0f);
+      else if constexpr (OP == OP_F16)
+        tz[slot] = p.z ? word_to_f32(twz[t], zdt, idx) : 8.0f;
       if constexpr (ZP) tz[slot] = (p.z ? word_to_f32(twz[t], zdt, idx) : 8.0f) - 8.0f;
     }
   };
@@ -817,7 +842,8 @@ __device__ __forceinline__ void stage_barrier() {
   asm volatile("" ::: "memory");
 }
 
-template <int OP, bool GROUPED, bool FLIP, int NT, int MT, bool SPLIT, bool PARTIALS, bool ZP, int SG>
+template <int OP, bool GROUPED, bool FLIP, int NT, int MT, bool SPLIT, bool PARTIALS, bool ZP, int SG,
+          bool PZ = false>
 __global__ __launch_bounds__(256, 2) void w4_gemm_tiled(GemmArgs p, int splitk) {
   using Acc = typename OpTraits<OP>::Acc;
   constexpr int EB = OpTraits<OP>::kElemBytes;
@@ -837,7 +863,9 @@ __global__ __launch_bounds__(256, 2) void w4_gemm_tiled(GemmArgs p, int splitk) 
   // loads of later stages.
   constexpr bool kFold = GROUPED && !PARTIALS;
   constexpr int BNW = 4 * NT * 16;   // columns of the workgroup
-  constexpr int kTables = kFold ? ((OP == OP_BF16 || ZP) ? 2 : 1) : 0;
+  constexpr int kTables = kFold ? ((OP == OP_BF16 || ZP || PZ) ? 2 : 1) : 0;
+  static_assert(!PZ || ((OP == OP_F16 || OP == OP_BF16) && GROUPED && !PARTIALS && SG == 1),
+                "pre-scaled zero-points: grouped W4A16 outputs only");
   static_assert(!ZP || (OP == OP_I8 && FLIP), "zero-points: int8 operand from raw uint4 codes");
   static_assert(SG == 1 || (GROUPED && (OP == OP_F16 || OP == OP_BF16)), "sub-groups: grouped W4A16 only");
   __shared__ __attribute__((aligned(1024))) uint8_t lds[3 * STAGE + kTables * 2 * SG * BNW * 4];
@@ -917,7 +945,7 @@ __global__ __launch_bounds__(256, 2) void w4_gemm_tiled(GemmArgs p, int splitk) 
             x.zd[nt][i] = load_word(rz, zdt, n * p.G + kb, kb < kb1 && p.z);
           }
         }
-        if constexpr (OP == OP_F16)
+        if constexpr (OP == OP_F16 && !PZ)
           x.wz[nt] = load_word(rz, zdt, (uint32_t)(((nb_base + nt) * 16 + r) * p.G + kb * SG + lane_subgroup<SG>(kq)),
                                kb < kb1 && p.z);
       }
@@ -973,7 +1001,7 @@ __global__ __launch_bounds__(256, 2) void w4_gemm_tiled(GemmArgs p, int splitk) 
       for (int sg = 0; sg < SG; ++sg) {
         const uint32_t idx = col_n * (uint32_t)p.G + (uint32_t)(kb * SG + sg);
         col_sw[sg] = load_word(rs, p.s_dtype, idx, kb < kb1 && col_n < (uint32_t)p.N);
-        if constexpr (OP == OP_BF16 || ZP)
+        if constexpr (OP == OP_BF16 || ZP || PZ)
           col_zw[sg] = load_word(rz, zdt, idx, kb < kb1 && p.z && col_n < (uint32_t)p.N);
       }
     }
@@ -988,7 +1016,10 @@ __global__ __launch_bounds__(256, 2) void w4_gemm_tiled(GemmArgs p, int splitk) 
         float sv = word_to_f32(col_sw[sg], p.s_dtype, idx);
         if constexpr (OP == OP_I8) sv *= 0.0625f;
         gsc[at] = sv;
-        if constexpr (OP == OP_BF16) gzc[at] = 128.0f + (p.z ? word_to_f32(col_zw[sg], zdt, idx) : 8.0f);
+        if constexpr (PZ)
+          gzc[at] = word_to_f32(col_zw[sg], zdt, idx);   // zs, the pre-scaled zero term
+        else if constexpr (OP == OP_BF16)
+          gzc[at] = 128.0f + (p.z ? word_to_f32(col_zw[sg], zdt, idx) : 8.0f);
         if constexpr (ZP) gzc[at] = (p.z ? word_to_f32(col_zw[sg], zdt, idx) : 8.0f) - 8.0f;
       }
     }
@@ -1007,7 +1038,10 @@ __global__ __launch_bounds__(256, 2) void w4_gemm_tiled(GemmArgs p, int splitk) 
     for (int nt = 0; nt < NT; ++nt) {
       f16x2 nz = {};
       if constexpr (OP == OP_F16) {
-        if constexpr (GROUPED) {
+        if constexpr (PZ) {
+          const _Float16 h = (_Float16)(-1024.0f);   // the raw code; the zero term comes with the fold
+          nz = f16x2{h, h};
+        } else if constexpr (GROUPED) {
           const uint32_t zi = (uint32_t)(((nb_base + nt) * 16 + r) * p.G + kb * SG + lane_subgroup<SG>(kq));
           const _Float16 h = (_Float16)(-(1024.0f + (p.z ? word_to_f32(x.wz[nt], zdt, zi) : 8.0f)));
           nz = f16x2{h, h};
@@ -1083,7 +1117,7 @@ __global__ __launch_bounds__(256, 2) void w4_gemm_tiled(GemmArgs p, int splitk) 
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         scv[nt] = *reinterpret_cast<const f32x4*>(&gsc[slot * BNW + (wave * NT + nt) * 16 + 4 * kq]);
-        if constexpr (OP == OP_BF16 || ZP)
+        if constexpr (OP == OP_BF16 || ZP || PZ)
           zcv[nt] = *reinterpret_cast<const f32x4*>(&gzc[slot * BNW + (wave * NT + nt) * 16 + 4 * kq]);
       }
       // Row mt's MFMAs start from zero; row mt - 1 is folded while they run.
@@ -1095,11 +1129,14 @@ __global__ __launch_bounds__(256, 2) void w4_gemm_tiled(GemmArgs p, int splitk) 
             pv = (float)(acc[nt][mt][i] - (int32_t)zcv[nt][i] * onesi[mt][i]);
           else if constexpr (OP == OP_I8)
             pv = (float)acc[nt][mt][i];
+          else if constexpr (PZ)
+            pv = fmaf(OP == OP_BF16 ? -128.0f : 0.0f, ones[mt][i], acc[nt][mt][i]);
           else if constexpr (OP == OP_BF16)
             pv = fmaf(-zcv[nt][i], ones[mt][i], acc[nt][mt][i]);
           else
             pv = acc[nt][mt][i];
           tot[nt][mt][i] = fmaf(pv, scv[nt][i], tot[nt][mt][i]);
+          if constexpr (PZ) tot[nt][mt][i] = fmaf(-zcv[nt][i], ones[mt][i], tot[nt][mt][i]);
         }
       };
       // Issue order, pinned: per tile row, the fragment reads of row mt + 2,
@@ -1113,9 +1150,9 @@ __global__ __launch_bounds__(256, 2) void w4_gemm_tiled(GemmArgs p, int splitk) 
           Acc t = Acc{};
           block_mma<OP>(e[nt], af[mt], t);
           acc[nt][mt] = t;
-          if (nt == NT - 1 && OP == OP_BF16) {
+          if (nt == NT - 1 && (OP == OP_BF16 || PZ)) {
             f32x4 o = f32x4{};
-            ones_mma(af[mt], o);
+            ones_mma_16<OP>(af[mt], o);
             ones[mt] = o;
           }
           if (nt == NT - 1 && ZP) {
@@ -1359,7 +1396,7 @@ void tiled_tile(int op, bool grouped, int tall, int* bm, int* bn, bool zp) {
   }
 }
 
-template <int OP, bool GROUPED, bool FLIP, bool ZP = false, int SG = 1>
+template <int OP, bool GROUPED, bool FLIP, bool ZP = false, int SG = 1, bool PZ = false>
 static hipError_t launch_typed(const GemmArgs& args, const GemmPlan& plan, hipStream_t stream) {
   if (plan.path == PATH_SKINNY) {
     // S waves split K; at least 4 NS waves are launched so that every output
@@ -1389,12 +1426,12 @@ static hipError_t launch_typed(const GemmArgs& args, const GemmPlan& plan, hipSt
       if (part)
         hipLaunchKernelGGL((w4_gemm_skinny<OP, GROUPED, FLIP, 2, true, ZP, SG, false>), grid, dim3(threads), tab, stream, args, S);
       else
-        hipLaunchKernelGGL((w4_gemm_skinny<OP, GROUPED, FLIP, 2, false, ZP, SG, false>), grid, dim3(threads), tab, stream, args, S);
+        hipLaunchKernelGGL((w4_gemm_skinny<OP, GROUPED, FLIP, 2, false, ZP, SG, false, PZ>), grid, dim3(threads), tab, stream, args, S);
     } else {
       if (part)
         hipLaunchKernelGGL((w4_gemm_skinny<OP, GROUPED, FLIP, 1, true, ZP, SG, false>), grid, dim3(threads), tab, stream, args, S);
       else
-        hipLaunchKernelGGL((w4_gemm_skinny<OP, GROUPED, FLIP, 1, false, ZP, SG, false>), grid, dim3(threads), tab, stream, args, S);
+        hipLaunchKernelGGL((w4_gemm_skinny<OP, GROUPED, FLIP, 1, false, ZP, SG, false, PZ>), grid, dim3(threads), tab, stream, args, S);
     }
     return hipGetLastError();
   }
@@ -1423,14 +1460,14 @@ static hipError_t launch_typed(const GemmArgs& args, const GemmPlan& plan, hipSt
         hipLaunchKernelGGL((w4_gemm_tiled<OP, GROUPED, FLIP, NT, MT, true, true, ZP, SG>), grid, dim3(256), 0, stream,
                            args, plan.splitk);
       else
-        hipLaunchKernelGGL((w4_gemm_tiled<OP, GROUPED, FLIP, NT, MT, true, false, ZP, SG>), grid, dim3(256), 0, stream,
+        hipLaunchKernelGGL((w4_gemm_tiled<OP, GROUPED, FLIP, NT, MT, true, false, ZP, SG, PZ>), grid, dim3(256), 0, stream,
                            args, plan.splitk);
     } else {
       if (part)
         hipLaunchKernelGGL((w4_gemm_tiled<OP, GROUPED, FLIP, NT, MT, false, true, ZP, SG>), grid, dim3(256), 0, stream,
                            args, 1);
       else
-        hipLaunchKernelGGL((w4_gemm_tiled<OP, GROUPED, FLIP, NT, MT, false, false, ZP, SG>), grid, dim3(256), 0, stream,
+        hipLaunchKernelGGL((w4_gemm_tiled<OP, GROUPED, FLIP, NT, MT, false, false, ZP, SG, PZ>), grid, dim3(256), 0, stream,
                            args, 1);
     }
   };
@@ -1475,6 +1512,11 @@ hipError_t launch_gemm(const GemmArgs& args, int op, bool grouped, bool flip, bo
     default: {
       // W4A16 groups of 128, 64 or 32: 1, 2 or 4 groups per 128-deep block
       const int64_t sg = grouped ? 128 * (int64_t)args.G / args.K : 1;
+      if (args.prescaled_zeros) {   // groups of 128 only (the API admits no other)
+        if (!grouped || sg != 1 || args.mode != MODE_OUTPUT) return hipErrorInvalidValue;
+        return op == OP_F16 ? launch_typed<OP_F16, true, false, false, 1, true>(args, plan, stream)
+                            : launch_typed<OP_BF16, true, false, false, 1, true>(args, plan, stream);
+      }
       if (op == OP_F16) {
         if (!grouped) return launch_typed<OP_F16, false, false>(args, plan, stream);
         return sg == 4 ? launch_typed<OP_F16, true, false, false, 4>(args, plan, stream)

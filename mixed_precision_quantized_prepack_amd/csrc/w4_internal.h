@@ -34,6 +34,9 @@ struct GemmArgs {
   const void* x;
   int x_dtype;
   float* a_scales_out;
+  // W4A16 with pre-scaled zero-points: z holds zs (in the activation dtype),
+  // subtracted after the scale
+  bool prescaled_zeros;
   int mode;                // Mode
   int64_t m0, m1, n0, n1;  // partials window
 };

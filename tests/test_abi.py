@@ -179,6 +179,22 @@ def test_w4a8_quant_fused_validation(lib):
     assert call(M=0) == W4_OK
 
 
+def test_w4a16_prescaled_validation(lib):
+    f = lib.w4a16_gemm_prescaled_zeros
+
+    def call(a=FAKE, a_dtype=1, b=FAKE, s=FAKE, z=FAKE, gs=128, out=FAKE, M=2, N=32, K=256):
+        return f(a, a_dtype, b, s, z, gs, None, out, M, N, K, None, 0, None)
+    assert call(a_dtype=3) == E_DTYPE
+    assert call(z=None) == E_NULL
+    assert call(s=None) == E_NULL
+    assert call(gs=64) == E_GROUP
+    assert call(gs=-1) == E_GROUP
+    assert call(K=128) == E_GROUP                          # one group: per channel
+    assert call(N=8) == E_SHAPE
+    assert call(out=MISALIGNED) == E_ALIGN
+    assert call(M=0) == W4_OK
+
+
 def test_w4a8_zp_validation(lib):
     f = lib.w4a8_gemm_zp
 
