@@ -63,6 +63,14 @@ def test_small_group_outputs(a_dtype, gs, M):
 
 
 @pytest.mark.parametrize("gs", [64, 32])
+@pytest.mark.parametrize("M", [3, 40])
+def test_small_group_single_block(gs, M):
+    """K = 128: one block holding 2 or 4 groups, on both kernels."""
+    c = Case(M, 64, 128, gs, "f16", seed=M + gs, bias=True)
+    assert_w4a16(c.run(), c.oracle(), "f16", label=f"W4A16 K=128 g{gs} M={M}")
+
+
+@pytest.mark.parametrize("gs", [64, 32])
 def test_small_group_without_zero_points(gs):
     c = Case(8, 256, 512, gs, "bf16", seed=gs, zeros=False)
     assert_w4a16(c.run(), c.oracle(), "bf16", label=f"W4A16 g{gs} z=8")
