@@ -6,7 +6,6 @@ import pytest
 import torch
 
 import mixed_precision_quantized_prepack_amd as w4
-import workloads
 from oracle import w4_oracle as O
 from tests.parity import DEV, DeviceCase, assert_w4a8, bits16
 

@@ -5,13 +5,10 @@
   integer z), zs = z * s gives the raw zero-point GEMM's result bit for bit.
 * zs = 0 gives the GEMM of u * s; doubling s and zs doubles the exact value.
 """
-from fractions import Fraction
 
 import numpy as np
-import pytest
 import torch
 
-from oracle import formats as F
 from oracle import w4_oracle as O
 from tests import exact as X
 

@@ -14,7 +14,6 @@ import numpy as np
 import pytest
 import torch
 
-import workloads
 from oracle import formats as F
 from oracle import w4_oracle as O
 
