@@ -101,11 +101,20 @@ def test_fp8_partials_within_bound(path, M, split, bm):
     P = O.w4a8_group_partials(codes, "fp8", dc.case.w_logical.numpy(), dc.K, "int4", 128)
     exact = P * 2.0 ** -9
     A = np.abs(O.activation_integers(codes, "fp8")).astype(np.float64) * 2.0 ** -9
-    W = np.abs(O.weight_values(dc.case.w_logical.numpy(), dc.K, "int4")).astype(np.float64)
+    wv = O.weight_values(dc.case.w_logical.numpy(), dc.K, "int4").astype(np.int64)
+    if path == 1:
+        # the small-M kernel writes w = (8 + l) - 8 (1 + s) (l = w mod 8,
+        # s = [w < 0]) and sums both operands' 256 exact products into one
+        # fp32 accumulator: within gamma_256 * (sum|a| (8 + l) + sum|a| 8 (1 + s))
+        W = (8 + (wv & 7) + 8 * (1 + (wv < 0))).astype(np.float64)
+        n = 256
+    else:
+        # the MFMA sums 128 exact products in fp32 in an order of its own: the
+        # result may round, within gamma_128 * sum|a w|
+        W = np.abs(wv).astype(np.float64)
+        n = 128
     bound = np.stack([A[:, g * 128:(g + 1) * 128] @ W[:, g * 128:(g + 1) * 128].T for g in range(dc.G)])
-    # the MFMA sums 128 exact products in fp32 in an order of its own: the
-    # result may round, within gamma_128 * sum|a w|
-    assert np.all(np.abs(part - exact) <= 128 * 2.0 ** -24 * bound)
+    assert np.all(np.abs(part - exact) <= n * 2.0 ** -24 * bound)
 
 
 @pytest.mark.parametrize("a_dtype", ["bf16", "f16"])
