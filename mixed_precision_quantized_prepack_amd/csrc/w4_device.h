@@ -67,25 +67,6 @@ __device__ __forceinline__ void expand_fp8(uint32_t w, uint32_t& k0123, uint32_t
   k4567 = __builtin_amdgcn_perm(n_hi, p_hi, pick_hi);
 }
 
-// 4-bit -> fp8 e4m3fn as two operands whose products sum to a*w, for kernels
-// whose MFMA pipe is mostly idle (small M).  A two's-complement int4 is
-// w = (8 + l) - 8 (1 + s), with l its low three bits and s its sign bit.
-// 8 + l is the e4m3fn code with exponent 3 and mantissa l (0x50 | l), and
-// -8 (1 + s) is -8 or -16 (0xD0 | s << 3).  Two MFMAs into one accumulator
-// give sum(a w) from five VALU ops per eight weights instead of the lookup's
-// thirteen.  Between the two MFMAs the fp32 accumulator holds a sum of terms
-// up to 15 |a|, so its rounding is relative to sum |a| (8 + l) + 8 |a| (1 + s)
-// rather than to sum |a w|.
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ void expand_fp8_split(uint32_t w, uint32_t& m0123, uint32_t& m4567, uint32_t& s0123,
-                                                 uint32_t& s4567) {
-  const uint32_t wh = w >> 4;
-  m0123 = (w & 0x07070707u) | 0x50505050u;
-  m4567 = (wh & 0x07070707u) | 0x50505050u;
-  s0123 = (w & 0x08080808u) | 0xD0D0D0D0u;
-  s4567 = (wh & 0x08080808u) | 0xD0D0D0D0u;
-}
-
 // ---------------------------------------------------------------------------
 // 4-bit -> fp16 / bf16 expansion (F16 operand class, ExLlama pair order).
 //

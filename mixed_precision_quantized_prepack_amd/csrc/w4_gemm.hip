@@ -62,19 +62,14 @@ constexpr int act_vecs() {
   return OpTraits<OP>::kElemBytes * 2;  // 32 bytes (8-bit) or 64 bytes (16-bit)
 }
 
-// Expand one lane's four packed words into MFMA operand words.  SPLIT (fp8
-// only): e[0..7] hold the 8 + l operand and e[8..15] the -8 (1 + s) operand
-// of expand_fp8_split, which block_mma<OP, true> feeds to two MFMAs.
-template <int OP, bool FLIP, bool SPLIT = false>
+// Expand one lane's four packed words into MFMA operand words.
+template <int OP, bool FLIP>
 __device__ __forceinline__ void expand_weights(const u32x4 w, const f16x2 nz, uint32_t e[16]) {
-  static_assert(!SPLIT || OP == OP_FP8, "the split expansion is an fp8 form");
   const uint32_t q[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     if constexpr (OP == OP_I8) {
       expand_i8x16(FLIP ? (q[j] ^ 0x88888888u) : q[j], e[2 * j], e[2 * j + 1]);
-    } else if constexpr (OP == OP_FP8 && SPLIT) {
-      expand_fp8_split(FLIP ? (q[j] ^ 0x88888888u) : q[j], e[2 * j], e[2 * j + 1], e[8 + 2 * j], e[9 + 2 * j]);
     } else if constexpr (OP == OP_FP8) {
       expand_fp8(FLIP ? (q[j] ^ 0x88888888u) : q[j], e[2 * j], e[2 * j + 1]);
     } else {
@@ -87,16 +82,15 @@ __device__ __forceinline__ void expand_weights(const u32x4 w, const f16x2 nz, ui
   }
 }
 
-template <int OP, bool SPLIT = false>
+template <int OP>
 __device__ __forceinline__ void block_mma(const uint32_t e[16], const u32x4* a,
                                           typename OpTraits<OP>::Acc& acc) {
   if constexpr (OP == OP_I8) {
     acc = mma_i8(u32x4{e[0], e[1], e[2], e[3]}, a[0], acc);
     acc = mma_i8(u32x4{e[4], e[5], e[6], e[7]}, a[1], acc);
   } else if constexpr (OP == OP_FP8) {
-    const u32x8 av{a[0].x, a[0].y, a[0].z, a[0].w, a[1].x, a[1].y, a[1].z, a[1].w};
-    acc = mma_fp8(u32x8{e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]}, av, acc);
-    if constexpr (SPLIT) acc = mma_fp8(u32x8{e[8], e[9], e[10], e[11], e[12], e[13], e[14], e[15]}, av, acc);
+    acc = mma_fp8(u32x8{e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]},
+                  u32x8{a[0].x, a[0].y, a[0].z, a[0].w, a[1].x, a[1].y, a[1].z, a[1].w}, acc);
   } else {
 #pragma unroll
     for (int kw = 0; kw < 4; ++kw) {
@@ -305,10 +299,6 @@ __global__ __launch_bounds__(64 * skinny_max_waves(OP, GROUPED)) void w4_gemm_sk
   constexpr int AV = act_vecs<OP>();
   constexpr int U = GROUPED ? (NS == 1 ? W4_SKINNY_UG1 : W4_SKINNY_UG2)
                             : (EB == 1) ? W4_SKINNY_U8 : W4_SKINNY_U16;   // K blocks per batch
-  // grouped fp8: the MFMA pipe is nearly idle at small M, so each weight
-  // block takes the five-op split expansion and two MFMAs instead of the
-  // table lookup (per channel it measured slower at M = 16)
-  constexpr bool kSplitFp8 = OP == OP_FP8 && GROUPED;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -560,8 +550,8 @@ __global__ __launch_bounds__(64 * skinny_max_waves(OP, GROUPED)) void w4_gemm_sk
           nz = f16x2{h, h};
         }
         uint32_t e[16];
-        expand_weights<OP, FLIP, kSplitFp8>(wv[buf][u][j], nz, e);
-        block_mma<OP, kSplitFp8>(e, av[buf][u], acc[j]);
+        expand_weights<OP, FLIP>(wv[buf][u][j], nz, e);
+        block_mma<OP>(e, av[buf][u], acc[j]);
       }
       if constexpr (GROUPED) {
         if (k < KB) {

@@ -14,12 +14,6 @@ Acceptance rules
   the split-K sums, the final scale and bias; plus the 128-term MFMA sums for
   the fp32-accumulating paths).  The second clause only matters for bf16
   outputs, whose half-ulp (up to 2**-8 relative) exceeds 2e-3.
-  The grouped fp8 small-M kernel sums two operands per weight, 8 + l and
-  -8 (1 + s), so its fp32 roundings are relative to sum|a| (8 + l + 8 (1 + s))
-  instead of sum|a w|: about 8 times larger on uniform int4 weights, which the
-  128 counted MFMA roundings cover many times over (each MFMA rounds a few
-  times at most).  Its group partials have an exact bound of their own
-  (test_fp8_partials_within_bound).
 * W4A16 outputs: |gpu - ref| <= 1e-2 * max|ref| over the whole output.
 """
 from __future__ import annotations

@@ -101,20 +101,11 @@ def test_fp8_partials_within_bound(path, M, split, bm):
     P = O.w4a8_group_partials(codes, "fp8", dc.case.w_logical.numpy(), dc.K, "int4", 128)
     exact = P * 2.0 ** -9
     A = np.abs(O.activation_integers(codes, "fp8")).astype(np.float64) * 2.0 ** -9
-    wv = O.weight_values(dc.case.w_logical.numpy(), dc.K, "int4").astype(np.int64)
-    if path == 1:
-        # the small-M kernel writes w = (8 + l) - 8 (1 + s) (l = w mod 8,
-        # s = [w < 0]) and sums both operands' 256 exact products into one
-        # fp32 accumulator: within gamma_256 * (sum|a| (8 + l) + sum|a| 8 (1 + s))
-        W = (8 + (wv & 7) + 8 * (1 + (wv < 0))).astype(np.float64)
-        n = 256
-    else:
-        # the MFMA sums 128 exact products in fp32 in an order of its own: the
-        # result may round, within gamma_128 * sum|a w|
-        W = np.abs(wv).astype(np.float64)
-        n = 128
+    W = np.abs(O.weight_values(dc.case.w_logical.numpy(), dc.K, "int4")).astype(np.float64)
     bound = np.stack([A[:, g * 128:(g + 1) * 128] @ W[:, g * 128:(g + 1) * 128].T for g in range(dc.G)])
-    assert np.all(np.abs(part - exact) <= n * 2.0 ** -24 * bound)
+    # the MFMA sums 128 exact products in fp32 in an order of its own: the
+    # result may round, within gamma_128 * sum|a w|
+    assert np.all(np.abs(part - exact) <= 128 * 2.0 ** -24 * bound)
 
 
 @pytest.mark.parametrize("a_dtype", ["bf16", "f16"])
@@ -250,6 +241,29 @@ def test_zero_weights_and_identity():
     dc.w_logical = torch.zeros_like(dc.w_logical)
     out, *_ = run_w4a8(dc)
     assert torch.count_nonzero(out) == 0
+
+
+@pytest.mark.parametrize("path", [1, 2])
+def test_fp8_grouped_zero_weights_identity_and_extremes(path):
+    """Grouped fp8 on both kernels with unit scales: identity weights give the
+    dequantised codes, zero weights give zero, weights of -8 give -8 times the
+    dequantised codes, bit for bit.  Each output then has one nonzero product
+    per group, which the MFMA's fp8 accumulation keeps exactly.  (An int4 ->
+    e4m3 expansion as two operands, 8 + l and -8 (1 + s), failed this: next to
+    the large 8a terms the accumulation dropped low-order bits of the small
+    ones, errors of 1e-3 on outputs of 5e-3.)"""
+    dc = DeviceCase("w4a8_fp8_g128_28672x8192", 9, N=256, K=256, seed_base=5)
+    dc.case.w_scales = torch.ones((256, 2), dtype=torch.float32)
+    dc.w_scales = dc.case.w_scales.to(DEV)
+    dc.case.bias = None
+    dc.bias = None
+    eye = torch.eye(256, dtype=torch.int16)
+    for mult in (1, 0, -8):
+        dc.w_logical = workloads.store_nibbles(mult * eye).to(DEV)
+        with options(path):
+            out, aq, sa, _ = run_w4a8(dc)
+        deq = aq.cpu().view(torch.float8_e4m3fn).float() * sa.cpu()[:, None]
+        assert torch.equal(out.cpu(), (mult * deq).to(torch.bfloat16)), f"weights {mult} * I"
 
 
 # ---------------------------------------------------------------------------
