@@ -243,6 +243,30 @@ def test_zero_weights_and_identity():
     assert torch.count_nonzero(out) == 0
 
 
+@pytest.mark.parametrize("wl", ["w4a8_i8_pc_256x512", "w4a8_fp8_g128_28672x8192", "w4a8_i8_g128_down"])
+@pytest.mark.parametrize("path,split,bm", [(1, 1, 0), (1, 8, 0), (2, 1, 64), (2, 5, 64), (2, 3, 128)])
+@pytest.mark.parametrize("sparse", [False, True])
+def test_w4a8_within_rounding_bound(wl, path, split, bm, sparse):
+    """Every output within the rounding bound of its own terms (the strict
+    clause alone), on both kernels, with dense weights and with 15 of 16
+    weights zero (small outputs, where the absolute 1e-3 of the tolerance
+    would hide errors)."""
+    M = 16 if path == 1 else (48 if bm == 64 else 150)
+    dc = DeviceCase(wl, M, N=272, K=1024, seed_base=78)
+    if sparse:
+        keep = torch.Generator().manual_seed(79)
+        mask = torch.rand(dc.N, dc.K, generator=keep) < 1 / 16
+        vals = O.weight_values(dc.case.w_logical.numpy(), dc.K, dc.wtype)
+        vals = torch.from_numpy(vals).to(torch.int16) * mask
+        dc.case.w_logical = workloads.store_nibbles(vals)
+        dc.w_logical = dc.case.w_logical.to(DEV)
+    with options(path, split, bm):
+        out, *_ = run_w4a8(dc)
+    codes, sa = dc.oracle_quant()
+    assert_w4a8(out, dc.oracle_w4a8(codes, sa), dc.wl.out_dtype, dc.wl.q_dtype, dc.G, strict=True,
+                label=f"{wl} path={path} split={split} bm={bm} sparse={sparse}")
+
+
 @pytest.mark.parametrize("path", [1, 2])
 def test_fp8_grouped_zero_weights_identity_and_extremes(path):
     """Grouped fp8 on both kernels with unit scales: identity weights give the
