@@ -202,6 +202,57 @@ def test_w4a16_outputs(a_dtype, M, zeros, group):
     assert_w4a16(out, ref, a_dtype, label=f"W4A16 {a_dtype} M={M}")
 
 
+@pytest.mark.parametrize("a_dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("path,M", [(1, 8), (2, 100)])
+@pytest.mark.parametrize("sparse", [False, True])
+def test_w4a16_within_rounding_bound(a_dtype, path, M, sparse):
+    """Every W4A16 output within a rounding bound of its own (stricter than
+    the 1e-2 * max|ref| contract), dense and with 15 of 16 codes equal to
+    their zero-point.  The fp16 operand is the exact c - z, so the MFMA
+    rounds relative to sum|a (c - z)|.  The bf16 operand is 128 + c and the
+    (128 + z) * sum(a) term is subtracted after the MFMAs, so they round
+    relative to sum|a| (128 + c) + (128 + z) sum|a|.  Either way the output
+    is a correct rounding of a value within n * 2**-24 * (that magnitude,
+    weighted by |s|) of the exact result, n = 128 MFMA terms + 2 per group
+    for the fold + 24 for split sums and the final steps."""
+    dc = DeviceCase("w4a16_bf16_g128_4096x4096", M, N=272, K=1024, seed_base=82)
+    c = dc.case
+    codes = O.weight_values(c.w_logical.numpy(), dc.K, "uint4")             # [N, K] in 0..15
+    zg = F.decode(bits16(c.zeros), "bf16")                                 # [N, G]
+    if sparse:
+        keep = (torch.rand(dc.N, dc.K, generator=torch.Generator().manual_seed(83)) < 1 / 16).numpy()
+        codes = np.where(keep, codes, np.repeat(zg, 128, axis=1).astype(np.int64))
+        c.w_logical = workloads.store_nibbles(torch.from_numpy(codes).to(torch.int16))
+        dc.w_logical = c.w_logical.to(DEV)
+    tdt = torch.bfloat16 if a_dtype == "bf16" else torch.float16
+    if a_dtype == "f16":
+        c.a = c.a.float().to(tdt)
+        c.w_scales = c.w_scales.float().to(tdt)
+        c.zeros = c.zeros.float().to(tdt)
+        dc.wl = workloads.Workload(**{**dc.wl.__dict__, "a_dtype": "f16", "out_dtype": "f16"})
+    with options(path):
+        out = w4.w4a16_gemm(c.a.to(DEV), w4.prepack_B(dc.w_logical, "f16"), c.w_scales.to(DEV),
+                            c.zeros.to(DEV), 128)
+    ref = dc.oracle_w4a16()
+    av = np.abs(F.decode(bits16(c.a), a_dtype))                            # [M, K]
+    sv = np.abs(F.decode(bits16(c.w_scales), a_dtype))                     # [N, G]
+    mag = np.zeros((M, dc.N))
+    for g in range(dc.G):
+        ks = slice(g * 128, (g + 1) * 128)
+        if a_dtype == "f16":
+            t = av[:, ks] @ np.abs(codes[:, ks] - zg[:, g:g + 1]).T
+        else:
+            t = av[:, ks] @ (128.0 + codes[:, ks]).T + av[:, ks].sum(axis=1, keepdims=True) * (128.0 + zg[:, g])
+        mag += t * sv[:, g]
+    E = (128 + 2 * dc.G + 24) * 2.0 ** -24 * mag
+    got = F.decode(bits16(out), a_dtype)
+    lo = F.round_to_format(ref["exact"] - E, a_dtype)
+    hi = F.round_to_format(ref["exact"] + E, a_dtype)
+    bad = ~((got >= lo) & (got <= hi))
+    assert not bad.any(), (f"{int(bad.sum())} outside; first "
+                           f"{[(tuple(i), float(got[tuple(i)]), float(ref['exact'][tuple(i)])) for i in np.argwhere(bad)[:3]]}")
+
+
 def test_w4a16_uint4b8_equals_zero_point_8():
     dc = DeviceCase("w4a16_bf16_g128_4096x4096", 8, N=256, K=512, seed_base=5, zeros=False)
     packed = w4.prepack_B(dc.w_logical, "f16")
