@@ -286,8 +286,9 @@ W4_API int w4a16_gemm_prescaled_zeros(const void* a, int a_dtype, const void* b_
  * q_dtype     : W4_I8 or W4_FP8_E4M3 (the activation codes).
  * a_scales_out: device, [M] fp32, receives the per-token scales, or NULL.
  * Other arguments as w4a8_gemm.  Supported where the problem takes the
- * small-M kernel (M <= 16) and the M*K codes fit its LDS (M*K + tables below
- * about 32 KiB); otherwise W4_E_UNSUPPORTED, and the two calls are the way.
+ * small-M kernel (M <= 16) and the M*K codes fit its LDS (M*K codes plus the
+ * scale tables and the reduction buffer at most 64 KiB); otherwise
+ * W4_E_UNSUPPORTED, and the two calls are the way.
  * No workspace.  Errors as w4a8_gemm, plus W4_E_UNSUPPORTED.
  * ------------------------------------------------------------------------- */
 W4_API int w4a8_gemm_quant_fused(const void* x, int x_dtype, int q_dtype, const void* b_packed, int wtype,

@@ -143,16 +143,18 @@ def _dtype_code(dt) -> int:
 
 
 def _workspace(ws, nbytes: int, device):
+    """(pointer, size, tensor) of the split-K workspace.  The caller keeps the
+    returned tensor alive until the C call has queued its kernels; after that
+    the caching allocator hands the block only to work queued later on the
+    same stream, which runs after them."""
     if nbytes == 0:
-        return None, 0
+        return None, 0, None
     if ws is not None:
         if ws.numel() * ws.element_size() < nbytes:
             raise ValueError(f"workspace needs {nbytes} bytes")
-        return _dev_ptr(ws, "workspace"), ws.numel() * ws.element_size()
-    # Freed when the caller drops it; the caching allocator only reuses the
-    # block for work queued after this call on the same stream.
+        return _dev_ptr(ws, "workspace"), ws.numel() * ws.element_size(), ws
     t = _torch().empty(nbytes, dtype=_torch().uint8, device=device)
-    return _dev_ptr(t, "workspace"), nbytes
+    return _dev_ptr(t, "workspace"), nbytes, t
 
 
 def prepack_B_bytes(N: int, K: int) -> int:
@@ -285,7 +287,7 @@ def w4a8_gemm(aq, a_scales, b_packed, b_scales, group_size: int, out_dtype, wtyp
     o_dt = _dtype_code(out_dtype)
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=aq.device)
-    wsp, wsb = _workspace(workspace, gemm_workspace_bytes(M, N, K, group_size, a_dt), aq.device)
+    wsp, wsb, ws_keep = _workspace(workspace, gemm_workspace_bytes(M, N, K, group_size, a_dt), aq.device)
     _check("w4a8_gemm", lib().w4a8_gemm(
         _dev_ptr(aq, "aq"), a_dt, _dev_ptr(a_scales, "a_scales"), _dev_ptr(b_packed, "b_packed"),
         WTYPES[wtype], _dev_ptr(b_scales, "b_scales"), _dtype_code(b_scales.dtype), group_size,
@@ -323,7 +325,7 @@ def w4a8_gemm_zp(aq, a_scales, b_packed, b_scales, zeros, group_size: int, out_d
         raise ValueError("aq must be int8 codes")
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=aq.device)
-    wsp, wsb = _workspace(workspace, gemm_workspace_bytes(M, N, K, group_size, I8), aq.device)
+    wsp, wsb, ws_keep = _workspace(workspace, gemm_workspace_bytes(M, N, K, group_size, I8), aq.device)
     _check("w4a8_gemm_zp", lib().w4a8_gemm_zp(
         _dev_ptr(aq, "aq"), _dev_ptr(a_scales, "a_scales"), _dev_ptr(b_packed, "b_packed"),
         _dev_ptr(b_scales, "b_scales"), _dtype_code(b_scales.dtype), _dev_ptr(zeros, "zeros"),
@@ -342,7 +344,7 @@ def w4a16_gemm_prescaled_zeros(a, b_packed, scales, zeros_scaled, group_size: in
     a_dt = _dtype_code(a.dtype)
     if out is None:
         out = torch.empty((M, N), dtype=a.dtype, device=a.device)
-    wsp, wsb = _workspace(workspace, gemm_workspace_bytes(M, N, K, group_size, a_dt), a.device)
+    wsp, wsb, ws_keep = _workspace(workspace, gemm_workspace_bytes(M, N, K, group_size, a_dt), a.device)
     _check("w4a16_gemm_prescaled_zeros", lib().w4a16_gemm_prescaled_zeros(
         _dev_ptr(a, "a"), a_dt, _dev_ptr(b_packed, "b_packed"), _dev_ptr(scales, "scales"),
         _dev_ptr(zeros_scaled, "zeros_scaled"), group_size, _dev_ptr(bias, "bias"), _dev_ptr(out, "out"),
@@ -360,7 +362,7 @@ def w4a16_gemm(a, b_packed, scales, zeros=None, group_size: int = 128, wtype: st
     a_dt = _dtype_code(a.dtype)
     if out is None:
         out = torch.empty((M, N), dtype=a.dtype, device=a.device)
-    wsp, wsb = _workspace(workspace, gemm_workspace_bytes(M, N, K, group_size, a_dt), a.device)
+    wsp, wsb, ws_keep = _workspace(workspace, gemm_workspace_bytes(M, N, K, group_size, a_dt), a.device)
     _check("w4a16_gemm", lib().w4a16_gemm(
         _dev_ptr(a, "a"), a_dt, _dev_ptr(b_packed, "b_packed"), WTYPES[wtype], _dev_ptr(scales, "scales"),
         _dev_ptr(zeros, "zeros"), group_size, _dev_ptr(bias, "bias"), _dev_ptr(out, "out"), M, N, K,
@@ -383,7 +385,7 @@ def w4a8_gemm_partials(aq, b_packed, N: int, group_size: int, wtype: str = "int4
     gs = K if group_size == -1 else group_size
     part = torch.zeros((K // gs, m1 - m0, n1 - n0), dtype=torch.int32 if a_dt == I8 else torch.float32,
                        device=aq.device)
-    wsp, wsb = _workspace(workspace, gemm_workspace_bytes(M, N, K, group_size, a_dt), aq.device)
+    wsp, wsb, ws_keep = _workspace(workspace, gemm_workspace_bytes(M, N, K, group_size, a_dt), aq.device)
     _check("w4a8_gemm_partials", lib().w4a8_gemm_partials(
         _dev_ptr(aq, "aq"), a_dt, _dev_ptr(b_packed, "b_packed"), WTYPES[wtype], group_size, M, N, K,
         m0, m1, n0, n1, _dev_ptr(part, "partials"), wsp, wsb, _stream(aq)))
@@ -399,7 +401,7 @@ def w4a16_gemm_partials(a, b_packed, N: int, group_size: int, zeros=None, wtype:
     m0, m1, n0, n1 = _window(M, N, window)
     gs = K if group_size == -1 else group_size
     part = torch.zeros((K // gs, m1 - m0, n1 - n0), dtype=torch.float32, device=a.device)
-    wsp, wsb = _workspace(workspace, gemm_workspace_bytes(M, N, K, group_size, a_dt), a.device)
+    wsp, wsb, ws_keep = _workspace(workspace, gemm_workspace_bytes(M, N, K, group_size, a_dt), a.device)
     _check("w4a16_gemm_partials", lib().w4a16_gemm_partials(
         _dev_ptr(a, "a"), a_dt, _dev_ptr(b_packed, "b_packed"), WTYPES[wtype], _dev_ptr(zeros, "zeros"),
         group_size, M, N, K, m0, m1, n0, n1, _dev_ptr(part, "partials"), wsp, wsb, _stream(a)))

@@ -951,12 +951,17 @@ __global__ __launch_bounds__(256, 2) void w4_gemm_tiled(GemmArgs p, int splitk) 
       }
     }
   };
-  // fp16 W4A16 per channel: one zero-point per operand row for all of K.
+  // fp16 W4A16 per channel: one zero-point per operand row for all of K
+  // (through the zero-point buffer: rows past N, in the last column tile,
+  // read nothing).
   f16x2 nz_fixed[NT];
   if constexpr (OP == OP_F16 && !GROUPED) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      const _Float16 h = (_Float16)(-(1024.0f + zero_point(p, (nb_base + nt) * 16 + r, 0)));
+      const int64_t n = (nb_base + nt) * 16 + r;
+      const uint32_t zi = (uint32_t)n * (uint32_t)p.G;
+      const float z = p.z ? word_to_f32(load_word(rz, zdt, zi, n < p.N), zdt, zi) : 8.0f;
+      const _Float16 h = (_Float16)(-(1024.0f + z));
       nz_fixed[nt] = f16x2{h, h};
     }
   }
