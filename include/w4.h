@@ -15,7 +15,8 @@
  * Entry points: w4_prepack_B (and w4_prepack_B_from_exllama), the activation
  * quantisers (w4_quant_act_per_token, w4_quant_act_per_tensor,
  * w4_rmsnorm_quant_per_token), the GEMMs (w4a8_gemm, w4a8_gemm_zp,
- * w4a8_gemm_quant_fused, w4a16_gemm, w4a16_gemm_prescaled_zeros), their
+ * w4a8_gemm_quant_fused, w4a8_gemm_no_alloc, w4a16_gemm,
+ * w4a16_gemm_prescaled_zeros), their
  * verification variants
  * (w4a8_gemm_partials, w4a16_gemm_partials), and the planning helpers
  * (w4_gemm_workspace_bytes, w4_gemm_plan, w4_schedule_add / _clear,
@@ -27,7 +28,9 @@
  *     pointer must be 16-byte aligned.
  *   - The caller owns every buffer.  The library never allocates, frees or
  *     synchronises; it keeps no per-call state and may be called concurrently
- *     from several threads (on distinct output/workspace buffers).  The
+ *     from several threads (on distinct output/workspace buffers; the one
+ *     exception is w4a8_gemm_no_alloc, whose workspace is a buffer built into
+ *     the library and shared by every call on a GPU).  The
  *     tuning options and the run-time schedule entries are process-wide.
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *     Work is enqueued on it and the call returns without waiting.
@@ -251,6 +254,24 @@ W4_API int w4a8_gemm(const void* aq, int a_dtype, const float* a_scales, const v
               int wtype, const void* b_scales, int s_dtype, int64_t group_size,
               const void* bias, void* out, int out_dtype, int64_t M, int64_t N, int64_t K,
               void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * W4A8 GEMM that allocates nothing.
+ *
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): w4a8_gemm
+ * with the split-K workspace taken from a buffer built into the library, one
+ * 64 MiB copy per GPU, held until the process ends.  Same arguments, results
+ * and errors as w4a8_gemm without workspace / workspace_bytes; problems
+ * whose workspace (w4_gemm_workspace_bytes) exceeds 64 MiB return
+ * W4_E_WORKSPACE (use w4a8_gemm with a workspace of your own).  No
+ * allocation, free or memset.  Every call on a GPU shares that GPU's buffer:
+ * calls that overlap on one GPU (other streams, other threads) race.
+ * ------------------------------------------------------------------------- */
+W4_API int w4a8_gemm_no_alloc(const void* aq, int a_dtype, const float* a_scales, const void* b_packed,
+                              int wtype, const void* b_scales, int s_dtype, int64_t group_size,
+                              const void* bias, void* out, int out_dtype, int64_t M, int64_t N, int64_t K,
+                              void* stream);
 
 /* ---------------------------------------------------------------------------
  * W4A16 GEMM with pre-scaled zero-points.

@@ -23,7 +23,7 @@ from typing import Optional
 __all__ = [
     "LIB_PATH", "lib", "W4Error", "prepack_B", "prepack_B_from_exllama", "prepack_B_bytes", "quant_act_per_token",
     "quant_act_per_tensor", "rmsnorm_quant_per_token",
-    "w4a8_gemm", "w4a8_gemm_quant_fused", "w4a8_gemm_zp", "w4a16_gemm", "w4a16_gemm_prescaled_zeros", "w4a8_gemm_partials", "w4a16_gemm_partials",
+    "w4a8_gemm", "w4a8_gemm_no_alloc", "w4a8_gemm_quant_fused", "w4a8_gemm_zp", "w4a16_gemm", "w4a16_gemm_prescaled_zeros", "w4a8_gemm_partials", "w4a16_gemm_partials",
     "gemm_workspace_bytes", "gemm_plan", "set_option", "get_option", "schedule_add", "schedule_clear",
     "EXPORTED_SYMBOLS",
 ]
@@ -59,6 +59,8 @@ _SIGNATURES = [
     ("w4_gemm_workspace_bytes", _sz, [_i64, _i64, _i64, _i64, _int]),
     ("w4a8_gemm", _int, [_vp, _int, _vp, _vp, _int, _vp, _int, _i64, _vp, _vp, _int,
                          _i64, _i64, _i64, _vp, _sz, _vp]),
+    ("w4a8_gemm_no_alloc", _int, [_vp, _int, _vp, _vp, _int, _vp, _int, _i64, _vp, _vp, _int,
+                                  _i64, _i64, _i64, _vp]),
     ("w4a8_gemm_quant_fused", _int, [_vp, _int, _int, _vp, _int, _vp, _int, _i64, _vp, _vp, _int,
                                      _i64, _i64, _i64, _vp, _vp]),
     ("w4a16_gemm_prescaled_zeros", _int, [_vp, _int, _vp, _vp, _vp, _i64, _vp, _vp, _i64, _i64, _i64,
@@ -292,6 +294,24 @@ def w4a8_gemm(aq, a_scales, b_packed, b_scales, group_size: int, out_dtype, wtyp
         _dev_ptr(aq, "aq"), a_dt, _dev_ptr(a_scales, "a_scales"), _dev_ptr(b_packed, "b_packed"),
         WTYPES[wtype], _dev_ptr(b_scales, "b_scales"), _dtype_code(b_scales.dtype), group_size,
         _dev_ptr(bias, "bias"), _dev_ptr(out, "out"), o_dt, M, N, K, wsp, wsb, _stream(aq)))
+    return out
+
+
+def w4a8_gemm_no_alloc(aq, a_scales, b_packed, b_scales, group_size: int, out_dtype, wtype: str = "int4",
+                       bias=None, out=None):
+    """w4a8_gemm whose split-K workspace is the library's built-in per-GPU
+    buffer (include/w4.h); ``out`` must be given by callers that cannot
+    allocate."""
+    torch = _torch()
+    M, K = aq.shape
+    N = b_scales.shape[0]
+    a_dt = I8 if aq.dtype == torch.int8 else FP8_E4M3
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=aq.device)
+    _check("w4a8_gemm_no_alloc", lib().w4a8_gemm_no_alloc(
+        _dev_ptr(aq, "aq"), a_dt, _dev_ptr(a_scales, "a_scales"), _dev_ptr(b_packed, "b_packed"),
+        WTYPES[wtype], _dev_ptr(b_scales, "b_scales"), _dtype_code(b_scales.dtype), group_size,
+        _dev_ptr(bias, "bias"), _dev_ptr(out, "out"), _dtype_code(out_dtype), M, N, K, _stream(aq)))
     return out
 
 

@@ -311,6 +311,35 @@ int run_gemm(GemmArgs& args, int op, bool grouped, bool flip, void* workspace, s
   return ok();
 }
 
+// Split-K workspace of w4a8_gemm_no_alloc, for callers that cannot allocate.
+// One copy per GPU, held until the process ends; every call on a GPU shares
+// it (overlapping calls on one GPU race).  In host code `scratch` is only a
+// stand-in for the device copy: kernels get the address that
+// hipGetSymbolAddress returns for the current device, never the name.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) __attribute__((used)) uint8_t scratch[kScratchBytes];
+
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[64];
+
+// Device address of the current device's scratch copy (looked up once per
+// device, with that device current).
+int scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= 64) return fail(W4_E_UNSUPPORTED, "device %d: at most 64 devices", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) return hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol, "hipGetSymbolAddress(scratch)");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return W4_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -458,10 +487,10 @@ static int validate_w4a8(const void* aq, int a_dtype, const void* b_packed, int 
   return W4_OK;
 }
 
-int w4a8_gemm(const void* aq, int a_dtype, const float* a_scales, const void* b_packed, int wtype,
-              const void* b_scales, int s_dtype, int64_t group_size, const void* bias, void* out,
-              int out_dtype, int64_t M, int64_t N, int64_t K, void* workspace, size_t workspace_bytes,
-              void* stream) {
+// Every check of w4a8_gemm but the workspace's.
+static int validate_w4a8_gemm(const void* aq, int a_dtype, const float* a_scales, const void* b_packed, int wtype,
+                              const void* b_scales, int s_dtype, int64_t group_size, const void* bias,
+                              const void* out, int out_dtype, int64_t M, int64_t N, int64_t K) {
   if (int st = validate_w4a8(aq, a_dtype, b_packed, wtype, group_size, M, N, K)) return st;
   if (s_dtype != W4_F32 && s_dtype != W4_F16 && s_dtype != W4_BF16)
     return fail(W4_E_DTYPE, "s_dtype must be W4_F32, W4_F16 or W4_BF16");
@@ -470,6 +499,16 @@ int w4a8_gemm(const void* aq, int a_dtype, const float* a_scales, const void* b_
   if (!aligned(out, 16) || !aligned(a_scales, 4) || !aligned(b_scales, s_dtype == W4_F32 ? 4 : 2) ||
       !aligned(bias, 2))
     return fail(W4_E_ALIGN, "out must be 16-byte aligned; scales and bias naturally aligned");
+  return W4_OK;
+}
+
+int w4a8_gemm(const void* aq, int a_dtype, const float* a_scales, const void* b_packed, int wtype,
+              const void* b_scales, int s_dtype, int64_t group_size, const void* bias, void* out,
+              int out_dtype, int64_t M, int64_t N, int64_t K, void* workspace, size_t workspace_bytes,
+              void* stream) {
+  if (int st = validate_w4a8_gemm(aq, a_dtype, a_scales, b_packed, wtype, b_scales, s_dtype, group_size, bias, out,
+                                  out_dtype, M, N, K))
+    return st;
   const int64_t g = resolve_group(group_size, K);
   GemmArgs args{};
   args.a = aq;
@@ -487,6 +526,26 @@ int w4a8_gemm(const void* aq, int a_dtype, const float* a_scales, const void* b_
   args.z_dtype = W4_F16;
   args.mode = MODE_OUTPUT;
   return run_gemm(args, op_of(a_dtype), g != K, wtype == W4_UINT4B8, workspace, workspace_bytes, stream);
+}
+
+int w4a8_gemm_no_alloc(const void* aq, int a_dtype, const float* a_scales, const void* b_packed, int wtype,
+                       const void* b_scales, int s_dtype, int64_t group_size, const void* bias, void* out,
+                       int out_dtype, int64_t M, int64_t N, int64_t K, void* stream) {
+  // the checks of w4a8_gemm first, so that an invalid call reports the same error
+  if (int st = validate_w4a8_gemm(aq, a_dtype, a_scales, b_packed, wtype, b_scales, s_dtype, group_size, bias, out,
+                                  out_dtype, M, N, K))
+    return st;
+  const size_t need = w4_gemm_workspace_bytes(M, N, K, group_size, a_dtype);
+  if (need > kScratchBytes)
+    return fail(W4_E_WORKSPACE,
+                "w4a8_gemm_no_alloc: this problem's split-K workspace (%zu bytes) exceeds the built-in %zu; "
+                "call w4a8_gemm with a workspace", need, kScratchBytes);
+  void* ws = nullptr;
+  if (need) {
+    if (int st = scratch_address(&ws)) return st;
+  }
+  return w4a8_gemm(aq, a_dtype, a_scales, b_packed, wtype, b_scales, s_dtype, group_size, bias, out, out_dtype, M,
+                   N, K, ws, need ? kScratchBytes : 0, stream);
 }
 
 int w4a8_gemm_quant_fused(const void* x, int x_dtype, int q_dtype, const void* b_packed, int wtype,

@@ -145,6 +145,35 @@ def test_w4a8_validation(lib):
     assert _w4a8(lib, gs=32) == E_GROUP                 # groups of 64 / 32: W4A16 only
 
 
+def test_w4a8_no_alloc_validation(lib):
+    """Invalid arguments give w4a8_gemm's status; a workspace beyond the
+    built-in buffer is refused before anything is enqueued."""
+    f = lib.w4a8_gemm_no_alloc
+
+    def call(aq=FAKE, a_dtype=3, sa=FAKE, b=FAKE, wtype=0, bs=FAKE, s_dtype=2, gs=128, bias=None, out=FAKE,
+             out_dtype=0, M=4, N=32, K=256):
+        return f(aq, a_dtype, sa, b, wtype, bs, s_dtype, gs, bias, out, out_dtype, M, N, K, None)
+    assert call(a_dtype=0) == E_DTYPE
+    assert call(s_dtype=3) == E_DTYPE
+    assert call(out_dtype=2) == E_DTYPE
+    assert call(N=40) == E_SHAPE
+    assert call(gs=64) == E_GROUP
+    assert call(out=None) == E_NULL
+    assert call(out=MISALIGNED) == E_ALIGN
+    assert call(M=0) == W4_OK
+    # the same problems with a split-K plan: validation still comes first
+    try:
+        w4.set_option("force_path", 2)
+        w4.set_option("splitk", 64)
+        assert call(s_dtype=3, M=64, N=8192, K=8192, gs=-1) == E_DTYPE
+        # 64 splits x 64 x 8192 x 4 bytes = 128 MiB > the 64 MiB buffer
+        assert call(M=64, N=8192, K=8192, gs=-1) == E_WS
+        assert "64 MiB" in lib.w4_last_error().decode() or "67108864" in lib.w4_last_error().decode()
+    finally:
+        w4.set_option("force_path", 0)
+        w4.set_option("splitk", 0)
+
+
 def test_w4a16_validation(lib):
     def call(a=FAKE, a_dtype=1, b=FAKE, wtype=1, s=FAKE, z=FAKE, gs=128, out=FAKE, M=2, N=32, K=256):
         return lib.w4a16_gemm(a, a_dtype, b, wtype, s, z, gs, None, out, M, N, K, None, 0, None)
