@@ -16,7 +16,8 @@ group-128 decode GEMM 4096 x 4096, the int8 group-128 7B-style decoder-layer
 shapes and the fp8 group-128 GEMM 28672 x 8192.  Each point is timed over
 back-to-back launches that rotate through at least 512 MB of weight copies,
 and is set against its roofline (HBM below the ridge, the MFMA peak of its
-operand type above it).
+operand type above it).  These launches are captured in a HIP graph and
+replayed, so that the host's launch rate does not bound the short ones.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 
@@ -56,6 +57,8 @@ METRIC = "W4A8 GEMM TOPS + weight GB/s (% roofline), N=8192 K=21760, M=1..4096"
 CALIB_BYTES = 256 << 20          # plain copy of known size: reads and writes this many bytes
 POOL_BYTES = 512 << 20           # weight copies rotated per workload: twice the last-level cache
 GEMM_SOURCES = ["mixed_precision_quantized_prepack_amd/csrc/w4_gemm.hip",
+                "mixed_precision_quantized_prepack_amd/csrc/w4_gemm_stream.hip",
+                "mixed_precision_quantized_prepack_amd/csrc/w4_gemm_common.h",
                 "mixed_precision_quantized_prepack_amd/csrc/w4_device.h",
                 "mixed_precision_quantized_prepack_amd/csrc/w4_api.cpp"]
 
@@ -465,29 +468,48 @@ class WorkloadBench:
     def quant(self, M: int):
         self.w4.quant_act_per_token(self.a_rows[M], self.wl.q_dtype, out=self.aq[M], scales=self.sa[M])
 
-    def time_us(self, fn, reps: int) -> float:
+    def time_us(self, fn, reps: int, replays: int = 3) -> float:
+        """Average launch time of `reps` launches captured in one HIP graph
+        (so that the host's launch rate, ~8 us per call from Python, does not
+        bound short kernels), over the fastest of `replays` replays timed with
+        events on the launch stream."""
         torch = self.torch
-        fn(0)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for r in range(reps):
-            fn(r + 1)
-        e1.record()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fn(0)
+        torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
-        return e0.elapsed_time(e1) * 1e3 / reps
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for r in range(reps):
+                fn(r + 1)
+        g.replay()
+        torch.cuda.synchronize()
+        best = float("inf")
+        for _ in range(replays):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            best = min(best, e0.elapsed_time(e1) * 1e3 / reps)
+        del g
+        return best
 
-    def sweep(self, config: int, min_ms: float = 25.0) -> list:
+    def sweep(self, config: int, min_ms: float = 10.0) -> list:
         wl = self.wl
         rows = []
         for M in self.Ms:
-            # a first estimate sizes the back-to-back batch: at least 20
-            # launches and about min_ms of GPU time
-            est = self.time_us(lambda r: self.gemm(M, r), 3)
-            reps = int(max(20, min(400, min_ms * 1e3 / max(est, 1.0))))
+            # a first estimate sizes the captured batch: at least 20 launches
+            # and about min_ms of GPU time per replay
+            est = self.time_us(lambda r: self.gemm(M, r), 3, 1)
+            reps = int(max(20, min(200, min_ms * 1e3 / max(est, 1.0))))
             us = self.time_us(lambda r: self.gemm(M, r), reps)
             row = {"config": config, "workload": wl.name, "M": M, "N": wl.N, "K": wl.K,
                    "kernel": kernel_label(self.plans[M], wl), "k_split": self.plans[M][1],
-                   "gemm_us": round(us, 2), "launches": reps, "weight_copies": self.copies}
+                   "gemm_us": round(us, 2), "launches": reps, "timing": "graph replay, fastest of 3",
+                   "weight_copies": self.copies}
             row.update(roofline_point(wl, M, us))
             row["meets_target"] = us <= row["target_us"]
             if wl.kind == "w4a8":

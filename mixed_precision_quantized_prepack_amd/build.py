@@ -34,7 +34,7 @@ COMMON_FLAGS = [
     "-I", INCLUDE, "-I", CSRC,
 ]
 
-SOURCES = ["w4_api.cpp", "w4_prepack_quant.hip", "w4_gemm.hip"]
+SOURCES = ["w4_api.cpp", "w4_prepack_quant.hip", "w4_gemm.hip", "w4_gemm_stream.hip"]
 
 
 def _compile(src: str, verbose: bool, build_dir: str, extra) -> str:

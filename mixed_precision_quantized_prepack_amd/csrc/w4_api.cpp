@@ -147,7 +147,8 @@ int plan_with(int64_t M, int64_t N, int64_t K, bool grouped, int op, const Sched
   // workgroups and either the fragment is worth sharing (M >= 8) or the
   // strips are long (K >= 8192) or many (N >= 16384): a wave then keeps
   // twice the weight bytes in flight.
-  const int64_t fns = forced.strips;
+  const int64_t fns = plan->path == PATH_SKINNY ? forced.strips : 0;
+  if (plan->path == PATH_SKINNY && fns > 2) return fail(W4_E_SHAPE, "small-M kernel: 1 or 2 strips per wave");
   const bool two = N % 32 == 0 && (!grouped || N >= 16384 || (N >= 8192 && (M >= 8 || KB >= 64)));
   int64_t ns = fns ? fns : (two ? 2 : 1);
   const int64_t groups = grouped ? KB * sg : 1;   // sg groups per 128-deep block
@@ -164,6 +165,38 @@ int plan_with(int64_t M, int64_t N, int64_t K, bool grouped, int op, const Sched
       // (whose workspace size callers query) has none: no K split either
       one_split = zp && skinny_table_bytes(op, grouped, groups, 1) <= kSkinnyTableMax;
     }
+  }
+  if (plan->path == PATH_STREAM) {
+    // streaming kernel: 8-bit symmetric operands, one workgroup per CU
+    if ((op != OP_I8 && op != OP_FP8) || zp || sg != 1)
+      return fail(W4_E_UNSUPPORTED, "the streaming kernel takes int8 / fp8 activations and symmetric weights");
+    const int64_t fbm = forced.tile_m;
+    if (fbm && fbm != 32 && fbm != 64 && fbm != 128)
+      return fail(W4_E_SHAPE, "streaming kernel: tile rows 32, 64 or 128 (got %lld)", (long long)fbm);
+    const int64_t bm = fbm ? fbm : (M <= 32 ? 32 : M <= 64 ? 64 : 128);
+    // 16-column blocks per wave (the strips field): 2 or 4; 128-row tiles take 2
+    const int64_t fnt = forced.strips;
+    if (fnt && fnt != 2 && fnt != 4) return fail(W4_E_SHAPE, "streaming kernel: 2 or 4 column blocks per wave");
+    if (bm == 128 && fnt == 4) return fail(W4_E_SHAPE, "streaming kernel: 128-row tiles take 2 column blocks per wave");
+    plan->bm = (int)bm;
+    plan->bn = (int)(64 * (fnt ? fnt : (bm == 128 ? 2 : 4)));
+    const int64_t tiles = ((M + plan->bm - 1) / plan->bm) * ((N + plan->bn - 1) / plan->bn);
+    int64_t s = fs;
+    if (!s) {
+      s = tiles >= cu ? 1 : cu / tiles;
+      if (s > 64) s = 64;
+      while (s > 1 && KB / s < 2) --s;
+    }
+    // a grouped split's scales must fit the kernel's table
+    if (grouped && (KB + s - 1) / s > kStreamTableGroups) {
+      if (fs) return fail(W4_E_SHAPE, "streaming kernel: %lld K splits leave more than %d groups per split",
+                          (long long)s, kStreamTableGroups);
+      s = (KB + kStreamTableGroups - 1) / kStreamTableGroups;
+    }
+    if (s < 1 || s > 64 || s > KB)
+      return fail(W4_E_SHAPE, "streaming kernel: K split %lld not in [1, min(64, K/128)]", (long long)s);
+    plan->splitk = (int)s;
+    return W4_OK;
   }
   if (plan->path == PATH_SKINNY) {
     if (M > 16) return fail(W4_E_UNSUPPORTED, "the small-M kernel handles M <= 16 (M=%lld)", (long long)M);
@@ -197,6 +230,7 @@ int plan_with(int64_t M, int64_t N, int64_t K, bool grouped, int op, const Sched
     const bool byte = op == OP_I8 || op == OP_FP8;
     const bool fp8g = op == OP_FP8 && grouped;
     const int64_t fbm = forced.tile_m;
+    if (fbm == 32) return fail(W4_E_SHAPE, "tiled_bm=32 is for the streaming kernel");
     if (byte) {
       int tall_bm, tall_bn;
       tiled_tile(op, grouped, 1, &tall_bm, &tall_bn, zp);
@@ -287,7 +321,7 @@ int subgroups(int64_t group_size, int64_t K) {
 }
 
 size_t workspace_for(const GemmPlan& plan, int64_t M, int64_t N) {
-  if (plan.path != PATH_TILED || plan.splitk <= 1) return 0;
+  if (plan.path == PATH_SKINNY || plan.splitk <= 1) return 0;
   return (size_t)plan.splitk * (size_t)M * (size_t)N * 4u;
 }
 
@@ -765,7 +799,7 @@ int w4a16_gemm_partials(const void* a, int a_dtype, const void* b_packed, int wt
 int w4_set_option(const char* key, int64_t value) {
   if (!key) return fail(W4_E_NULL, "key is required");
   if (!strcmp(key, "force_path")) {
-    if (value < 0 || value > 2) return fail(W4_E_SHAPE, "force_path must be 0, 1 or 2");
+    if (value < 0 || value > 3) return fail(W4_E_SHAPE, "force_path must be 0, 1, 2 or 3");
     g_force_path.store(value);
     return ok();
   }
@@ -775,12 +809,13 @@ int w4_set_option(const char* key, int64_t value) {
     return ok();
   }
   if (!strcmp(key, "skinny_strips")) {
-    if (value < 0 || value > 2) return fail(W4_E_SHAPE, "skinny_strips must be 0, 1 or 2");
+    if (value < 0 || value > 4 || value == 3) return fail(W4_E_SHAPE, "skinny_strips must be 0, 1, 2 or 4");
     g_skinny_strips.store(value);
     return ok();
   }
   if (!strcmp(key, "tiled_bm")) {
-    if (value != 0 && value != 64 && value != 128) return fail(W4_E_SHAPE, "tiled_bm must be 0, 64 or 128");
+    if (value != 0 && value != 32 && value != 64 && value != 128)
+      return fail(W4_E_SHAPE, "tiled_bm must be 0, 32, 64 or 128");
     g_tiled_bm.store(value);
     return ok();
   }
@@ -814,10 +849,11 @@ int w4_schedule_add(int a_dtype, int group_mode, int64_t N, int64_t K, int64_t m
   if (group_mode != 0 && group_mode != 1) return fail(W4_E_SHAPE, "group_mode must be 0 or 1");
   if (N <= 0 || K <= 0 || m_lo < 0 || m_hi < m_lo)
     return fail(W4_E_SHAPE, "need N > 0, K > 0, 0 <= m_lo <= m_hi");
-  if (path < 0 || path > 2) return fail(W4_E_SHAPE, "path must be 0, 1 or 2");
+  if (path < 0 || path > 3) return fail(W4_E_SHAPE, "path must be 0, 1, 2 or 3");
   if (splitk < 0 || splitk > 64) return fail(W4_E_SHAPE, "splitk must be in [0, 64]");
-  if (tile_m != 0 && tile_m != 64 && tile_m != 128) return fail(W4_E_SHAPE, "tile_m must be 0, 64 or 128");
-  if (strips < 0 || strips > 2) return fail(W4_E_SHAPE, "strips must be 0, 1 or 2");
+  if (tile_m != 0 && tile_m != 32 && tile_m != 64 && tile_m != 128)
+    return fail(W4_E_SHAPE, "tile_m must be 0, 32, 64 or 128");
+  if (strips < 0 || strips > 4 || strips == 3) return fail(W4_E_SHAPE, "strips must be 0, 1, 2 or 4");
   if (path == 1 && m_hi > 16) return fail(W4_E_SHAPE, "the small-M kernel handles M <= 16");
   std::lock_guard<std::mutex> lock(g_sched_mutex);
   // a later entry for the same problems replaces an earlier one

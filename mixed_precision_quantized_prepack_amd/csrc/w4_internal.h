@@ -9,7 +9,7 @@ namespace w4 {
 // Matrix-core operand class of a GEMM (the activation type it multiplies).
 enum Op : int { OP_I8 = 0, OP_FP8 = 1, OP_F16 = 2, OP_BF16 = 3 };
 
-enum Path : int { PATH_AUTO = 0, PATH_SKINNY = 1, PATH_TILED = 2 };
+enum Path : int { PATH_AUTO = 0, PATH_SKINNY = 1, PATH_TILED = 2, PATH_STREAM = 3 };
 enum Mode : int { MODE_OUTPUT = 0, MODE_PARTIALS = 1 };
 
 // Everything a GEMM kernel reads, in element units unless noted.
@@ -63,7 +63,7 @@ inline int64_t skinny_table_bytes(int op, bool grouped, int64_t groups, int stri
 constexpr int64_t kSkinnyTableMax = 48 * 1024;
 
 struct GemmPlan {
-  int path;    // PATH_SKINNY or PATH_TILED
+  int path;    // PATH_SKINNY, PATH_TILED or PATH_STREAM
   int splitk;  // skinny: waves per workgroup splitting K; tiled: K splits across workgroups
   int bm, bn;  // tiled block tile (rows of A, columns of W)
 };
@@ -89,5 +89,21 @@ constexpr int64_t skinny_static_lds(int op, bool grouped, int strips) {
 // The fused quantisation (args.x set) takes the small-M kernel (plan.path == PATH_SKINNY).
 hipError_t launch_gemm(const GemmArgs& args, int op, bool grouped, bool flip, bool zp, const GemmPlan& plan,
                        hipStream_t stream);
+
+// The streaming kernel (8-bit operands, symmetric weights; plan.path ==
+// PATH_STREAM): tiles 32 x 256, 64 x 256 and 128 x 128.
+hipError_t launch_stream(const GemmArgs& args, int op, bool grouped, bool flip, const GemmPlan& plan,
+                         hipStream_t stream);
+// Steps the streaming kernel's LDS ring holds for a tile of 16 mt rows and 4 nt
+// n-blocks: as many 128-deep steps (activation tile + the four waves' weight
+// blocks) as fit 120 KiB, at most 8; 32 KiB more hold a grouped problem's
+// scale table.
+constexpr int stream_stages(int mt, int nt) {
+  return (120 * 1024) / (mt * 16 * 128 + 4 * nt * 1024) > 8 ? 8 : (120 * 1024) / (mt * 16 * 128 + 4 * nt * 1024);
+}
+// Groups of 128 the streaming kernel's scale table holds (the K range of one split).
+constexpr int kStreamTableGroups = 32;
+// Sum of the split-K slots and the epilogue (the workspace of a split plan).
+hipError_t launch_splitk_reduce(const GemmArgs& args, int op, bool grouped, int splitk, hipStream_t stream);
 
 }  // namespace w4

@@ -49,6 +49,31 @@ def n_round(q_dtype: str, G: int, splits: int = 16) -> int:
     return n if q_dtype == "i8" else n + 128
 
 
+def fp8_partials_bound(codes: np.ndarray, w_logical: np.ndarray, K: int, wtype: str = "int4",
+                       rows=None, cols=None) -> np.ndarray:
+    """Per-group bound [G, M, N] on |GPU fp8 partial - exact partial|.
+
+    The partial is the sum of the group's 128 exact products a*w, formed by
+    one fp8 MFMA.  That instruction does not sum them as a sequence of IEEE
+    fp32 additions: measured on MI355X, its result can differ from the exact
+    sum by up to about 2**-12 of the largest product's binade (it behaves
+    like products aligned to the largest one with ~12-13 bits kept below it),
+    which exceeds gamma_128 * sum|a*w| on some outputs.  The bound is the
+    larger of gamma_128 * sum|a*w| and 2**-10 * 2**floor(log2 max|a*w|)."""
+    A = O.activation_integers(codes if rows is None else codes[rows], "fp8").astype(np.float64) * 2.0 ** -9
+    wl = w_logical if cols is None else w_logical[cols]
+    W = O.weight_values(wl, K, wtype).astype(np.float64)
+    G = K // 128
+    out = np.empty((G, A.shape[0], W.shape[0]))
+    for g in range(G):
+        Ag, Wg = np.abs(A[:, g * 128:(g + 1) * 128]), np.abs(W[:, g * 128:(g + 1) * 128])
+        s = Ag @ Wg.T
+        mx = np.max(Ag[:, None, :] * Wg[None, :, :], axis=2)
+        win = np.where(mx > 0, 2.0 ** (np.floor(np.log2(np.where(mx > 0, mx, 1.0))) - 10), 0.0)
+        out[g] = np.maximum(128 * 2.0 ** -24 * s, win)
+    return out
+
+
 def w4a8_accept(gpu_bits: np.ndarray, ref: dict, out_dtype: str, q_dtype: str, G: int, strict: bool = False):
     """Per-element acceptance.  fp16 outputs: the tolerance |d| <= 2e-3 |ref|
     + 1e-3 alone; bf16 outputs: that or the rounding-bound clause.  strict:

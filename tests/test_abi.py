@@ -342,7 +342,7 @@ def test_schedule_add_validation(lib):
     assert f(3, 2, 8192, 21760, 1, 16, 1, 2, 0, 0) == E_SHAPE         # group mode
     assert f(3, 0, 8192, 21760, 17, 16, 2, 2, 0, 0) == E_SHAPE        # m_hi < m_lo
     assert f(3, 0, 8192, 21760, 1, 64, 1, 2, 0, 0) == E_SHAPE         # small-M kernel above M = 16
-    assert f(3, 0, 8192, 21760, 1, 16, 3, 2, 0, 0) == E_SHAPE
+    assert f(3, 0, 8192, 21760, 1, 16, 4, 2, 0, 0) == E_SHAPE         # paths 0..3
     assert f(3, 0, 8192, 21760, 1, 16, 2, 65, 0, 0) == E_SHAPE
     assert f(3, 0, 8192, 21760, 1, 16, 2, 2, 96, 0) == E_SHAPE
     assert f(3, 0, 8192, 21760, 1, 16, 1, 2, 0, 3) == E_SHAPE

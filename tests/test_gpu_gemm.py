@@ -17,7 +17,7 @@ import mixed_precision_quantized_prepack_amd as w4
 import workloads
 from oracle import formats as F
 from oracle import w4_oracle as O
-from tests.parity import DEV, DeviceCase, assert_w4a8, assert_w4a16, bits16
+from tests.parity import DEV, DeviceCase, assert_w4a8, assert_w4a16, bits16, fp8_partials_bound
 
 pytestmark = pytest.mark.gpu
 
@@ -100,12 +100,8 @@ def test_fp8_partials_within_bound(path, M, split, bm):
     codes = aq.cpu().numpy()
     P = O.w4a8_group_partials(codes, "fp8", dc.case.w_logical.numpy(), dc.K, "int4", 128)
     exact = P * 2.0 ** -9
-    A = np.abs(O.activation_integers(codes, "fp8")).astype(np.float64) * 2.0 ** -9
-    W = np.abs(O.weight_values(dc.case.w_logical.numpy(), dc.K, "int4")).astype(np.float64)
-    bound = np.stack([A[:, g * 128:(g + 1) * 128] @ W[:, g * 128:(g + 1) * 128].T for g in range(dc.G)])
-    # the MFMA sums 128 exact products in fp32 in an order of its own: the
-    # result may round, within gamma_128 * sum|a w|
-    assert np.all(np.abs(part - exact) <= 128 * 2.0 ** -24 * bound)
+    # the fp8 MFMA sums the 128 exact products with a precision of its own
+    assert np.all(np.abs(part - exact) <= fp8_partials_bound(codes, dc.case.w_logical.numpy(), dc.K))
 
 
 @pytest.mark.parametrize("a_dtype", ["bf16", "f16"])

@@ -39,3 +39,23 @@ def test_bf16_outputs_may_be_a_rounding_within_the_bound():
     far = F.round_and_encode(np.array([[1.1]]), "bf16")
     ok, _ = w4a8_accept(far, ref, "bf16", "fp8", G=64)
     assert not ok.any()
+
+
+def test_fp8_partials_bound_separates_rounding_from_wrong_pairing():
+    """The fp8 partials bound admits the exact sum's rounding but not a
+    partial formed with the activations paired with the wrong k."""
+    import workloads
+    from oracle import w4_oracle as O
+    from tests.parity import bits16, fp8_partials_bound
+    wl = workloads.WORKLOADS["w4a8_fp8_g128_28672x8192"]
+    c = workloads.make_case(wl, 6, N=32, K=256, seed_base=4)
+    codes, _ = O.quant_act_per_token(bits16(c.a), "bf16", "fp8")
+    exact = O.w4a8_group_partials(codes, "fp8", c.w_logical.numpy(), 256, "int4", 128) * 2.0 ** -9
+    bound = fp8_partials_bound(codes, c.w_logical.numpy(), 256)
+    assert np.all(bound >= 128 * 2.0 ** -24 * np.abs(exact))
+    # rounding the exact sums to fp32 stays inside
+    assert np.all(np.abs(exact.astype(np.float32).astype(np.float64) - exact) <= bound)
+    # activations shifted by one k inside each group: far outside
+    shifted = np.concatenate([np.roll(codes[:, g * 128:(g + 1) * 128], 1, axis=1) for g in range(2)], axis=1)
+    wrong = O.w4a8_group_partials(shifted, "fp8", c.w_logical.numpy(), 256, "int4", 128) * 2.0 ** -9
+    assert np.mean(np.abs(wrong - exact) > bound) > 0.9
