@@ -108,7 +108,8 @@ def kernel_label(plan, wl) -> str:
     op = {"i8": "int8", "fp8": "fp8", "f16": "fp16", "bf16": "bf16"}[op_name(wl)]
     if path == 1:
         return f"w4_gemm_skinny<{op}, {grp}, {tn // 16} strip(s)>"
-    return f"w4_gemm_tiled<{op}, {grp}, {tm}x{tn} tile, {'K split' if split > 1 else 'no K split'}>"
+    kern = "w4_gemm_stream" if path == 3 else "w4_gemm_tiled"
+    return f"{kern}<{op}, {grp}, {tm}x{tn} tile, {'K split' if split > 1 else 'no K split'}>"
 
 
 def gemm_alg_bytes(wl, M: int, n: int = None, k: int = None) -> int:
@@ -405,6 +406,10 @@ def kernel_key_of(wl, plan) -> str:
     if path == 1:
         return f"w4::w4_gemm_skinny<{op}, {grouped}, false, {tn // 16}, false, false, 1, false, false>"
     nt, mt = tn // 64, tm // 16
+    if path == 3:
+        stages = min(8, (120 * 1024) // (mt * 16 * 128 + 4 * nt * 1024))
+        return (f"w4::w4_gemm_stream<{op}, {grouped}, false, {nt}, {mt}, {stages}, "
+                f"{'true' if split > 1 else 'false'}, false>")
     return (f"w4::w4_gemm_tiled<{op}, {grouped}, false, {nt}, {mt}, {'true' if split > 1 else 'false'}, false, "
             f"false, 1, false>")
 

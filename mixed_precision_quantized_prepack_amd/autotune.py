@@ -2,7 +2,8 @@
 on the GPU and write the built-in schedule table.
 
 A schedule is (path, K split, tile rows, strips per wave), the fields of the
-library's tuning options.  For every M bucket the module times the
+library's tuning options (path 3, the streaming kernel, reads the strips
+field as 16-column blocks per wave).  For every M bucket the module times the
 heuristic's choice and each schedule that fits the problem, at the bucket's
 largest M, and keeps an entry only where the best schedule beats the
 heuristic by a margin (the heuristic stays in charge elsewhere).
@@ -64,6 +65,12 @@ def candidates(a_dtype: int, grouped: bool, M: int, N: int, K: int):
         for s in (1, 2, 4, 8, 16):
             if s <= K // 128:
                 out.append((2, s, tm, 0))
+    if byte and 16 < M <= 256:
+        for tm in (32, 64, 128):
+            for nt in ((2,) if tm == 128 else (2, 4)):
+                for s in (0, 1, 2, 4, 8, 16):
+                    if s <= K // 128:
+                        out.append((3, s, tm, nt))
     fits = []
     gs = 128 if grouped else -1
     for c in out:
@@ -122,14 +129,30 @@ class Problem:
 
 
 def _time_us(torch, fn, reps: int) -> float:
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    fn(0)
-    e0.record()
-    for r in range(reps):
-        fn(r + 1)
-    e1.record()
+    """Average launch time of `reps` launches captured in a HIP graph (so
+    the host's launch rate does not bound short kernels), fastest of two
+    replays."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn(0)
+    torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) * 1e3 / reps
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for r in range(reps):
+            fn(r + 1)
+    g.replay()
+    best = float("inf")
+    for _ in range(2):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        best = min(best, e0.elapsed_time(e1) * 1e3 / reps)
+    del g
+    return best
 
 
 def tune(shapes, buckets, trials: int, margin: float, log=print):
@@ -160,7 +183,7 @@ def tune(shapes, buckets, trials: int, margin: float, log=print):
                     fn = prob.launcher(M)
                     if est is None:
                         est = _time_us(torch, fn, 3)
-                    reps = max(3, min(200, int(3000.0 / max(est, 1.0))))
+                    reps = max(5, min(100, int(3000.0 / max(est, 1.0))))
                     us = _time_us(torch, fn, reps)
                     best[c] = min(best.get(c, float("inf")), us)
             _set_schedule()
@@ -186,18 +209,26 @@ def same_schedule(plan, cand) -> bool:
     (path, splitk, tile_m, tile_n) itself: then a faster timing is noise."""
     path, split, tm, tn = plan
     cp, cs, ctm, cst = cand
-    if cp != path or cs != split:
+    if cp != path or (cs != split and cs != 0):
         return False
-    return ctm == tm if path == 2 else cst * 16 == tn
+    if path == 2:
+        return ctm == tm
+    if path == 3:
+        return (ctm == tm or ctm == 0) and (cst * 64 == tn or cst == 0)
+    return cst * 16 == tn
 
 
-def write_table(results, path: str = TABLE_PATH) -> int:
+def write_table(results, path: str = TABLE_PATH, margin: float = None) -> int:
+    """Write the entries of a results file; `margin`, when given, re-decides
+    which entries to keep from the recorded timings."""
     lines = ["// Schedule table: {a_dtype, grouped, N, K, m_lo, m_hi, path, splitk, tile_m, strips}.",
              "// Written by mixed_precision_quantized_prepack_amd/autotune.py from MI355X measurements;",
              "// each entry beat the heuristic's schedule at m_hi (timings in the comment)."]
     n = 0
     for r in results:
-        if not r["keep"] or same_schedule(r["heuristic"], r["best"]):
+        keep = r["keep"] if margin is None else (r["best"] is not None and
+                                                 r["best_us"] < r["heuristic_us"] * (1.0 - margin))
+        if not keep or same_schedule(r["heuristic"], r["best"]):
             continue
         p, s, tm, st = r["best"]
         lines.append(f"    {{{DTYPE_NAMES[r['a_dtype']]}, {int(r['grouped'])}, {r['N']}, {r['K']}, {r['m_lo']}, "
@@ -220,7 +251,7 @@ def main(argv=None) -> int:
     args = ap.parse_args(argv)
     if args.write_table:
         with open(args.write_table) as f:
-            n = write_table(json.load(f)["results"])
+            n = write_table(json.load(f)["results"], margin=args.margin)
         print(f"wrote {n} entries to {TABLE_PATH}")
         return 0
     if not args.out:

@@ -98,6 +98,18 @@ int cu_count() {
 
 int64_t resolve_group(int64_t group_size, int64_t K) { return group_size == -1 ? K : group_size; }
 
+// Tile rows of the streaming kernel for 16 < M <= 64 (128-column tiles, one
+// workgroup per CU): 32 up to M = 32 and for grouped problems up to M = 64
+// (more tiles, fewer K splits: faster on the grouped benchmark shapes), 64
+// otherwise, or 64 when 32-row tiles would need more than one round of
+// workgroups; 0 when even 64-row tiles would (the tiled kernel then).
+int64_t stream_tile_m(int64_t M, int64_t N, bool grouped, int cu) {
+  const int64_t cols = (N + 127) / 128;
+  int64_t bm = (M <= 32 || grouped) ? 32 : 64;
+  if (bm == 32 && M > 32 && ((M + 31) / 32) * cols > cu) bm = 64;
+  return ((M + bm - 1) / bm) * cols > cu ? 0 : bm;
+}
+
 int op_of(int a_dtype) {
   switch (a_dtype) {
     case W4_I8: return OP_I8;
@@ -140,7 +152,12 @@ int plan_with(int64_t M, int64_t N, int64_t K, bool grouped, int op, const Sched
   const int64_t fp = forced.path, fs = forced.splitk;
   const int64_t KB = K / 128;
   const int cu = cu_count();
-  plan->path = fp ? (int)fp : (M <= 16 ? PATH_SKINNY : PATH_TILED);
+  // small M: the small-M kernel; 16 < M <= 64 with symmetric int8: the
+  // streaming kernel (measured faster on every int8 benchmark shape at
+  // M = 32 and on most at M = 64; fp8, whose lookup expansion keeps one wave
+  // per SIMD busy, is faster tiled); larger M: the tiled kernel
+  const bool stream_ok = op == OP_I8 && !zp && sg == 1 && M > 16 && M <= 64 && stream_tile_m(M, N, grouped, cu);
+  plan->path = fp ? (int)fp : (M <= 16 ? PATH_SKINNY : stream_ok ? PATH_STREAM : PATH_TILED);
   tiled_tile(op, grouped, 0, &plan->bm, &plan->bn, zp);
   // strips of 16 columns per wave of the small-M kernel: two strips share
   // one activation fragment.  Grouped problems take two when N leaves enough
@@ -173,13 +190,18 @@ int plan_with(int64_t M, int64_t N, int64_t K, bool grouped, int op, const Sched
     const int64_t fbm = forced.tile_m;
     if (fbm && fbm != 32 && fbm != 64 && fbm != 128)
       return fail(W4_E_SHAPE, "streaming kernel: tile rows 32, 64 or 128 (got %lld)", (long long)fbm);
-    const int64_t bm = fbm ? fbm : (M <= 32 ? 32 : M <= 64 ? 64 : 128);
-    // 16-column blocks per wave (the strips field): 2 or 4; 128-row tiles take 2
+    int64_t bm = fbm;
+    if (!bm) {
+      bm = M <= 64 ? stream_tile_m(M, N, grouped, cu) : 128;
+      if (!bm) bm = M <= 32 ? 32 : 64;   // forced onto a problem with more tiles than CUs
+    }
+    // 16-column blocks per wave (the strips field): 2 (the default: more
+    // column tiles, fewer K splits) or 4; 128-row tiles take 2
     const int64_t fnt = forced.strips;
     if (fnt && fnt != 2 && fnt != 4) return fail(W4_E_SHAPE, "streaming kernel: 2 or 4 column blocks per wave");
     if (bm == 128 && fnt == 4) return fail(W4_E_SHAPE, "streaming kernel: 128-row tiles take 2 column blocks per wave");
     plan->bm = (int)bm;
-    plan->bn = (int)(64 * (fnt ? fnt : (bm == 128 ? 2 : 4)));
+    plan->bn = (int)(64 * (fnt ? fnt : 2));
     const int64_t tiles = ((M + plan->bm - 1) / plan->bm) * ((N + plan->bn - 1) / plan->bn);
     int64_t s = fs;
     if (!s) {
@@ -188,10 +210,11 @@ int plan_with(int64_t M, int64_t N, int64_t K, bool grouped, int op, const Sched
       while (s > 1 && KB / s < 2) --s;
     }
     // a grouped split's scales must fit the kernel's table
-    if (grouped && (KB + s - 1) / s > kStreamTableGroups) {
+    const int tg = stream_table_groups(plan->bn);
+    if (grouped && (KB + s - 1) / s > tg) {
       if (fs) return fail(W4_E_SHAPE, "streaming kernel: %lld K splits leave more than %d groups per split",
-                          (long long)s, kStreamTableGroups);
-      s = (KB + kStreamTableGroups - 1) / kStreamTableGroups;
+                          (long long)s, tg);
+      s = (KB + tg - 1) / tg;
     }
     if (s < 1 || s > 64 || s > KB)
       return fail(W4_E_SHAPE, "streaming kernel: K split %lld not in [1, min(64, K/128)]", (long long)s);
@@ -487,7 +510,15 @@ size_t w4_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t group_si
   GemmPlan plan;
   const bool grouped = resolve_group(group_size, K) != K;
   if (make_plan(M, N, K, grouped, op, &plan, false, subgroups(group_size, K))) return 0;
-  return workspace_for(plan, M, N);
+  size_t need = workspace_for(plan, M, N);
+  // int8: also large enough for the asymmetric GEMM (w4a8_gemm_zp), whose
+  // plan may differ
+  GemmPlan zp_plan;
+  if (op == OP_I8 && make_plan(M, N, K, grouped, op, &zp_plan, true) == W4_OK) {
+    const size_t zneed = workspace_for(zp_plan, M, N);
+    if (zneed > need) need = zneed;
+  }
+  return need;
 }
 
 int w4_gemm_plan(int64_t M, int64_t N, int64_t K, int64_t group_size, int a_dtype, int* path, int* splitk,

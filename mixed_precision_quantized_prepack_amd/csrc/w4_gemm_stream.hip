@@ -42,7 +42,7 @@ struct StreamShape {
   static constexpr int WSTAGE = 4 * NT * 1024;       // the four waves' weight blocks
   static constexpr int STAGE = ASTAGE + WSTAGE;
   static constexpr int BNW = 4 * NT * 16;            // columns of the workgroup
-  static constexpr int TABG = kStreamTableGroups;    // groups the scale table holds
+  static constexpr int TABG = stream_table_groups(BNW);   // groups the 32 KiB scale table holds
   static constexpr int TAB = TABG * BNW * 4;
   static constexpr int LDS = STAGES * STAGE;         // plus TAB when grouped
 };

@@ -101,8 +101,9 @@ hipError_t launch_stream(const GemmArgs& args, int op, bool grouped, bool flip, 
 constexpr int stream_stages(int mt, int nt) {
   return (120 * 1024) / (mt * 16 * 128 + 4 * nt * 1024) > 8 ? 8 : (120 * 1024) / (mt * 16 * 128 + 4 * nt * 1024);
 }
-// Groups of 128 the streaming kernel's scale table holds (the K range of one split).
-constexpr int kStreamTableGroups = 32;
+// Groups of 128 the streaming kernel's 32 KiB scale table holds for a tile of
+// bn columns (the K range of one split).
+constexpr int stream_table_groups(int bn) { return 8192 / bn; }
 // Sum of the split-K slots and the epilogue (the workspace of a split plan).
 hipError_t launch_splitk_reduce(const GemmArgs& args, int op, bool grouped, int splitk, hipStream_t stream);
 

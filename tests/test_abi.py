@@ -267,7 +267,8 @@ def test_plan_choices(lib, heuristic_only):
     plans = {M: w4.gemm_plan(M, 8192, 21760, -1, w4.I8) for M in (1, 16, 64, 128, 256, 512, 1024, 4096)}
     assert plans[1][0] == plans[16][0] == 1                      # small-M kernel
     assert plans[1][3] == 32                                     # two 16-column strips per wave
-    assert [plans[M][1] for M in (64, 128, 256, 512, 1024)] == [8, 4, 4, 2, 1]
+    assert plans[64] == (3, 4, 64, 128)                         # streaming kernel, 64 tiles x 4 K splits
+    assert [plans[M][1] for M in (128, 256, 512, 1024)] == [4, 4, 2, 1]
     assert plans[4096][1:] == (1, 128, 256)                      # one 128 x 256 tile per workgroup
     # grouped small M: two strips from M = 8 when N >= 8192, at any M when
     # N >= 16384 or (N >= 8192 and K >= 8192), else one
@@ -278,21 +279,40 @@ def test_plan_choices(lib, heuristic_only):
     assert w4.gemm_plan(1, 8192, 8192, 128, w4.BF16)[:2] == (1, 8) and w4.gemm_plan(1, 8192, 8192, 128, w4.BF16)[3] == 32
     assert w4.gemm_plan(16, 22016, 4096, 128, w4.I8)[3] == 32
     assert w4.gemm_plan(16, 4096, 11008, 128, w4.I8)[3] == 16
-    # grouped int8 K splits: the most that keep one workgroup per CU (at least 4 K blocks each)
-    assert w4.gemm_plan(64, 12288, 4096, 128, w4.I8)[1] == 4          # 48 tiles
-    assert w4.gemm_plan(128, 22016, 4096, 128, w4.I8)[1] == 1         # 172 tiles
-    assert w4.gemm_plan(32, 4096, 11008, 128, w4.I8)[1] == 16         # 16 tiles, 86 K blocks
-    assert w4.gemm_plan(32, 4096, 4096, 128, w4.I8)[1] == 8           # 32 K blocks
+    # 16 < M <= 64, 8-bit operands: the streaming kernel, 32- or 64-row
+    # tiles of 128 columns, K split to one workgroup per CU
+    assert w4.gemm_plan(64, 12288, 4096, 128, w4.I8) == (3, 1, 32, 128)       # 192 tiles
+    assert w4.gemm_plan(32, 4096, 11008, 128, w4.I8) == (3, 8, 32, 128)       # 32 tiles, 86 K blocks
+    assert w4.gemm_plan(32, 4096, 4096, 128, w4.I8) == (3, 8, 32, 128)
+    # ... whose grouped K range must fit the scale table (64 groups of 128-column tiles)
+    assert w4.gemm_plan(32, 28672, 16384, 128, w4.I8) == (3, 2, 32, 128)      # 224 tiles
+    # more 32-row tiles than CUs: 64-row tiles; more 64-row tiles than CUs: tiled
+    assert w4.gemm_plan(64, 22016, 4096, 128, w4.I8) == (3, 1, 64, 128)       # 172 tiles
+    assert w4.gemm_plan(64, 65536, 4096, 128, w4.I8)[0] == 2
+    # fp8 stays on the tiled kernel
+    assert w4.gemm_plan(32, 28672, 8192, 128, w4.FP8_E4M3)[0] == 2
     # grouped int8 and fp8: 128 x 128 tiles once there is one per CU, else 64 x 256
     assert w4.gemm_plan(1024, 22016, 4096, 128, w4.I8)[2:] == (128, 128)
     assert w4.gemm_plan(128, 22016, 4096, 128, w4.I8)[2:] == (64, 256)
     assert w4.gemm_plan(8192, 28672, 8192, 128, w4.FP8_E4M3)[1:] == (1, 128, 128)
-    assert w4.gemm_plan(32, 28672, 8192, 128, w4.FP8_E4M3)[2:] == (64, 256)
     # grouped fp8: the tall tile from M = 128 (half a workgroup per CU), the
     # most K splits that fit two workgroups per CU
     assert w4.gemm_plan(128, 28672, 8192, 128, w4.FP8_E4M3)[1:] == (2, 128, 128)
     assert w4.gemm_plan(256, 28672, 8192, 128, w4.FP8_E4M3)[1:] == (1, 128, 128)
-    assert w4.gemm_plan(64, 28672, 8192, 128, w4.FP8_E4M3)[1:] == (4, 64, 256)
+    # the tiled kernel's K splits at M <= 64 (forced): grouped int8 takes the
+    # most that keep one workgroup per CU (at least 4 K blocks each)
+    try:
+        w4.set_option("force_path", 2)
+        assert w4.gemm_plan(64, 12288, 4096, 128, w4.I8)[1] == 4          # 48 tiles
+        assert w4.gemm_plan(32, 4096, 11008, 128, w4.I8)[1] == 16         # 16 tiles, 86 K blocks
+        assert w4.gemm_plan(32, 28672, 8192, 128, w4.FP8_E4M3)[2:] == (64, 256)
+        assert w4.gemm_plan(64, 28672, 8192, 128, w4.FP8_E4M3)[1:] == (4, 64, 256)
+        assert w4.gemm_plan(64, 8192, 21760, -1, w4.I8)[1] == 8
+    finally:
+        w4.set_option("force_path", 0)
+    assert w4.gemm_plan(128, 22016, 4096, 128, w4.I8)[1] == 1         # 172 tiles
+    # int8 workspace: large enough for the asymmetric GEMM's (tiled) plan too
+    assert w4.gemm_workspace_bytes(64, 8192, 21760, -1, w4.I8) >= 8 * 64 * 8192 * 4
     # a grouped K whose LDS scale table would not fit the small-M kernel: tiled
     assert w4.gemm_plan(1, 8192, 131072, 128, w4.I8)[0] == 2
     try:

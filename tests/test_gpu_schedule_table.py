@@ -21,7 +21,9 @@ def _workload(a_dtype, grouped):
         return workloads.WORKLOADS["w4a8_i8_g128_o" if grouped else "w4a8_i8_pc_8192x21760"]
     if a_dtype == w4.FP8_E4M3 and grouped:
         return workloads.WORKLOADS["w4a8_fp8_g128_28672x8192"]
-    if a_dtype == w4.BF16 and grouped:
+    if a_dtype in (w4.BF16, w4.F16):
+        # the W4A16 workload's dtypes and distributions (converted to fp16 and
+        # to one group per row below where the entry asks for them)
         return workloads.WORKLOADS["w4a16_bf16_g128_4096x4096"]
     raise AssertionError(f"no workload for a_dtype={a_dtype} grouped={grouped}")
 
@@ -58,8 +60,13 @@ def test_table_schedule_parity(entry):
             sub = out.cpu()[torch.as_tensor(rows)][:, torch.as_tensor(cols)]
             assert_w4a8(sub, ref, wl.out_dtype, wl.q_dtype, G, label=f"{entry} M={M}")
         else:
-            out = w4.w4a16_gemm(a.to(DEV), packed, case.w_scales.to(DEV), case.zeros.to(DEV), 128)
-            ref = O.w4a16_gemm(bits16(a), wl.a_dtype, case.w_logical.numpy(), K, wl.wtype,
-                               bits16(case.w_scales), bits16(case.zeros), 128, rows=rows, cols=cols)
+            dt, dname = (torch.float16, "f16") if a_dtype == w4.F16 else (torch.bfloat16, "bf16")
+            gsz = 128 if grouped else K
+            a16 = a.float().to(dt)
+            s16 = case.w_scales.float()[:, :K // gsz].contiguous().to(dt)
+            z16 = case.zeros.float()[:, :K // gsz].contiguous().to(dt)
+            out = w4.w4a16_gemm(a16.to(DEV), packed, s16.to(DEV), z16.to(DEV), gsz if grouped else -1)
+            ref = O.w4a16_gemm(bits16(a16), dname, case.w_logical.numpy(), K, wl.wtype,
+                               bits16(s16), bits16(z16), gsz, rows=rows, cols=cols)
             sub = out.cpu()[torch.as_tensor(rows)][:, torch.as_tensor(cols)]
-            assert_w4a16(sub, ref, wl.a_dtype, label=f"{entry} M={M}")
+            assert_w4a16(sub, ref, dname, label=f"{entry} M={M}")

@@ -88,13 +88,18 @@ def test_stream_outputs(wl, wtype, M, bm, split):
 
 
 def test_stream_grouped_long_k_takes_enough_splits():
-    """A grouped K range longer than the scale table is split until it fits."""
-    dc = DeviceCase("w4a8_i8_g128_o", 40, N=256, K=128 * 70, seed_base=2)
+    """A grouped K range longer than the scale table is split until it fits
+    (a forced split that leaves too many groups is refused)."""
+    dc = DeviceCase("w4a8_i8_g128_o", 40, N=256, K=128 * 140, seed_base=2)
     packed = w4.prepack_B(dc.w_logical, "i8")
     aq, sa = w4.quant_act_per_token(dc.a, "i8")
-    with options(0, 0):
+    with options(1, 0):
+        # one split would leave 140 groups for a 64-group table
+        with pytest.raises(w4.W4Error):
+            w4.gemm_plan(40, 256, dc.K, 128, w4.I8)
+    with options(3, 0):
         path, split, bm, bn = w4.gemm_plan(40, 256, dc.K, 128, w4.I8)
-        assert path == STREAM and (70 + split - 1) // split <= 32
+        assert path == STREAM and (140 + split - 1) // split <= 8192 // bn
         out = w4.w4a8_gemm(aq, sa, packed, dc.w_scales, 128, torch.float16)
     codes, sa_o = dc.oracle_quant()
     assert_w4a8(out, dc.oracle_w4a8(codes, sa_o), "f16", "i8", dc.G, label="stream long K")
