@@ -94,10 +94,11 @@ class W4Error(RuntimeError):
 
 def lib(path: Optional[str] = None) -> ctypes.CDLL:
     """Load libw4.so (once).  Raises if it has not been built.  ``path``
-    binds another build of the same ABI instead (tuning experiments)."""
+    binds another build of the same ABI instead (tuning experiments), as does
+    the W4_LIBRARY environment variable (the host-sanitized build)."""
     global _LIB
     if _LIB is None or path is not None:
-        path = path or LIB_PATH
+        path = path or os.environ.get("W4_LIBRARY") or LIB_PATH
         if not os.path.exists(path):
             raise ImportError(f"{path} is missing: build it with "
                               "`python -m mixed_precision_quantized_prepack_amd.build`")

@@ -1,9 +1,17 @@
 """Build libw4.so (the HIP library behind the C ABI in include/w4.h) for gfx950.
 
     python -m mixed_precision_quantized_prepack_amd.build [-j JOBS] [-v]
+    python -m mixed_precision_quantized_prepack_amd.build --sanitize
 
 Each source is compiled separately (in parallel) into _build/ and linked into
 mixed_precision_quantized_prepack_amd/libw4.so.  Always recompiles.
+
+--sanitize builds _build/sanitize/libw4_sanitize.so: the host code of the C ABI
+(w4_api.cpp: argument validation, planning, schedule table, options) compiled
+with AddressSanitizer and UndefinedBehaviorSanitizer (host side only; the GPU
+code is unchanged), linked with the kernels' objects of the last plain build.
+It is loaded through W4_LIBRARY with the sanitizer runtime preloaded, for the
+CPU tests of the ABI (tests/test_sanitized_abi.py); it is not for GPU runs.
 """
 from __future__ import annotations
 
@@ -74,12 +82,51 @@ def build(jobs: int = 4, verbose: bool = False, extra_flags=(), out_path: str = 
     return out_path
 
 
+SANITIZE_DIR = os.path.join(BUILD_DIR, "sanitize")
+SANITIZE_LIB = os.path.join(SANITIZE_DIR, "libw4_sanitize.so")
+# host-side only (each sanitizer flag applies to the host compilation)
+SANITIZE_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                  "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer",
+                  "-Xarch_host", "-g"]
+
+
+def sanitizer_runtime() -> str:
+    """The shared AddressSanitizer runtime of the host compiler (to preload)."""
+    r = subprocess.run([HIPCC, "--print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    path = r.stdout.strip()
+    if r.returncode != 0 or not os.path.isabs(path) or not os.path.exists(path):
+        raise RuntimeError(f"the AddressSanitizer runtime was not found ({path!r})")
+    return path
+
+
+def build_sanitized(verbose: bool = False) -> str:
+    """w4_api.cpp with host sanitizers, linked with the kernel objects in
+    _build/ (built first if missing)."""
+    kernel_srcs = [s for s in SOURCES if s.endswith(".hip")]
+    kernel_objs = [os.path.join(BUILD_DIR, s + ".o") for s in kernel_srcs]
+    if not all(os.path.exists(o) for o in kernel_objs):
+        build(verbose=verbose)
+    os.makedirs(SANITIZE_DIR, exist_ok=True)
+    api_obj = _compile("w4_api.cpp", verbose, SANITIZE_DIR, SANITIZE_FLAGS)
+    tmp = SANITIZE_LIB + ".tmp"
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-shared-libasan", *SANITIZE_FLAGS[:4],
+           "-o", tmp, api_obj, *kernel_objs]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"linking {SANITIZE_LIB} failed:\n{r.stdout}{r.stderr}")
+    os.replace(tmp, SANITIZE_LIB)
+    return SANITIZE_LIB
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("-j", "--jobs", type=int, default=4)
     ap.add_argument("-v", "--verbose", action="store_true")
+    ap.add_argument("--sanitize", action="store_true", help="build the host-sanitized ABI library instead")
     a = ap.parse_args(argv)
-    print(build(a.jobs, a.verbose))
+    print(build_sanitized(a.verbose) if a.sanitize else build(a.jobs, a.verbose))
     return 0
 
 

@@ -261,6 +261,18 @@ int plan_with(int64_t M, int64_t N, int64_t K, bool grouped, int op, const Sched
       const int64_t need = (op == OP_I8 && !grouped) ? 2LL * cu : (int64_t)cu;
       const bool tall = fbm ? fbm == 128 : (fp8g ? M >= 128 && 2 * tall_tiles >= cu : tall_tiles >= need);
       tiled_tile(op, grouped, tall ? 1 : 0, &plan->bm, &plan->bn, zp);
+      // 16-column blocks per wave (the strips field): 2 (tiles of 128
+      // columns) or 4 (256 columns: 64-row tiles, and 128-row tiles of
+      // symmetric int8 per channel)
+      const int64_t fnt = forced.strips;
+      if (fnt) {
+        if (fnt != 2 && fnt != 4) return fail(W4_E_SHAPE, "tiled kernel: 2 or 4 column blocks per wave");
+        if (fnt == 4 && plan->bm == 128 && !(op == OP_I8 && !grouped && !zp))
+          return fail(W4_E_SHAPE, "tiled kernel: 128 x 256 tiles are for symmetric int8 per channel");
+        plan->bn = (int)(64 * fnt);
+      }
+    } else if (forced.strips && forced.strips != 2) {
+      return fail(W4_E_SHAPE, "tiled kernel: 16-bit activations take 128-column tiles (2 blocks per wave)");
     } else if (fbm && fbm != plan->bm) {
       return fail(W4_E_SHAPE, "tiled_bm=%lld is not available for this problem", (long long)fbm);
     }

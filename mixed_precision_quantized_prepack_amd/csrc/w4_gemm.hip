@@ -1052,10 +1052,27 @@ __global__ __launch_bounds__(256, (tiled_min_blocks<OP, GROUPED, MT, PARTIALS, Z
   }
 }
 
+// Four consecutive elements [i, i + 4) of an fp32 / fp16 / bf16 array as fp32
+// (i a multiple of 4; the array 16-byte aligned).
+__device__ __forceinline__ f32x4 load_quad_f32(const void* p, int dtype, int64_t i) {
+  if (dtype == W4_F32) {
+    const float4 v = *reinterpret_cast<const float4*>(static_cast<const float*>(p) + i);
+    return f32x4{v.x, v.y, v.z, v.w};
+  }
+  const uint2 w = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p) + i);
+  const uint32_t h[4] = {w.x & 0xFFFFu, w.x >> 16, w.y & 0xFFFFu, w.y >> 16};
+  f32x4 r;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) r[j] = dtype == W4_F16 ? f16_bits_to_f32(h[j]) : bf16_bits_to_f32(h[j]);
+  return r;
+}
+
 // Sum the split-K slots of the tiled kernel in split order, then the epilogue.
-// A thread owns four consecutive columns of one row; the slots are loaded
-// eight at a time (all in flight together; slots past the last read zero)
-// and added in slot order.
+// A thread owns four consecutive columns of one row.  Its epilogue operands
+// (per-channel scales, bias, the row's activation scale) are loaded first, so
+// that they are in flight with the slots; the slots are loaded eight at a
+// time (all in flight together; slots past the last read zero) and added in
+// slot order.  The epilogue is the one `finalize` computes, term for term.
 template <int OP, bool GROUPED>
 __global__ __launch_bounds__(256) void w4_splitk_reduce(GemmArgs p, int splitk) {
   const int64_t quads = p.N >> 2;
@@ -1071,6 +1088,13 @@ __global__ __launch_bounds__(256) void w4_splitk_reduce(GemmArgs p, int splitk) 
     const int64_t m = t / quads;
     const int64_t n = (t - m * quads) * 4;
     const int64_t base = m * p.N + n;   // word index in slot 0
+    f32x4 sv{1.0f, 1.0f, 1.0f, 1.0f}, bv{0.0f, 0.0f, 0.0f, 0.0f};
+    float am = 1.0f;
+    if (!partials) {
+      if (!GROUPED) sv = load_quad_f32(p.s, p.s_dtype, n);
+      if (p.bias) bv = load_quad_f32(p.bias, p.out_dtype, n);
+      if (p.a_scales) am = p.a_scales[m];
+    }
     float fv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     int32_t iv[4] = {0, 0, 0, 0};
     auto add = [&](const u32x4& v) {
@@ -1104,7 +1128,13 @@ __global__ __launch_bounds__(256) void w4_splitk_reduce(GemmArgs p, int splitk) 
       uint16_t o[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float v = finalize<OP, GROUPED>(p, m, n + i, fv[i], iv[i]);
+        float v;
+        if constexpr (GROUPED)
+          v = fv[i];
+        else
+          v = (OP == OP_I8) ? (float)iv[i] * (sv[i] * 0.0625f) : fv[i] * sv[i];
+        if (p.a_scales) v *= am;
+        if (p.bias) v += bv[i];
         o[i] = p.out_dtype == W4_F16 ? f32_to_f16_bits(v) : f32_to_bf16_bits(v);
       }
       *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + m * p.N + n) =
@@ -1229,6 +1259,8 @@ static hipError_t launch_typed(const GemmArgs& args, const GemmPlan& plan, hipSt
         return hipErrorInvalidValue;
     } else if (plan.bm == 128)
       launch(std::integral_constant<int, 8>{}, std::integral_constant<int, 2>{});
+    else if (plan.bn == 128)
+      launch(std::integral_constant<int, 4>{}, std::integral_constant<int, 2>{});
     else
       launch(std::integral_constant<int, 4>{}, std::integral_constant<int, 4>{});
   } else if constexpr (SG == 4) {

@@ -343,9 +343,24 @@ def test_options_and_plans(lib, heuristic_only):
         assert w4.gemm_workspace_bytes(1, 8192, 21760, -1, w4.I8) == 4 * 1 * 8192 * 4
         # a split-K tiled plan needs its workspace
         assert _w4a8(lib, M=1, N=8192, K=21760, gs=-1, s_dtype=2) == E_WS
+        # tiled column blocks per wave: 2 (128 columns) or 4 (256); 128 x 256
+        # tiles for symmetric int8 per channel only; 16-bit tiles are 64 x 128
+        w4.set_option("skinny_strips", 2)
+        w4.set_option("tiled_bm", 64)
+        assert w4.gemm_plan(100, 8192, 21760, -1, w4.I8) == (2, 4, 64, 128)
+        assert w4.gemm_plan(100, 4096, 4096, 128, w4.FP8_E4M3) == (2, 4, 64, 128)
+        assert w4.gemm_plan(100, 4096, 4096, 128, w4.BF16)[2:] == (64, 128)
+        w4.set_option("skinny_strips", 4)
+        assert w4.gemm_plan(100, 4096, 4096, 128, w4.I8)[2:] == (64, 256)
+        with pytest.raises(w4.W4Error):
+            w4.gemm_plan(100, 4096, 4096, 128, w4.BF16)
+        w4.set_option("tiled_bm", 128)
+        assert w4.gemm_plan(200, 8192, 21760, -1, w4.I8)[2:] == (128, 256)
+        with pytest.raises(w4.W4Error):
+            w4.gemm_plan(200, 4096, 4096, 128, w4.I8)
     finally:
-        w4.set_option("force_path", 0)
-        w4.set_option("splitk", 0)
+        for k in ("force_path", "splitk", "skinny_strips", "tiled_bm"):
+            w4.set_option(k, 0)
     assert w4.get_option("force_path") == 0
 
 
@@ -414,7 +429,9 @@ def test_builtin_schedule_entries_fit_their_problems(lib):
         for M in (m_lo, m_hi):
             p = w4.gemm_plan(M, N, K, gs, a_dtype)
             assert p[0] == path and (splitk == 0 or p[1] == splitk), (N, K, M)
-            if path == 2 and tile_m:
+            if path in (2, 3) and tile_m:
                 assert p[2] == tile_m, (N, K, M)
             if path == 1 and strips:
                 assert p[3] == 16 * strips, (N, K, M)
+            if path in (2, 3) and strips:
+                assert p[3] == 64 * strips, (N, K, M)

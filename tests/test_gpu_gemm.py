@@ -23,16 +23,16 @@ pytestmark = pytest.mark.gpu
 
 
 @contextlib.contextmanager
-def options(path=0, splitk=0, bm=0):
+def options(path=0, splitk=0, bm=0, strips=0):
     w4.set_option("force_path", path)
     w4.set_option("splitk", splitk)
     w4.set_option("tiled_bm", bm)
+    w4.set_option("skinny_strips", strips)
     try:
         yield
     finally:
-        w4.set_option("force_path", 0)
-        w4.set_option("splitk", 0)
-        w4.set_option("tiled_bm", 0)
+        for k in ("force_path", "splitk", "tiled_bm", "skinny_strips"):
+            w4.set_option(k, 0)
 
 
 def run_w4a8(dc: DeviceCase):
@@ -79,6 +79,34 @@ def test_int8_partials_bit_exact_tall_tiles(wl, M, split):
     assert np.array_equal(part.cpu().numpy().astype(np.int64), want)
 
 
+@pytest.mark.parametrize("wl", ["w4a8_i8_pc_256x512", "w4a8_i8_g128_o"])
+@pytest.mark.parametrize("M,split", [(17, 1), (100, 3), (128, 2)])
+@pytest.mark.parametrize("wtype", ["int4", "uint4b8"])
+def test_int8_partials_bit_exact_narrow_tiles(wl, M, split, wtype):
+    """64 x 128 tiles (2 column blocks per wave), ragged M and N."""
+    dc = DeviceCase(wl, M, N=272, K=640, seed_base=M * 13 + split, wtype=wtype)
+    packed = w4.prepack_B(dc.w_logical, "i8")
+    aq, _ = w4.quant_act_per_token(dc.a, "i8")
+    gs = -1 if dc.gs == dc.K else dc.gs
+    with options(2, split, 64, 2):
+        assert w4.gemm_plan(M, dc.N, dc.K, gs, w4.I8) == (2, split, 64, 128)
+        part = w4.w4a8_gemm_partials(aq, packed, dc.N, gs, wtype=dc.wtype)
+    want = O.w4a8_group_partials(aq.cpu().numpy(), "i8", dc.case.w_logical.numpy(), dc.K, dc.wtype, dc.gs)
+    assert np.array_equal(part.cpu().numpy().astype(np.int64), want)
+
+
+@pytest.mark.parametrize("wl", ["w4a8_i8_pc_256x512", "w4a8_i8_g128_o", "w4a8_fp8_g128_28672x8192"])
+@pytest.mark.parametrize("M,split", [(33, 1), (130, 2)])
+def test_w4a8_narrow_tiles_outputs(wl, M, split):
+    dc = DeviceCase(wl, M, N=400, K=1280, with_bias=True, seed_base=M + split)
+    with options(2, split, 64, 2):
+        out, *_ = run_w4a8(dc)
+    codes, sa = dc.oracle_quant()
+    ref = dc.oracle_w4a8(codes, sa)
+    assert_w4a8(out, ref, dc.wl.out_dtype, dc.wl.q_dtype, dc.G, label=f"{wl} 64x128 M={M}")
+    assert_w4a8(out, ref, dc.wl.out_dtype, dc.wl.q_dtype, dc.G, strict=True, label=f"{wl} 64x128 strict M={M}")
+
+
 def test_int8_partials_window():
     dc = DeviceCase("w4a8_i8_g128_o", 40, N=512, K=1024, seed_base=3)
     packed = w4.prepack_B(dc.w_logical, "i8")
@@ -90,12 +118,13 @@ def test_int8_partials_window():
     assert np.array_equal(part.cpu().numpy().astype(np.int64), want)
 
 
-@pytest.mark.parametrize("path,M,split,bm", [(1, 5, 4, 0), (2, 70, 2, 64), (2, 70, 2, 128), (2, 150, 1, 128)])
-def test_fp8_partials_within_bound(path, M, split, bm):
+@pytest.mark.parametrize("path,M,split,bm,strips", [(1, 5, 4, 0, 0), (2, 70, 2, 64, 0), (2, 70, 2, 128, 0),
+                                                    (2, 150, 1, 128, 0), (2, 90, 3, 64, 2)])
+def test_fp8_partials_within_bound(path, M, split, bm, strips):
     dc = DeviceCase("w4a8_fp8_g128_28672x8192", M, N=272, K=512, seed_base=11)
     packed = w4.prepack_B(dc.w_logical, "i8")
     aq, _ = w4.quant_act_per_token(dc.a, "fp8")
-    with options(path, split, bm):
+    with options(path, split, bm, strips):
         part = w4.w4a8_gemm_partials(aq, packed, dc.N, 128).cpu().numpy().astype(np.float64)
     codes = aq.cpu().numpy()
     P = O.w4a8_group_partials(codes, "fp8", dc.case.w_logical.numpy(), dc.K, "int4", 128)
