@@ -99,13 +99,14 @@ int cu_count() {
 int64_t resolve_group(int64_t group_size, int64_t K) { return group_size == -1 ? K : group_size; }
 
 // Tile rows of the streaming kernel for 16 < M <= 64 (128-column tiles, one
-// workgroup per CU): 32 up to M = 32 and for grouped problems up to M = 64
-// (more tiles, fewer K splits: faster on the grouped benchmark shapes), 64
-// otherwise, or 64 when 32-row tiles would need more than one round of
-// workgroups; 0 when even 64-row tiles would (the tiled kernel then).
+// workgroup per CU): 32 up to M = 32, 64 above, or 64 when 32-row tiles would
+// need more than one round of workgroups; 0 when even 64-row tiles would, and
+// for grouped problems above M = 32 (the tiled kernel then: its 64 x 128
+// tiles measured faster there on the grouped benchmark shapes).
 int64_t stream_tile_m(int64_t M, int64_t N, bool grouped, int cu) {
   const int64_t cols = (N + 127) / 128;
-  int64_t bm = (M <= 32 || grouped) ? 32 : 64;
+  if (grouped && M > 32) return 0;   // the tiled kernel's 64 x 128 tiles
+  int64_t bm = M <= 32 ? 32 : 64;
   if (bm == 32 && M > 32 && ((M + 31) / 32) * cols > cu) bm = 64;
   return ((M + bm - 1) / bm) * cols > cu ? 0 : bm;
 }
@@ -152,10 +153,10 @@ int plan_with(int64_t M, int64_t N, int64_t K, bool grouped, int op, const Sched
   const int64_t fp = forced.path, fs = forced.splitk;
   const int64_t KB = K / 128;
   const int cu = cu_count();
-  // small M: the small-M kernel; 16 < M <= 64 with symmetric int8: the
-  // streaming kernel (measured faster on every int8 benchmark shape at
-  // M = 32 and on most at M = 64; fp8, whose lookup expansion keeps one wave
-  // per SIMD busy, is faster tiled); larger M: the tiled kernel
+  // small M: the small-M kernel; 16 < M <= 64 with symmetric int8 (grouped:
+  // M <= 32): the streaming kernel (measured faster on every int8 benchmark
+  // shape at M = 32 and per channel at M = 64; fp8, whose lookup expansion
+  // keeps one wave per SIMD busy, is faster tiled); larger M: the tiled kernel
   const bool stream_ok = op == OP_I8 && !zp && sg == 1 && M > 16 && M <= 64 && stream_tile_m(M, N, grouped, cu);
   plan->path = fp ? (int)fp : (M <= 16 ? PATH_SKINNY : stream_ok ? PATH_STREAM : PATH_TILED);
   tiled_tile(op, grouped, 0, &plan->bm, &plan->bn, zp);
@@ -261,6 +262,16 @@ int plan_with(int64_t M, int64_t N, int64_t K, bool grouped, int op, const Sched
       const int64_t need = (op == OP_I8 && !grouped) ? 2LL * cu : (int64_t)cu;
       const bool tall = fbm ? fbm == 128 : (fp8g ? M >= 128 && 2 * tall_tiles >= cu : tall_tiles >= need);
       tiled_tile(op, grouped, tall ? 1 : 0, &plan->bm, &plan->bn, zp);
+      // grouped int8: 64 x 128 tiles while there are at most three per CU
+      // (two workgroups per CU, half the per-group fold work per wave and
+      // step of a 64 x 256 tile; measured faster than both other tiles on the
+      // 7B-layer shapes from M = 33 to 512-1024), for long K (> 8192, where
+      // 128 x 128 tiles with K splits win from M = 256) up to M = 128
+      const int64_t narrow_tiles = ((M + 63) / 64) * ((N + 127) / 128);
+      if (!fbm && op == OP_I8 && grouped && !zp && (K <= 8192 || M <= 128) && narrow_tiles <= 3LL * cu) {
+        plan->bm = 64;
+        plan->bn = 128;
+      }
       // 16-column blocks per wave (the strips field): 2 (tiles of 128
       // columns) or 4 (256 columns: 64-row tiles, and 128-row tiles of
       // symmetric int8 per channel)

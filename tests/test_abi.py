@@ -279,21 +279,32 @@ def test_plan_choices(lib, heuristic_only):
     assert w4.gemm_plan(1, 8192, 8192, 128, w4.BF16)[:2] == (1, 8) and w4.gemm_plan(1, 8192, 8192, 128, w4.BF16)[3] == 32
     assert w4.gemm_plan(16, 22016, 4096, 128, w4.I8)[3] == 32
     assert w4.gemm_plan(16, 4096, 11008, 128, w4.I8)[3] == 16
-    # 16 < M <= 64, 8-bit operands: the streaming kernel, 32- or 64-row
-    # tiles of 128 columns, K split to one workgroup per CU
-    assert w4.gemm_plan(64, 12288, 4096, 128, w4.I8) == (3, 1, 32, 128)       # 192 tiles
+    # 16 < M <= 64, int8 (grouped: M <= 32): the streaming kernel, 32- or
+    # 64-row tiles of 128 columns, K split to one workgroup per CU
     assert w4.gemm_plan(32, 4096, 11008, 128, w4.I8) == (3, 8, 32, 128)       # 32 tiles, 86 K blocks
     assert w4.gemm_plan(32, 4096, 4096, 128, w4.I8) == (3, 8, 32, 128)
+    assert w4.gemm_plan(64, 8192, 21760, -1, w4.I8) == (3, 4, 64, 128)        # 64 tiles
+    assert w4.gemm_plan(48, 8192, 21760, -1, w4.I8) == (3, 4, 64, 128)
+    assert w4.gemm_plan(32, 8192, 21760, -1, w4.I8) == (3, 4, 32, 128)
     # ... whose grouped K range must fit the scale table (64 groups of 128-column tiles)
     assert w4.gemm_plan(32, 28672, 16384, 128, w4.I8) == (3, 2, 32, 128)      # 224 tiles
     # more 32-row tiles than CUs: 64-row tiles; more 64-row tiles than CUs: tiled
-    assert w4.gemm_plan(64, 22016, 4096, 128, w4.I8) == (3, 1, 64, 128)       # 172 tiles
-    assert w4.gemm_plan(64, 65536, 4096, 128, w4.I8)[0] == 2
+    assert w4.gemm_plan(64, 65536, 8192, -1, w4.I8)[0] == 2
+    # grouped above M = 32: the tiled kernel's 64 x 128 tiles
+    assert w4.gemm_plan(64, 12288, 4096, 128, w4.I8) == (2, 2, 64, 128)       # 96 tiles
+    assert w4.gemm_plan(64, 22016, 4096, 128, w4.I8) == (2, 1, 64, 128)       # 172 tiles
+    assert w4.gemm_plan(64, 4096, 11008, 128, w4.I8) == (2, 8, 64, 128)       # 32 tiles, long K
     # fp8 stays on the tiled kernel
     assert w4.gemm_plan(32, 28672, 8192, 128, w4.FP8_E4M3)[0] == 2
-    # grouped int8 and fp8: 128 x 128 tiles once there is one per CU, else 64 x 256
-    assert w4.gemm_plan(1024, 22016, 4096, 128, w4.I8)[2:] == (128, 128)
-    assert w4.gemm_plan(128, 22016, 4096, 128, w4.I8)[2:] == (64, 256)
+    # grouped int8 and fp8: 128 x 128 tiles once there is one per CU, else 64 x 256;
+    # grouped int8 with K <= 8192 takes 64 x 128 tiles while they number at most 3 per CU
+    assert w4.gemm_plan(1024, 22016, 4096, 128, w4.I8)[2:] == (128, 128)      # 2752 narrow tiles
+    assert w4.gemm_plan(128, 22016, 4096, 128, w4.I8)[2:] == (64, 128)        # 344
+    assert w4.gemm_plan(512, 12288, 4096, 128, w4.I8) == (2, 1, 64, 128)      # 768
+    assert w4.gemm_plan(1024, 12288, 4096, 128, w4.I8)[2:] == (128, 128)      # 1536
+    assert w4.gemm_plan(256, 4096, 4096, 128, w4.I8) == (2, 2, 64, 128)       # 128: two K splits
+    assert w4.gemm_plan(256, 4096, 11008, 128, w4.I8)[2:] == (64, 256)        # K > 8192
+    assert w4.gemm_plan(256, 28672, 8192, 128, w4.FP8_E4M3)[2:] == (128, 128)
     assert w4.gemm_plan(8192, 28672, 8192, 128, w4.FP8_E4M3)[1:] == (1, 128, 128)
     # grouped fp8: the tall tile from M = 128 (half a workgroup per CU), the
     # most K splits that fit two workgroups per CU
@@ -303,8 +314,8 @@ def test_plan_choices(lib, heuristic_only):
     # most that keep one workgroup per CU (at least 4 K blocks each)
     try:
         w4.set_option("force_path", 2)
-        assert w4.gemm_plan(64, 12288, 4096, 128, w4.I8)[1] == 4          # 48 tiles
-        assert w4.gemm_plan(32, 4096, 11008, 128, w4.I8)[1] == 16         # 16 tiles, 86 K blocks
+        assert w4.gemm_plan(64, 12288, 4096, 128, w4.I8) == (2, 2, 64, 128)   # 96 tiles
+        assert w4.gemm_plan(32, 4096, 11008, 128, w4.I8) == (2, 8, 64, 128)   # 32 tiles, 86 K blocks
         assert w4.gemm_plan(32, 28672, 8192, 128, w4.FP8_E4M3)[2:] == (64, 256)
         assert w4.gemm_plan(64, 28672, 8192, 128, w4.FP8_E4M3)[1:] == (4, 64, 256)
         assert w4.gemm_plan(64, 8192, 21760, -1, w4.I8)[1] == 8
