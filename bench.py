@@ -343,7 +343,7 @@ def summarize_counters(set_name: str, dirs) -> int:
               f"({XCDS} XCDs x duration); MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / ({SIMDS} SIMDs x GRBM_GUI_ACTIVE / "
               f"{XCDS}); MFMA ops = 512 x SQ_INSTS_VALU_MFMA_MOPS_(I8 + F8) (equal to 2 M N K when the tile covers "
               "M and N exactly); VALU / MFMA = SQ_INSTS_VALU / SQ_INSTS_MFMA; wait = SQ_WAIT_INST_ANY / "
-              "SQ_WAVE_CYCLES (share of resident wave cycles spent waiting on s_waitcnt); the clock and MFMA busy "
+              "SQ_WAVE_CYCLES (share of resident wave cycles in which the wave had an instruction waiting to issue: on a dependency, a wait count or a unit busy with another wave); the clock and MFMA busy "
               "columns hold for launches of ~50 us or more (GRBM_GUI_ACTIVE also counts cycles outside a short "
               "kernel's own timestamps); L2 hit = TCC_HIT / (TCC_HIT + "
               "TCC_MISS); EA reads = TCC_EA0_RDREQ (requests from the L2s to the fabric, each 64 B or 128 B; "
