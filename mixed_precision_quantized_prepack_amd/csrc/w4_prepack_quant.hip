@@ -337,6 +337,69 @@ __global__ __launch_bounds__(THREADS, (THREADS == 256 && QT == W4_I8) ? 3 : 1) v
   }
 }
 
+// Per-token quantisation of a few long rows: P workgroups per row, so that a
+// batch of a few tokens keeps P CUs per row busy instead of one.  Every
+// workgroup finds the maximum of the whole row (its re-reads of the row hit
+// the L2; the maximum is exact in any order) and codes its own P-th of the
+// chunks.  Scale and codes are those of w4_quant_kernel; part 0 writes the
+// scale.
+#ifndef W4_QUANT_PARTS_MAX
+#define W4_QUANT_PARTS_MAX 16
+#endif
+template <int XT, int QT>
+__global__ __launch_bounds__(256) void w4_quant_parts_kernel(const uint16_t* __restrict__ x,
+                                                             uint8_t* __restrict__ xq,
+                                                             float* __restrict__ scales, int64_t K) {
+  constexpr int T = 256;
+  constexpr int B = 8;   // chunk loads per thread in flight in the maximum pass
+  const int64_t row = blockIdx.y;
+  const int part = blockIdx.x, parts = gridDim.x;
+  const int tid = threadIdx.x;
+  const int nchunks = (int)(K / 8);
+  const __amdgpu_buffer_rsrc_t rx = row_rsrc(x + row * K, K * 2);
+  const __amdgpu_buffer_rsrc_t rq = row_rsrc(xq + row * K, K);
+  auto load = [&](int idx) -> uint4 {
+    const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(
+        rx, (int)(idx < nchunks ? (uint32_t)idx * 16u : kRowOutOfRange), 0, 0);
+    return make_uint4(w.x, w.y, w.z, w.w);
+  };
+  auto store = [&](int idx, uint2 q) {
+    __builtin_amdgcn_raw_buffer_store_b64(u32x2{q.x, q.y}, rq, (int)((uint32_t)idx * 8u), 0, 0);
+  };
+  __shared__ float wave_max[T / 64];
+  // the whole row's maximum (chunks past the row read zero)
+  float amax = 0.0f;
+  for (int base = 0; base < nchunks; base += B * T) {
+    uint4 v[B];
+#pragma unroll
+    for (int c = 0; c < B; ++c) v[c] = load(base + c * T + tid);
+#pragma unroll
+    for (int c = 0; c < B; ++c) amax = chunk_absmax<XT>(amax, v[c]);
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+  if ((tid & 63) == 0) wave_max[tid >> 6] = amax;
+  __syncthreads();
+  amax = wave_max[0];
+#pragma unroll
+  for (int w = 1; w < T / 64; ++w) amax = fmaxf(amax, wave_max[w]);
+
+  const float s = amax / ((QT == W4_I8) ? 127.0f : 448.0f);
+  if (part == 0 && tid == 0) scales[row] = s;
+  const int c0 = (int)((int64_t)nchunks * part / parts);
+  const int c1 = (int)((int64_t)nchunks * (part + 1) / parts);
+  if (s == 0.0f) {
+    for (int idx = c0 + tid; idx < c1; idx += T) store(idx, make_uint2(0u, 0u));
+    return;
+  }
+  const float y = 1.0f / s;
+  if (s >= 0x1p-100f) {
+    for (int idx = c0 + tid; idx < c1; idx += T) store(idx, quant_chunk<XT, QT, true>(load(idx), s, y));
+  } else {
+    for (int idx = c0 + tid; idx < c1; idx += T) store(idx, quant_chunk<XT, QT, false>(load(idx), s, y));
+  }
+}
+
 // The tensor's scale from its row maxima (held in scales[0, M)):
 // s = fp32(max_m scales[m] / qmax), written to every scales[m].  One
 // workgroup; each thread writes only the entries it has read, after the
@@ -409,6 +472,23 @@ static void launch_quant_n(const void* x, int x_dtype, void* xq, int q_dtype, fl
 
 hipError_t launch_quant(const void* x, int x_dtype, void* xq, int q_dtype, float* scales, int64_t M,
                         int64_t K, hipStream_t stream) {
+  // a few long rows: several workgroups per row (P = 16 rows' worth of CUs
+  // per row up to M = 16, 4 up to M = 64)
+  if (K >= 8192 && M > 0 && M <= 64) {
+    const int parts = M <= 16 ? W4_QUANT_PARTS_MAX : 4;
+    const dim3 grid((unsigned)parts, (unsigned)M), block(256);
+    const uint16_t* xp = (const uint16_t*)x;
+    uint8_t* qp = (uint8_t*)xq;
+    if (x_dtype == W4_F16 && q_dtype == W4_I8)
+      hipLaunchKernelGGL((w4_quant_parts_kernel<W4_F16, W4_I8>), grid, block, 0, stream, xp, qp, scales, K);
+    else if (x_dtype == W4_F16)
+      hipLaunchKernelGGL((w4_quant_parts_kernel<W4_F16, W4_FP8_E4M3>), grid, block, 0, stream, xp, qp, scales, K);
+    else if (q_dtype == W4_I8)
+      hipLaunchKernelGGL((w4_quant_parts_kernel<W4_BF16, W4_I8>), grid, block, 0, stream, xp, qp, scales, K);
+    else
+      hipLaunchKernelGGL((w4_quant_parts_kernel<W4_BF16, W4_FP8_E4M3>), grid, block, 0, stream, xp, qp, scales, K);
+    return hipGetLastError();
+  }
   launch_quant_n<false>(x, x_dtype, xq, q_dtype, scales, M, K, nullptr, 0.0f, 0, stream);
   return hipGetLastError();
 }

@@ -33,7 +33,11 @@ def test_prepack_bit_exact_full_size(N, K, operand):
                                       (5, 8, "normal"), (7, 40000, "normal"), (33, 21760, "wide"),
                                       (64, 8192, "normal"),
                                       # rows longer than the register-resident chunks: tail pass
-                                      (520, 30000, "normal"), (2, 100000, "wide")])
+                                      (520, 30000, "normal"), (2, 100000, "wide"),
+                                      # a few long rows: several workgroups per row, chunk counts
+                                      # that do not divide evenly among them
+                                      (1, 21760, "normal"), (16, 21760, "wide"), (1, 8192, "normal"),
+                                      (40, 8200, "normal"), (17, 9000, "wide")])
 def test_quant_bit_exact(x_dtype, q_dtype, M, K, dist):
     x = workloads.activations(M, K, x_dtype, seed=M * 31 + K, dist=dist)
     if M >= 3:
@@ -57,6 +61,21 @@ def test_quant_bit_exact_full_size(M, K, x_dtype, q_dtype):
     qo, so = O.quant_act_per_token(bits16(x), x_dtype, q_dtype)
     assert np.array_equal(s.cpu().numpy().view(np.uint32), so.view(np.uint32))
     assert np.array_equal(q.cpu().numpy().view(np.uint8), qo.view(np.uint8))
+
+
+@pytest.mark.parametrize("M,K", [(2, 21760), (12, 8192), (48, 16392)])
+def test_quant_row_maximum_in_any_part(M, K):
+    """Rows split over several workgroups: the row maximum placed in the
+    first, a middle and the last chunk of different rows; every workgroup
+    must code with the same scale."""
+    x = workloads.activations(M, K, "f16", seed=M + K)
+    for m in range(M):
+        pos = [0, K // 2 + 3, K - 1][m % 3]
+        x[m, pos] = 60.0 if m % 2 else -60.0
+    q, s = w4.quant_act_per_token(x.to(DEV), "i8")
+    qo, so = O.quant_act_per_token(bits16(x), "f16", "i8")
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), so.view(np.uint32))
+    assert np.array_equal(q.cpu().numpy(), qo)
 
 
 def test_quant_empty_rows_is_a_no_op():
