@@ -58,6 +58,7 @@ CALIB_BYTES = 256 << 20          # plain copy of known size: reads and writes th
 POOL_BYTES = 512 << 20           # weight copies rotated per workload: twice the last-level cache
 GEMM_SOURCES = ["mixed_precision_quantized_prepack_amd/csrc/w4_gemm.hip",
                 "mixed_precision_quantized_prepack_amd/csrc/w4_gemm_stream.hip",
+                "mixed_precision_quantized_prepack_amd/csrc/w4_gemm_pingpong.hip",
                 "mixed_precision_quantized_prepack_amd/csrc/w4_gemm_common.h",
                 "mixed_precision_quantized_prepack_amd/csrc/w4_device.h",
                 "mixed_precision_quantized_prepack_amd/csrc/w4_api.cpp"]
@@ -108,7 +109,7 @@ def kernel_label(plan, wl) -> str:
     op = {"i8": "int8", "fp8": "fp8", "f16": "fp16", "bf16": "bf16"}[op_name(wl)]
     if path == 1:
         return f"w4_gemm_skinny<{op}, {grp}, {tn // 16} strip(s)>"
-    kern = "w4_gemm_stream" if path == 3 else "w4_gemm_tiled"
+    kern = "w4_gemm_stream" if path == 3 else ("w4_gemm_pingpong" if tm == 256 else "w4_gemm_tiled")
     return f"{kern}<{op}, {grp}, {tm}x{tn} tile, {'K split' if split > 1 else 'no K split'}>"
 
 
@@ -406,6 +407,8 @@ def kernel_key_of(wl, plan) -> str:
     if path == 1:
         return f"w4::w4_gemm_skinny<{op}, {grouped}, false, {tn // 16}, false, false, 1, false, false>"
     nt, mt = tn // 64, tm // 16
+    if path == 2 and tm == 256:
+        return f"w4::w4_gemm_pingpong<false, {'true' if split > 1 else 'false'}, false>"
     if path == 3:
         stages = min(8, (120 * 1024) // (mt * 16 * 128 + 4 * nt * 1024))
         return (f"w4::w4_gemm_stream<{op}, {grouped}, false, {nt}, {mt}, {stages}, "
@@ -420,7 +423,8 @@ def grid_threads(wl, plan, M: int) -> int:
     if path == 1:
         # one workgroup per tn columns, 64 max(S, 4 strips) threads
         return (wl.N // tn) * 64 * max(split, 4 * (tn // 16))
-    return ((M + tm - 1) // tm) * ((wl.N + tn - 1) // tn) * split * 256
+    threads = 512 if (path == 2 and tm == 256) else 256   # the ping-pong kernel: eight waves
+    return ((M + tm - 1) // tm) * ((wl.N + tn - 1) // tn) * split * threads
 
 
 # ---------------------------------------------------------------------------

@@ -414,8 +414,10 @@ W4_API int w4a16_gemm_partials(const void* a, int a_dtype, const void* b_packed,
  *                  kernel)
  *   "tiled_bm"   : 0 = automatic, 64 or 128 rows per tile of the tiled kernel
  *                  (128 only for int8 and fp8 activations; by default its tile
- *                  is 128 x 256 for int8 per channel, 128 x 128 otherwise), 32,
- *                  64 or 128 for the streaming kernel
+ *                  is 128 x 256 for int8 per channel, 128 x 128 otherwise), 256
+ *                  for its ping-pong form (256 x 256 tiles of eight waves;
+ *                  symmetric int8 per channel only), 32, 64 or 128 for the
+ *                  streaming kernel
  *   "norm_exact_sum": 1 = w4_rmsnorm_quant_per_token always re-sums the squares
  *                  with error-free pair arithmetic (the path it otherwise takes
  *                  only when the fast sum cannot decide r); same results
@@ -446,7 +448,7 @@ W4_API int64_t w4_get_option(const char* key);
  * (W4_I8, W4_FP8_E4M3, W4_F16, W4_BF16), group_mode (0 = one group over K,
  * 1 = group size 128), N, K and m_lo <= M <= m_hi take path (0 = heuristic,
  * 1 = small-M, which needs m_hi <= 16, 2 = tiled, 3 = streaming), splitk
- * (0 = heuristic, 1..64), tile_m (0, 32, 64 or 128) and strips (0, 1, 2 or
+ * (0 = heuristic, 1..64), tile_m (0, 32, 64, 128 or 256) and strips (0, 1, 2 or
  * 4; the meanings of the options above).  This is also the
  * per-shape override of the heuristic.  The workspace size the GEMM needs
  * follows the schedule in force (w4_gemm_workspace_bytes and w4_gemm_plan

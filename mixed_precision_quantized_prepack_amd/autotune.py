@@ -62,8 +62,9 @@ def candidates(a_dtype: int, grouped: bool, M: int, N: int, K: int):
                 if s <= smax and s <= K // 128:
                     out.append((1, s, 0, strips))
     # tiled: the default tile for the rows (0), or 128 columns (2 blocks per
-    # wave) for 8-bit operands with 64-row tiles
-    for tm, nt in (((64, 0), (64, 2), (128, 0)) if byte else ((64, 0),)):
+    # wave) for 8-bit operands with 64-row tiles; 256 rows: the ping-pong
+    # kernel (int8 per channel; other problems refuse it)
+    for tm, nt in (((64, 0), (64, 2), (128, 0), (256, 0)) if byte else ((64, 0),)):
         for s in (1, 2, 4, 8, 16):
             if s <= K // 128:
                 out.append((2, s, tm, nt))

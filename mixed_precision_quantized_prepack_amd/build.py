@@ -42,7 +42,7 @@ COMMON_FLAGS = [
     "-I", INCLUDE, "-I", CSRC,
 ]
 
-SOURCES = ["w4_api.cpp", "w4_prepack_quant.hip", "w4_gemm.hip", "w4_gemm_stream.hip"]
+SOURCES = ["w4_api.cpp", "w4_prepack_quant.hip", "w4_gemm.hip", "w4_gemm_stream.hip", "w4_gemm_pingpong.hip"]
 
 
 def _compile(src: str, verbose: bool, build_dir: str, extra) -> str:

@@ -1250,6 +1250,11 @@ static hipError_t launch_typed(const GemmArgs& args, const GemmPlan& plan, hipSt
                            args, 1);
     }
   };
+  if (plan.bm == 256) {
+    // 256 x 256 tiles: the ping-pong kernel (symmetric int8 per channel)
+    if constexpr (OP == OP_I8 && !GROUPED && !ZP && SG == 1) return launch_pingpong(args, FLIP, plan, stream);
+    return hipErrorInvalidValue;
+  }
   if constexpr (kByte) {
     if (plan.bm == 128 && plan.bn == 256) {
       // the 128 x 256 tile exists for symmetric int8 per channel only

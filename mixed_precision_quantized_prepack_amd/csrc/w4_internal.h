@@ -92,6 +92,8 @@ hipError_t launch_gemm(const GemmArgs& args, int op, bool grouped, bool flip, bo
 
 // The streaming kernel (8-bit operands, symmetric weights; plan.path ==
 // PATH_STREAM): tiles 32 x 256, 64 x 256 and 128 x 128.
+// Ping-pong kernel (int8 per channel, symmetric weights, 256 x 256 tiles).
+hipError_t launch_pingpong(const GemmArgs& args, bool flip, const GemmPlan& plan, hipStream_t stream);
 hipError_t launch_stream(const GemmArgs& args, int op, bool grouped, bool flip, const GemmPlan& plan,
                          hipStream_t stream);
 // Steps the streaming kernel's LDS ring holds for a tile of 16 mt rows and 4 nt

@@ -269,7 +269,24 @@ def test_plan_choices(lib, heuristic_only):
     assert plans[1][3] == 32                                     # two 16-column strips per wave
     assert plans[64] == (3, 4, 64, 128)                         # streaming kernel, 64 tiles x 4 K splits
     assert [plans[M][1] for M in (128, 256, 512, 1024)] == [4, 4, 2, 1]
-    assert plans[4096][1:] == (1, 128, 256)                      # one 128 x 256 tile per workgroup
+    assert plans[4096][1:] == (1, 256, 256)                      # ping-pong: one 256 x 256 tile per CU
+    assert w4.gemm_plan(2048, 8192, 21760, -1, w4.I8)[1:] == (1, 256, 256)   # 256 tiles
+    assert w4.gemm_plan(2048, 4096, 21760, -1, w4.I8)[1:] == (1, 64, 256)    # 256 tall tiles: 64 rows
+    assert w4.gemm_plan(4096, 8192, 21760, 128, w4.I8)[2:] == (128, 128)     # grouped: tiled
+    assert w4.gemm_plan(4096, 8192, 21760, -1, w4.FP8_E4M3)[2:] == (128, 128)
+    try:
+        w4.set_option("tiled_bm", 256)
+        assert w4.gemm_plan(300, 8192, 21760, -1, w4.I8) == (2, 4, 256, 256)    # 64 tiles x 4 K splits
+        with pytest.raises(w4.W4Error):
+            w4.gemm_plan(300, 8192, 21760, 128, w4.I8)
+        with pytest.raises(w4.W4Error):
+            w4.gemm_plan(300, 8192, 21760, -1, w4.FP8_E4M3)
+        w4.set_option("skinny_strips", 2)
+        with pytest.raises(w4.W4Error):
+            w4.gemm_plan(300, 8192, 21760, -1, w4.I8)
+    finally:
+        w4.set_option("tiled_bm", 0)
+        w4.set_option("skinny_strips", 0)
     # grouped small M: two strips from M = 8 when N >= 8192, at any M when
     # N >= 16384 or (N >= 8192 and K >= 8192), else one
     assert w4.gemm_plan(1, 12288, 4096, 128, w4.I8)[3] == 16
