@@ -109,7 +109,7 @@ def kernel_label(plan, wl) -> str:
     op = {"i8": "int8", "fp8": "fp8", "f16": "fp16", "bf16": "bf16"}[op_name(wl)]
     if path == 1:
         return f"w4_gemm_skinny<{op}, {grp}, {tn // 16} strip(s)>"
-    kern = "w4_gemm_stream" if path == 3 else ("w4_gemm_pingpong" if tm == 256 else "w4_gemm_tiled")
+    kern = {3: "w4_gemm_stream", 4: "w4_gemm_pingpong"}.get(path, "w4_gemm_tiled")
     return f"{kern}<{op}, {grp}, {tm}x{tn} tile, {'K split' if split > 1 else 'no K split'}>"
 
 
@@ -407,8 +407,8 @@ def kernel_key_of(wl, plan) -> str:
     if path == 1:
         return f"w4::w4_gemm_skinny<{op}, {grouped}, false, {tn // 16}, false, false, 1, false, false>"
     nt, mt = tn // 64, tm // 16
-    if path == 2 and tm == 256:
-        return f"w4::w4_gemm_pingpong<false, {'true' if split > 1 else 'false'}, false>"
+    if path == 4:
+        return f"w4::w4_gemm_pingpong<{tm // 32}, false, {'true' if split > 1 else 'false'}, false>"
     if path == 3:
         stages = min(8, (120 * 1024) // (mt * 16 * 128 + 4 * nt * 1024))
         return (f"w4::w4_gemm_stream<{op}, {grouped}, false, {nt}, {mt}, {stages}, "
@@ -423,7 +423,7 @@ def grid_threads(wl, plan, M: int) -> int:
     if path == 1:
         # one workgroup per tn columns, 64 max(S, 4 strips) threads
         return (wl.N // tn) * 64 * max(split, 4 * (tn // 16))
-    threads = 512 if (path == 2 and tm == 256) else 256   # the ping-pong kernel: eight waves
+    threads = 512 if path == 4 else 256   # the ping-pong kernel: eight waves
     return ((M + tm - 1) // tm) * ((wl.N + tn - 1) // tn) * split * threads
 
 

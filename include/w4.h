@@ -401,7 +401,7 @@ W4_API int w4a16_gemm_partials(const void* a, int a_dtype, const void* b_packed,
  * calls; set them before issuing work).
  *   "force_path" : 0 = automatic, 1 = small-M kernel, 2 = tiled kernel,
  *                  3 = streaming kernel (int8 / fp8 activations, symmetric
- *                  weights)
+ *                  weights), 4 = ping-pong kernel (symmetric int8 per channel)
  *   "splitk"     : 0 = automatic, else the number of K splits (tiled and
  *                  streaming kernels, 1..64) or waves splitting K (small-M
  *                  kernel: 1..16 for ungrouped int8 / fp8, 1..8 otherwise)
@@ -414,10 +414,10 @@ W4_API int w4a16_gemm_partials(const void* a, int a_dtype, const void* b_packed,
  *                  kernel)
  *   "tiled_bm"   : 0 = automatic, 64 or 128 rows per tile of the tiled kernel
  *                  (128 only for int8 and fp8 activations; by default its tile
- *                  is 128 x 256 for int8 per channel, 128 x 128 otherwise), 256
- *                  for its ping-pong form (256 x 256 tiles of eight waves;
- *                  symmetric int8 per channel only), 32, 64 or 128 for the
- *                  streaming kernel
+ *                  is 128 x 256 for int8 per channel, 128 x 128 otherwise), 32,
+ *                  64 or 128 for the streaming kernel, 128 or 256 for the
+ *                  ping-pong kernel (tiles of 256 columns; 256 alone selects
+ *                  that kernel)
  *   "norm_exact_sum": 1 = w4_rmsnorm_quant_per_token always re-sums the squares
  *                  with error-free pair arithmetic (the path it otherwise takes
  *                  only when the fast sum cannot decide r); same results
@@ -447,7 +447,8 @@ W4_API int64_t w4_get_option(const char* key);
  * w4_schedule_add registers a run-time entry: problems with this a_dtype
  * (W4_I8, W4_FP8_E4M3, W4_F16, W4_BF16), group_mode (0 = one group over K,
  * 1 = group size 128), N, K and m_lo <= M <= m_hi take path (0 = heuristic,
- * 1 = small-M, which needs m_hi <= 16, 2 = tiled, 3 = streaming), splitk
+ * 1 = small-M, which needs m_hi <= 16, 2 = tiled, 3 = streaming,
+ * 4 = ping-pong), splitk
  * (0 = heuristic, 1..64), tile_m (0, 32, 64, 128 or 256) and strips (0, 1, 2 or
  * 4; the meanings of the options above).  This is also the
  * per-shape override of the heuristic.  The workspace size the GEMM needs
@@ -462,7 +463,7 @@ W4_API int w4_schedule_clear(void);
 
 /* The kernel the GEMM entry points would choose for this problem under the
  * current options, for logging and tests: *path (1 = small-M, 2 = tiled,
- * 3 = streaming), its
+ * 3 = streaming, 4 = ping-pong), its
  * K split (*splitk), and the output tile one workgroup computes (*tile_m rows
  * x *tile_n columns; for the small-M kernel tile_m is 16).  Any out pointer
  * may be NULL.  Errors as for the GEMM's shape checks. */

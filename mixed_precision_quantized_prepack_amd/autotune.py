@@ -62,12 +62,17 @@ def candidates(a_dtype: int, grouped: bool, M: int, N: int, K: int):
                 if s <= smax and s <= K // 128:
                     out.append((1, s, 0, strips))
     # tiled: the default tile for the rows (0), or 128 columns (2 blocks per
-    # wave) for 8-bit operands with 64-row tiles; 256 rows: the ping-pong
-    # kernel (int8 per channel; other problems refuse it)
-    for tm, nt in (((64, 0), (64, 2), (128, 0), (256, 0)) if byte else ((64, 0),)):
+    # wave) for 8-bit operands with 64-row tiles
+    for tm, nt in (((64, 0), (64, 2), (128, 0)) if byte else ((64, 0),)):
         for s in (1, 2, 4, 8, 16):
             if s <= K // 128:
                 out.append((2, s, tm, nt))
+    # the ping-pong kernel (int8 per channel; other problems refuse it)
+    if a_dtype == w4.I8 and not grouped and M > 64:
+        for tm in (128, 256):
+            for s in (1, 2, 4, 8):
+                if s <= K // 128:
+                    out.append((4, s, tm, 0))
     if byte and 16 < M <= 256:
         for tm in (32, 64, 128):
             for nt in ((2,) if tm == 128 else (2, 4)):
@@ -214,7 +219,7 @@ def same_schedule(plan, cand) -> bool:
     cp, cs, ctm, cst = cand
     if cp != path or (cs != split and cs != 0):
         return False
-    if path == 2:
+    if path in (2, 4):
         return ctm == tm and (cst * 64 == tn or cst == 0)
     if path == 3:
         return (ctm == tm or ctm == 0) and (cst * 64 == tn or cst == 0)

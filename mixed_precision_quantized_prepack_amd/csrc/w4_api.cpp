@@ -158,7 +158,18 @@ int plan_with(int64_t M, int64_t N, int64_t K, bool grouped, int op, const Sched
   // shape at M = 32 and per channel at M = 64; fp8, whose lookup expansion
   // keeps one wave per SIMD busy, is faster tiled); larger M: the tiled kernel
   const bool stream_ok = op == OP_I8 && !zp && sg == 1 && M > 16 && M <= 64 && stream_tile_m(M, N, grouped, cu);
-  plan->path = fp ? (int)fp : (M <= 16 ? PATH_SKINNY : stream_ok ? PATH_STREAM : PATH_TILED);
+  // symmetric int8 per channel with a 256 x 256 tile per two CUs or more:
+  // the ping-pong kernel (one eight-wave workgroup per CU whose two halves
+  // take turns on the MFMAs, K split to fill the CUs; on 8192 x 21760
+  // measured 4-5% faster than two tiled workgroups per CU at M = 2048-8192
+  // and 3.7% at M = 1024 with two K splits; at M = 512 within 2%, at
+  // M = 256 slower); a forced 256-row tile selects it too
+  const bool pc8 = op == OP_I8 && !grouped && !zp && sg == 1;
+  const int64_t pp_tiles = ((M + 255) / 256) * ((N + 255) / 256);
+  const bool pp_ok =
+      pc8 && M > 64 && (forced.tile_m == 256 || (!forced.tile_m && !forced.strips && 2 * pp_tiles >= cu));
+  plan->path = fp ? (int)fp
+                  : (M <= 16 ? PATH_SKINNY : stream_ok ? PATH_STREAM : pp_ok ? PATH_PINGPONG : PATH_TILED);
   tiled_tile(op, grouped, 0, &plan->bm, &plan->bn, zp);
   // strips of 16 columns per wave of the small-M kernel: two strips share
   // one activation fragment.  Grouped problems take two when N leaves enough
@@ -183,6 +194,29 @@ int plan_with(int64_t M, int64_t N, int64_t K, bool grouped, int op, const Sched
       // (whose workspace size callers query) has none: no K split either
       one_split = zp && skinny_table_bytes(op, grouped, groups, 1) <= kSkinnyTableMax;
     }
+  }
+  if (plan->path == PATH_PINGPONG) {
+    // ping-pong kernel: symmetric int8 per channel, 256 or 128 rows x 256
+    // columns, one workgroup per CU
+    if (!pc8) return fail(W4_E_UNSUPPORTED, "the ping-pong kernel takes symmetric int8 per channel");
+    const int64_t fbm = forced.tile_m;
+    if (fbm && fbm != 128 && fbm != 256)
+      return fail(W4_E_SHAPE, "ping-pong kernel: tile rows 128 or 256 (got %lld)", (long long)fbm);
+    if (forced.strips && forced.strips != 4)
+      return fail(W4_E_SHAPE, "ping-pong kernel: tiles are 256 columns wide (4 column blocks per wave)");
+    plan->bm = (int)(fbm ? fbm : 256);   // 128-row tiles (forced) measured slower at every M
+    plan->bn = 256;
+    const int64_t tiles = ((M + plan->bm - 1) / plan->bm) * ((N + 255) / 256);
+    int64_t s = fs;
+    if (!s) {
+      s = 1;
+      while (tiles * s < cu && s * 2 <= 8) s *= 2;
+      while (s > 1 && KB / s < 4) s /= 2;
+    }
+    if (s < 1 || s > 64 || s > KB)
+      return fail(W4_E_SHAPE, "ping-pong kernel: K split %lld not in [1, min(64, K/128)]", (long long)s);
+    plan->splitk = (int)s;
+    return W4_OK;
   }
   if (plan->path == PATH_STREAM) {
     // streaming kernel: 8-bit symmetric operands, one workgroup per CU
@@ -254,7 +288,8 @@ int plan_with(int64_t M, int64_t N, int64_t K, bool grouped, int op, const Sched
     const bool byte = op == OP_I8 || op == OP_FP8;
     const bool fp8g = op == OP_FP8 && grouped;
     const int64_t fbm = forced.tile_m;
-    if (fbm == 32) return fail(W4_E_SHAPE, "tiled_bm=32 is for the streaming kernel");
+    if (fbm == 32 || fbm == 256)
+      return fail(W4_E_SHAPE, "tiled_bm=%lld is for the %s kernel", (long long)fbm, fbm == 32 ? "streaming" : "ping-pong");
     if (byte) {
       int tall_bm, tall_bn;
       tiled_tile(op, grouped, 1, &tall_bm, &tall_bn, zp);
@@ -272,27 +307,12 @@ int plan_with(int64_t M, int64_t N, int64_t K, bool grouped, int op, const Sched
         plan->bm = 64;
         plan->bn = 128;
       }
-      // symmetric int8 per channel with 128 x 256 tiles and at least one
-      // 256 x 256 tile per CU: the ping-pong kernel (one eight-wave workgroup
-      // per CU, two 128 x 256 halves taking turns on the MFMAs; measured
-      // 4-5% faster than two tiled workgroups per CU at M = 2048-8192)
-      const bool pc8 = op == OP_I8 && !grouped && !zp;
-      const int64_t pp_tiles = ((M + 255) / 256) * ((N + 255) / 256);
-      if (fbm == 256) {
-        if (!pc8) return fail(W4_E_SHAPE, "tiled_bm=256 (the ping-pong kernel) is for symmetric int8 per channel");
-        plan->bm = 256;
-        plan->bn = 256;
-      } else if (!fbm && !forced.strips && pc8 && plan->bm == 128 && pp_tiles >= cu) {
-        plan->bm = 256;
-        plan->bn = 256;
-      }
       // 16-column blocks per wave (the strips field): 2 (tiles of 128
       // columns) or 4 (256 columns: 64-row tiles, and 128-row tiles of
       // symmetric int8 per channel)
       const int64_t fnt = forced.strips;
       if (fnt) {
         if (fnt != 2 && fnt != 4) return fail(W4_E_SHAPE, "tiled kernel: 2 or 4 column blocks per wave");
-        if (fnt != 4 && plan->bm == 256) return fail(W4_E_SHAPE, "tiled kernel: 256-row tiles are 256 columns wide");
         if (fnt == 4 && plan->bm == 128 && !(op == OP_I8 && !grouped && !zp))
           return fail(W4_E_SHAPE, "tiled kernel: 128 x 256 tiles are for symmetric int8 per channel");
         plan->bn = (int)(64 * fnt);
@@ -317,10 +337,7 @@ int plan_with(int64_t M, int64_t N, int64_t K, bool grouped, int op, const Sched
       // fold): the most that fit two.
       const int64_t tiles = ((M + plan->bm - 1) / plan->bm) * ((N + plan->bn - 1) / plan->bn);
       s = 1;
-      if (plan->bm == 256) {
-        // one workgroup per CU (only forced tiles can number fewer)
-        while (tiles * s < cu && s * 2 <= 8) s *= 2;
-      } else if (op == OP_I8 && grouped) {
+      if (op == OP_I8 && grouped) {
         while (tiles * s * 2 <= cu && s * 2 <= 16) s *= 2;
       } else if (fp8g) {
         while (tiles * s * 2 <= 2LL * cu && s * 2 <= 16) s *= 2;
@@ -871,7 +888,7 @@ int w4a16_gemm_partials(const void* a, int a_dtype, const void* b_packed, int wt
 int w4_set_option(const char* key, int64_t value) {
   if (!key) return fail(W4_E_NULL, "key is required");
   if (!strcmp(key, "force_path")) {
-    if (value < 0 || value > 3) return fail(W4_E_SHAPE, "force_path must be 0, 1, 2 or 3");
+    if (value < 0 || value > 4) return fail(W4_E_SHAPE, "force_path must be 0, 1, 2, 3 or 4");
     g_force_path.store(value);
     return ok();
   }
@@ -921,7 +938,7 @@ int w4_schedule_add(int a_dtype, int group_mode, int64_t N, int64_t K, int64_t m
   if (group_mode != 0 && group_mode != 1) return fail(W4_E_SHAPE, "group_mode must be 0 or 1");
   if (N <= 0 || K <= 0 || m_lo < 0 || m_hi < m_lo)
     return fail(W4_E_SHAPE, "need N > 0, K > 0, 0 <= m_lo <= m_hi");
-  if (path < 0 || path > 3) return fail(W4_E_SHAPE, "path must be 0, 1, 2 or 3");
+  if (path < 0 || path > 4) return fail(W4_E_SHAPE, "path must be 0, 1, 2, 3 or 4");
   if (splitk < 0 || splitk > 64) return fail(W4_E_SHAPE, "splitk must be in [0, 64]");
   if (tile_m != 0 && tile_m != 32 && tile_m != 64 && tile_m != 128 && tile_m != 256)
     return fail(W4_E_SHAPE, "tile_m must be 0, 32, 64, 128 or 256");

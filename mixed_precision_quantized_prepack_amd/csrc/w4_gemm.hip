@@ -1250,11 +1250,6 @@ static hipError_t launch_typed(const GemmArgs& args, const GemmPlan& plan, hipSt
                            args, 1);
     }
   };
-  if (plan.bm == 256) {
-    // 256 x 256 tiles: the ping-pong kernel (symmetric int8 per channel)
-    if constexpr (OP == OP_I8 && !GROUPED && !ZP && SG == 1) return launch_pingpong(args, FLIP, plan, stream);
-    return hipErrorInvalidValue;
-  }
   if constexpr (kByte) {
     if (plan.bm == 128 && plan.bn == 256) {
       // the 128 x 256 tile exists for symmetric int8 per channel only
@@ -1281,6 +1276,10 @@ static hipError_t launch_typed(const GemmArgs& args, const GemmPlan& plan, hipSt
 hipError_t launch_gemm(const GemmArgs& args, int op, bool grouped, bool flip, bool zp, const GemmPlan& plan,
                        hipStream_t stream) {
   if (plan.path == PATH_STREAM) return zp ? hipErrorInvalidValue : launch_stream(args, op, grouped, flip, plan, stream);
+  if (plan.path == PATH_PINGPONG) {
+    if (op != OP_I8 || grouped || zp || args.x || args.z) return hipErrorInvalidValue;
+    return launch_pingpong(args, flip, plan, stream);
+  }
   if (zp) {   // asymmetric int8 W4A8 (the API admits no other combination)
     if (op != OP_I8 || !flip) return hipErrorInvalidValue;
     return grouped ? launch_typed<OP_I8, true, true, true>(args, plan, stream)

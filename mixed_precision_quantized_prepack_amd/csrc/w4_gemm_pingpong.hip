@@ -10,11 +10,11 @@
 namespace w4 {
 
 // ===========================================================================
-// One workgroup of eight waves per CU computes a 256 x 256 tile as two
-// groups of four waves, each the tiled kernel's 128 x 256 tile (wave w of a
-// group owns 4 16-column n-blocks across its 128 rows; its own half of a
-// three-stage LDS ring for the activation rows; weights in registers, two
-// steps ahead).  A group alternates two phases per 128-deep K step:
+// One workgroup of eight waves per CU computes a 2 GM x 256 tile (GM = 128
+// or 64 rows) as two groups of four waves, each the tiled kernel's GM x 256
+// tile (wave w of a group owns 4 16-column n-blocks across its GM rows; its
+// own half of a three-stage LDS ring for the activation rows; weights in
+// registers, two steps ahead).  A group alternates two phases per 128-deep K step:
 //   V: wait for the step's loads, expand the weights, issue the loads of the
 //      step two ahead;
 //   M: the step's fragment reads and 64 MFMAs per wave.
@@ -25,16 +25,17 @@ namespace w4 {
 // both expand.)  The two groups share no LDS and no registers; the barriers
 // only pace them.
 // ===========================================================================
-template <bool FLIP, bool SPLIT, bool PARTIALS>
+template <int MT, bool FLIP, bool SPLIT, bool PARTIALS>
 __global__ __launch_bounds__(512, 1) void w4_gemm_pingpong(GemmArgs p, int splitk) {
   constexpr int OP = OP_I8;
   using Acc = typename OpTraits<OP>::Acc;
   constexpr int AV = act_vecs<OP>();
-  constexpr int MT = 8, NT = 4;
+  constexpr int NT = 4;
+  constexpr int GM = 16 * MT;               // rows of one group
   constexpr int ROWB = 128, CPR = 8, RPL = 8;
-  constexpr int HALF = 128 * ROWB;          // one group's rows of a stage
+  constexpr int HALF = GM * ROWB;           // one group's rows of a stage
   constexpr int STAGE = 2 * HALF;
-  constexpr int LPT = 128 / (4 * RPL);       // tile loads per wave per step
+  constexpr int LPT = GM / (4 * RPL);        // tile loads per wave per step
   constexpr int kAfter = LPT + NT;           // loads issued after a step's own
   __shared__ __attribute__((aligned(1024))) uint8_t lds[3 * STAGE];
 
@@ -47,14 +48,14 @@ __global__ __launch_bounds__(512, 1) void w4_gemm_pingpong(GemmArgs p, int split
   const int kq = lane >> 4;
   int bx, by, bz;
   tile_of_block(bx, by, bz);
-  const int64_t m_base = (int64_t)bx * 256 + grp * 128;
+  const int64_t m_base = (int64_t)bx * (2 * GM) + grp * GM;
   const int64_t NB = p.N >> 4;
   const int64_t nb_base = (int64_t)by * 16 + gw * NT;
   const int KB = (int)(p.K >> 7);
   const int kb0 = (int)((int64_t)KB * bz / splitk);
   const int kb1 = (int)((int64_t)KB * (bz + 1) / splitk);
 
-  const int64_t rows_valid = p.M - m_base < 128 ? p.M - m_base : 128;
+  const int64_t rows_valid = p.M - m_base < GM ? p.M - m_base : GM;
   const __amdgpu_buffer_rsrc_t ra =
       make_rsrc(static_cast<const uint8_t*>(p.a) + (rows_valid > 0 ? m_base * p.K : 0), rows_valid * p.K);
   const __amdgpu_buffer_rsrc_t rw =
@@ -206,20 +207,29 @@ __global__ __launch_bounds__(512, 1) void w4_gemm_pingpong(GemmArgs p, int split
   }
 }
 
-hipError_t launch_pingpong(const GemmArgs& args, bool flip, const GemmPlan& plan, hipStream_t stream) {
-  const dim3 grid((unsigned)((args.M + 255) / 256), (unsigned)((args.N + 255) / 256), (unsigned)plan.splitk);
+template <int MT>
+static hipError_t launch_rows(const GemmArgs& args, bool flip, const GemmPlan& plan, hipStream_t stream) {
+  const int64_t BM = 32 * MT;
+  const dim3 grid((unsigned)((args.M + BM - 1) / BM), (unsigned)((args.N + 255) / 256), (unsigned)plan.splitk);
   const bool part = args.mode == MODE_PARTIALS;
   if (plan.splitk > 1) {
-    if (flip) hipLaunchKernelGGL((w4_gemm_pingpong<true, true, false>), grid, dim3(512), 0, stream, args, plan.splitk);
-    else hipLaunchKernelGGL((w4_gemm_pingpong<false, true, false>), grid, dim3(512), 0, stream, args, plan.splitk);
+    if (flip) hipLaunchKernelGGL((w4_gemm_pingpong<MT, true, true, false>), grid, dim3(512), 0, stream, args, plan.splitk);
+    else hipLaunchKernelGGL((w4_gemm_pingpong<MT, false, true, false>), grid, dim3(512), 0, stream, args, plan.splitk);
   } else if (part) {
-    if (flip) hipLaunchKernelGGL((w4_gemm_pingpong<true, false, true>), grid, dim3(512), 0, stream, args, 1);
-    else hipLaunchKernelGGL((w4_gemm_pingpong<false, false, true>), grid, dim3(512), 0, stream, args, 1);
+    if (flip) hipLaunchKernelGGL((w4_gemm_pingpong<MT, true, false, true>), grid, dim3(512), 0, stream, args, 1);
+    else hipLaunchKernelGGL((w4_gemm_pingpong<MT, false, false, true>), grid, dim3(512), 0, stream, args, 1);
   } else {
-    if (flip) hipLaunchKernelGGL((w4_gemm_pingpong<true, false, false>), grid, dim3(512), 0, stream, args, 1);
-    else hipLaunchKernelGGL((w4_gemm_pingpong<false, false, false>), grid, dim3(512), 0, stream, args, 1);
+    if (flip) hipLaunchKernelGGL((w4_gemm_pingpong<MT, true, false, false>), grid, dim3(512), 0, stream, args, 1);
+    else hipLaunchKernelGGL((w4_gemm_pingpong<MT, false, false, false>), grid, dim3(512), 0, stream, args, 1);
   }
-  hipError_t e = hipGetLastError();
+  return hipGetLastError();
+}
+
+hipError_t launch_pingpong(const GemmArgs& args, bool flip, const GemmPlan& plan, hipStream_t stream) {
+  if (plan.bn != 256) return hipErrorInvalidValue;
+  hipError_t e = plan.bm == 256 ? launch_rows<8>(args, flip, plan, stream)
+                 : plan.bm == 128 ? launch_rows<4>(args, flip, plan, stream)
+                                  : hipErrorInvalidValue;
   if (e != hipSuccess || plan.splitk == 1) return e;
   return launch_splitk_reduce(args, OP_I8, false, plan.splitk, stream);
 }

@@ -9,7 +9,7 @@ namespace w4 {
 // Matrix-core operand class of a GEMM (the activation type it multiplies).
 enum Op : int { OP_I8 = 0, OP_FP8 = 1, OP_F16 = 2, OP_BF16 = 3 };
 
-enum Path : int { PATH_AUTO = 0, PATH_SKINNY = 1, PATH_TILED = 2, PATH_STREAM = 3 };
+enum Path : int { PATH_AUTO = 0, PATH_SKINNY = 1, PATH_TILED = 2, PATH_STREAM = 3, PATH_PINGPONG = 4 };
 enum Mode : int { MODE_OUTPUT = 0, MODE_PARTIALS = 1 };
 
 // Everything a GEMM kernel reads, in element units unless noted.
@@ -63,7 +63,7 @@ inline int64_t skinny_table_bytes(int op, bool grouped, int64_t groups, int stri
 constexpr int64_t kSkinnyTableMax = 48 * 1024;
 
 struct GemmPlan {
-  int path;    // PATH_SKINNY, PATH_TILED or PATH_STREAM
+  int path;    // PATH_SKINNY, PATH_TILED, PATH_STREAM or PATH_PINGPONG
   int splitk;  // skinny: waves per workgroup splitting K; tiled: K splits across workgroups
   int bm, bn;  // tiled block tile (rows of A, columns of W)
 };
@@ -92,7 +92,8 @@ hipError_t launch_gemm(const GemmArgs& args, int op, bool grouped, bool flip, bo
 
 // The streaming kernel (8-bit operands, symmetric weights; plan.path ==
 // PATH_STREAM): tiles 32 x 256, 64 x 256 and 128 x 128.
-// Ping-pong kernel (int8 per channel, symmetric weights, 256 x 256 tiles).
+// Ping-pong kernel (int8 per channel, symmetric weights; plan.bm = 256 or 128
+// rows, plan.bn = 256 columns).
 hipError_t launch_pingpong(const GemmArgs& args, bool flip, const GemmPlan& plan, hipStream_t stream);
 hipError_t launch_stream(const GemmArgs& args, int op, bool grouped, bool flip, const GemmPlan& plan,
                          hipStream_t stream);

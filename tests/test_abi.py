@@ -268,25 +268,32 @@ def test_plan_choices(lib, heuristic_only):
     assert plans[1][0] == plans[16][0] == 1                      # small-M kernel
     assert plans[1][3] == 32                                     # two 16-column strips per wave
     assert plans[64] == (3, 4, 64, 128)                         # streaming kernel, 64 tiles x 4 K splits
-    assert [plans[M][1] for M in (128, 256, 512, 1024)] == [4, 4, 2, 1]
-    assert plans[4096][1:] == (1, 256, 256)                      # ping-pong: one 256 x 256 tile per CU
-    assert w4.gemm_plan(2048, 8192, 21760, -1, w4.I8)[1:] == (1, 256, 256)   # 256 tiles
-    assert w4.gemm_plan(2048, 4096, 21760, -1, w4.I8)[1:] == (1, 64, 256)    # 256 tall tiles: 64 rows
-    assert w4.gemm_plan(4096, 8192, 21760, 128, w4.I8)[2:] == (128, 128)     # grouped: tiled
-    assert w4.gemm_plan(4096, 8192, 21760, -1, w4.FP8_E4M3)[2:] == (128, 128)
+    assert [plans[M][1] for M in (128, 256, 512)] == [4, 4, 2]
+    assert plans[1024] == (4, 2, 256, 256)                      # ping-pong: 128 tiles x 2 K splits
+    assert plans[4096] == (4, 1, 256, 256)                      # ping-pong: one 256 x 256 tile per CU
+    assert w4.gemm_plan(2048, 8192, 21760, -1, w4.I8) == (4, 1, 256, 256)    # 256 tiles
+    assert w4.gemm_plan(2048, 4096, 21760, -1, w4.I8) == (4, 2, 256, 256)   # 128 ping-pong tiles x 2 splits
+    assert w4.gemm_plan(1024, 4096, 21760, -1, w4.I8)[:3] == (2, 2, 64)     # 64: tiled
+    assert w4.gemm_plan(4096, 8192, 21760, 128, w4.I8)[:3] == (2, 1, 128)   # grouped: tiled
+    assert w4.gemm_plan(4096, 8192, 21760, -1, w4.FP8_E4M3)[0] == 2
     try:
-        w4.set_option("tiled_bm", 256)
-        assert w4.gemm_plan(300, 8192, 21760, -1, w4.I8) == (2, 4, 256, 256)    # 64 tiles x 4 K splits
+        w4.set_option("tiled_bm", 256)                               # a 256-row tile forces the ping-pong kernel
+        assert w4.gemm_plan(300, 8192, 21760, -1, w4.I8) == (4, 4, 256, 256)    # 64 tiles x 4 K splits
         with pytest.raises(w4.W4Error):
-            w4.gemm_plan(300, 8192, 21760, 128, w4.I8)
-        with pytest.raises(w4.W4Error):
-            w4.gemm_plan(300, 8192, 21760, -1, w4.FP8_E4M3)
+            w4.gemm_plan(300, 8192, 21760, 128, w4.I8)               # grouped: the tiled kernel has no 256 rows
+        w4.set_option("force_path", 4)
+        w4.set_option("tiled_bm", 128)
+        assert w4.gemm_plan(300, 8192, 21760, -1, w4.I8) == (4, 4, 128, 256)    # 96 tiles x 4 K splits
+        for bad in ((300, 8192, 21760, 128, w4.I8), (300, 8192, 21760, -1, w4.FP8_E4M3),
+                    (300, 8192, 4096, -1, w4.BF16)):
+            with pytest.raises(w4.W4Error):
+                w4.gemm_plan(*bad)
         w4.set_option("skinny_strips", 2)
         with pytest.raises(w4.W4Error):
             w4.gemm_plan(300, 8192, 21760, -1, w4.I8)
     finally:
-        w4.set_option("tiled_bm", 0)
-        w4.set_option("skinny_strips", 0)
+        for k in ("tiled_bm", "skinny_strips", "force_path"):
+            w4.set_option(k, 0)
     # grouped small M: two strips from M = 8 when N >= 8192, at any M when
     # N >= 16384 or (N >= 8192 and K >= 8192), else one
     assert w4.gemm_plan(1, 12288, 4096, 128, w4.I8)[3] == 16
@@ -355,8 +362,11 @@ def test_options_and_plans(lib, heuristic_only):
     try:
         assert lib.w4_set_option(b"nonsense", 1) == E_UNSUP
         assert lib.w4_set_option(b"force_path", 5) == E_SHAPE
+        assert lib.w4_set_option(b"force_path", 4) == W4_OK
+        w4.set_option("force_path", 0)
         assert w4.gemm_plan(1, 8192, 21760, -1, w4.I8)[0] == 1     # small M -> skinny
-        assert w4.gemm_plan(4096, 8192, 21760, -1, w4.I8)[0] == 2  # large M -> tiled
+        assert w4.gemm_plan(512, 8192, 21760, -1, w4.I8)[0] == 2   # large M -> tiled
+        assert w4.gemm_plan(4096, 8192, 21760, -1, w4.I8)[0] == 4  # ... ping-pong from a 256-row tile per 2 CUs
         assert lib.w4_set_option(b"norm_exact_sum", 2) == E_SHAPE
         w4.set_option("norm_exact_sum", 1)
         assert w4.get_option("norm_exact_sum") == 1
@@ -405,7 +415,7 @@ def test_schedule_add_validation(lib):
     assert f(3, 2, 8192, 21760, 1, 16, 1, 2, 0, 0) == E_SHAPE         # group mode
     assert f(3, 0, 8192, 21760, 17, 16, 2, 2, 0, 0) == E_SHAPE        # m_hi < m_lo
     assert f(3, 0, 8192, 21760, 1, 64, 1, 2, 0, 0) == E_SHAPE         # small-M kernel above M = 16
-    assert f(3, 0, 8192, 21760, 1, 16, 4, 2, 0, 0) == E_SHAPE         # paths 0..3
+    assert f(3, 0, 8192, 21760, 1, 16, 5, 2, 0, 0) == E_SHAPE         # paths 0..4
     assert f(3, 0, 8192, 21760, 1, 16, 2, 65, 0, 0) == E_SHAPE
     assert f(3, 0, 8192, 21760, 1, 16, 2, 2, 96, 0) == E_SHAPE
     assert f(3, 0, 8192, 21760, 1, 16, 1, 2, 0, 3) == E_SHAPE

@@ -107,26 +107,28 @@ def test_w4a8_narrow_tiles_outputs(wl, M, split):
     assert_w4a8(out, ref, dc.wl.out_dtype, dc.wl.q_dtype, dc.G, strict=True, label=f"{wl} 64x128 strict M={M}")
 
 
-@pytest.mark.parametrize("M,split", [(130, 1), (300, 3), (520, 2), (256, 1)])
+@pytest.mark.parametrize("M,split,bm", [(130, 1, 256), (300, 3, 256), (520, 2, 256), (256, 1, 256),
+                                        (70, 1, 128), (130, 2, 128), (200, 3, 128)])
 @pytest.mark.parametrize("wtype", ["int4", "uint4b8"])
-def test_int8_partials_bit_exact_pingpong(M, split, wtype):
-    """The ping-pong kernel's 256 x 256 tiles (two 128-row halves), ragged M
-    (a half with no rows, a partial half) and N = 272 (a second column tile
-    with one n-block), with and without K splits."""
+def test_int8_partials_bit_exact_pingpong(M, split, bm, wtype):
+    """The ping-pong kernel's 256 x 256 and 128 x 256 tiles (two halves),
+    ragged M (a half with no rows, a partial half) and N = 272 (a second
+    column tile with one n-block), with and without K splits."""
     dc = DeviceCase("w4a8_i8_pc_256x512", M, N=272, K=1280, seed_base=M * 17 + split, wtype=wtype)
     packed = w4.prepack_B(dc.w_logical, "i8")
     aq, _ = w4.quant_act_per_token(dc.a, "i8")
-    with options(2, split, 256):
-        assert w4.gemm_plan(M, dc.N, dc.K, -1, w4.I8) == (2, split, 256, 256)
+    with options(4, split, bm):
+        assert w4.gemm_plan(M, dc.N, dc.K, -1, w4.I8) == (4, split, bm, 256)
         part = w4.w4a8_gemm_partials(aq, packed, dc.N, -1, wtype=dc.wtype)
     want = O.w4a8_group_partials(aq.cpu().numpy(), "i8", dc.case.w_logical.numpy(), dc.K, dc.wtype, dc.K)
     assert np.array_equal(part.cpu().numpy().astype(np.int64), want)
 
 
-@pytest.mark.parametrize("M,split,wtype", [(200, 1, "int4"), (400, 2, "uint4b8"), (513, 1, "int4")])
-def test_w4a8_pingpong_outputs(M, split, wtype):
+@pytest.mark.parametrize("M,split,bm,wtype", [(200, 1, 256, "int4"), (400, 2, 256, "uint4b8"), (513, 1, 256, "int4"),
+                                               (100, 2, 128, "int4"), (333, 1, 128, "uint4b8")])
+def test_w4a8_pingpong_outputs(M, split, bm, wtype):
     dc = DeviceCase("w4a8_i8_pc_256x512", M, N=528, K=1536, with_bias=True, seed_base=M + 7, wtype=wtype)
-    with options(2, split, 256):
+    with options(4, split, bm):
         out_t, *_ = run_w4a8(dc)
     codes, sa = dc.oracle_quant()
     ref = dc.oracle_w4a8(codes, sa)

@@ -4,7 +4,7 @@ Outputs, split-K workspaces and partials buffers are placed between two
 4 KiB bands of canary bytes; after each call the bands must be intact and the
 result must pass the oracle.  Cases cover ragged M and N on every kernel and
 tile shape (small-M with one and two strips; tiled 64 x 256, 128 x 256,
-128 x 128 and 64 x 128 (8- and 16-bit), the ping-pong kernel's 256 x 256; streaming 32 x 256, 64 x 128 and 128 x 128), with
+128 x 128 and 64 x 128 (8- and 16-bit); ping-pong 256 x 256 and 128 x 256; streaming 32 x 256, 64 x 128 and 128 x 128), with
 and without K splits.  The W4A16
 zero-points of the per-channel fp16 case are followed by NaN bytes: columns
 past N must not read them into any stored output.
@@ -78,15 +78,15 @@ SHAPES = [
     (1, 1, 272, 0, 0, 1), (1, 13, 288, 0, 0, 2), (1, 16, 272, 3, 0, 1),
     (2, 17, 272, 1, 64, 0), (2, 70, 272, 3, 64, 0), (2, 130, 272, 1, 128, 0), (2, 200, 272, 2, 128, 0),
     (3, 20, 272, 2, 32, 4), (3, 50, 272, 1, 64, 2), (3, 100, 272, 3, 128, 0), (2, 70, 272, 2, 64, 2),
-    (2, 300, 272, 2, 256, 0), (2, 130, 272, 1, 256, 0),
+    (4, 300, 272, 2, 256, 0), (4, 130, 272, 1, 128, 0),
 ]
 
 W4A8 = ["w4a8_i8_pc_256x512", "w4a8_i8_g128_o", "w4a8_fp8_g128_28672x8192"]
 
 
-# the ping-pong kernel's 256-row tiles exist for int8 per channel only
+# the ping-pong kernel (path 4) is for int8 per channel only
 W4A8_CASES = [(wl,) + shape for wl in W4A8 for shape in SHAPES
-              if shape[4] != 256 or wl == "w4a8_i8_pc_256x512"]
+              if shape[0] != 4 or wl == "w4a8_i8_pc_256x512"]
 
 
 @pytest.mark.parametrize("wl,path,M,N,split,bm,strips", W4A8_CASES)
