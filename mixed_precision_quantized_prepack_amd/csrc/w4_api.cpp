@@ -158,16 +158,18 @@ int plan_with(int64_t M, int64_t N, int64_t K, bool grouped, int op, const Sched
   // shape at M = 32 and per channel at M = 64; fp8, whose lookup expansion
   // keeps one wave per SIMD busy, is faster tiled); larger M: the tiled kernel
   const bool stream_ok = op == OP_I8 && !zp && sg == 1 && M > 16 && M <= 64 && stream_tile_m(M, N, grouped, cu);
-  // symmetric int8 per channel with a 256 x 256 tile per two CUs or more:
+  // symmetric int8 per channel with a 128 x 256 tile per two CUs or more:
   // the ping-pong kernel (one eight-wave workgroup per CU whose two halves
-  // take turns on the MFMAs, K split to fill the CUs; on 8192 x 21760
-  // measured 4-5% faster than two tiled workgroups per CU at M = 2048-8192
-  // and 3.7% at M = 1024 with two K splits; at M = 512 within 2%, at
-  // M = 256 slower); a forced 256-row tile selects it too
+  // take turns on the MFMAs), K split until the tiles fill the CUs.  256 x 256
+  // tiles from one per two CUs (on 8192 x 21760 4-5% faster than two tiled
+  // workgroups per CU at M = 2048-8192, 3% at M = 1024 with two K splits),
+  // else 128 x 256 tiles whose halves split K between them (M = 512 with two
+  // K splits: 79 against 85 us); a forced 256-row tile selects it too
   const bool pc8 = op == OP_I8 && !grouped && !zp && sg == 1;
   const int64_t pp_tiles = ((M + 255) / 256) * ((N + 255) / 256);
+  const int64_t pp_ks_tiles = ((M + 127) / 128) * ((N + 255) / 256);
   const bool pp_ok =
-      pc8 && M > 64 && (forced.tile_m == 256 || (!forced.tile_m && !forced.strips && 2 * pp_tiles >= cu));
+      pc8 && M > 64 && (forced.tile_m == 256 || (!forced.tile_m && !forced.strips && 2 * pp_ks_tiles >= cu));
   plan->path = fp ? (int)fp
                   : (M <= 16 ? PATH_SKINNY : stream_ok ? PATH_STREAM : pp_ok ? PATH_PINGPONG : PATH_TILED);
   tiled_tile(op, grouped, 0, &plan->bm, &plan->bn, zp);
@@ -196,15 +198,16 @@ int plan_with(int64_t M, int64_t N, int64_t K, bool grouped, int op, const Sched
     }
   }
   if (plan->path == PATH_PINGPONG) {
-    // ping-pong kernel: symmetric int8 per channel, 256 or 128 rows x 256
-    // columns, one workgroup per CU
+    // ping-pong kernel: symmetric int8 per channel, 256 rows (two 128-row
+    // halves) or 128 rows (two halves splitting K) x 256 columns, one
+    // workgroup per CU
     if (!pc8) return fail(W4_E_UNSUPPORTED, "the ping-pong kernel takes symmetric int8 per channel");
     const int64_t fbm = forced.tile_m;
     if (fbm && fbm != 128 && fbm != 256)
       return fail(W4_E_SHAPE, "ping-pong kernel: tile rows 128 or 256 (got %lld)", (long long)fbm);
     if (forced.strips && forced.strips != 4)
       return fail(W4_E_SHAPE, "ping-pong kernel: tiles are 256 columns wide (4 column blocks per wave)");
-    plan->bm = (int)(fbm ? fbm : 256);   // 128-row tiles (forced) measured slower at every M
+    plan->bm = (int)(fbm ? fbm : (2 * pp_tiles >= cu ? 256 : 128));
     plan->bn = 256;
     const int64_t tiles = ((M + plan->bm - 1) / plan->bm) * ((N + 255) / 256);
     int64_t s = fs;

@@ -25,8 +25,9 @@ namespace w4 {
 // both expand.)  The two groups share no LDS and no registers; the barriers
 // only pace them.
 // ===========================================================================
-template <int MT, bool FLIP, bool SPLIT, bool PARTIALS>
+template <bool KS, bool FLIP, bool SPLIT, bool PARTIALS>
 __global__ __launch_bounds__(512, 1) void w4_gemm_pingpong(GemmArgs p, int splitk) {
+  constexpr int MT = 8;
   constexpr int OP = OP_I8;
   using Acc = typename OpTraits<OP>::Acc;
   constexpr int AV = act_vecs<OP>();
@@ -37,7 +38,10 @@ __global__ __launch_bounds__(512, 1) void w4_gemm_pingpong(GemmArgs p, int split
   constexpr int STAGE = 2 * HALF;
   constexpr int LPT = GM / (4 * RPL);        // tile loads per wave per step
   constexpr int kAfter = LPT + NT;           // loads issued after a step's own
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[3 * STAGE];
+  constexpr int STRIDE = KS ? 2 : 1;         // K steps between a group's steps
+  constexpr int RED = 4 * NT * MT * 64 * 16; // the K-split halves' sum: group 1's accumulators
+  constexpr int LDS = (KS && RED > 3 * STAGE) ? RED : 3 * STAGE;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[LDS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -48,12 +52,14 @@ __global__ __launch_bounds__(512, 1) void w4_gemm_pingpong(GemmArgs p, int split
   const int kq = lane >> 4;
   int bx, by, bz;
   tile_of_block(bx, by, bz);
-  const int64_t m_base = (int64_t)bx * (2 * GM) + grp * GM;
+  // K split (KS): both groups take the same rows and alternate K steps
+  const int64_t m_base = KS ? (int64_t)bx * GM : (int64_t)bx * (2 * GM) + grp * GM;
   const int64_t NB = p.N >> 4;
   const int64_t nb_base = (int64_t)by * 16 + gw * NT;
   const int KB = (int)(p.K >> 7);
   const int kb0 = (int)((int64_t)KB * bz / splitk);
   const int kb1 = (int)((int64_t)KB * (bz + 1) / splitk);
+  const int kb_first = KS ? kb0 + grp : kb0;   // this group's first K step
 
   const int64_t rows_valid = p.M - m_base < GM ? p.M - m_base : GM;
   const __amdgpu_buffer_rsrc_t ra =
@@ -105,16 +111,15 @@ __global__ __launch_bounds__(512, 1) void w4_gemm_pingpong(GemmArgs p, int split
     for (int nt = 0; nt < NT; ++nt) expand_weights<OP, FLIP>(w[nt], f16x2{}, e[nt]);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) pin_words<kExpandedWords<OP>>(e[nt]);
-    load_w(kb + 2, w);
-    const int st2 = (kb + 2 - kb0) % 3;
-    load_a(kb + 2, st2);
+    load_w(kb + 2 * STRIDE, w);
+    load_a(kb + 2 * STRIDE, ((kb - kb_first) / STRIDE + 2) % 3);
     asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
   };
   // M: the step's MFMAs on its stage.
   auto phase_m = [&](int kb) {
     __builtin_amdgcn_sched_barrier(0);
-    const uint8_t* src = my_lds + ((kb - kb0) % 3) * STAGE;
+    const uint8_t* src = my_lds + (((kb - kb_first) / STRIDE) % 3) * STAGE;
     u32x4 af[MT][AV];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
@@ -139,11 +144,11 @@ __global__ __launch_bounds__(512, 1) void w4_gemm_pingpong(GemmArgs p, int split
   };
 
   u32x4 w0[NT], w1[NT];
-  load_a(kb0, 0);
-  load_w(kb0, w0);
+  load_a(kb_first, 0);
+  load_w(kb_first, w0);
   asm volatile("" ::: "memory");
-  load_a(kb0 + 1, 1);
-  load_w(kb0 + 1, w1);
+  load_a(kb_first + STRIDE, 1);
+  load_w(kb_first + STRIDE, w1);
   asm volatile("" ::: "memory");
 
   // Slots separated by workgroup barriers.  Every wave runs V(kb) M(kb)
@@ -151,18 +156,20 @@ __global__ __launch_bounds__(512, 1) void w4_gemm_pingpong(GemmArgs p, int split
   // later (and group 0 ends with one more), so in every slot one group issues
   // its MFMAs while the other expands and loads.  Both groups pass the same
   // number of barriers.
-  const int n = kb1 - kb0;
+  // steps per group: with the K split both groups take the same count (group
+  // 1's last step may lie past the range: its loads read zeros)
+  const int n = KS ? (kb1 - kb0 + 1) / 2 : kb1 - kb0;
   if (grp == 1) bar();
-  int kb = kb0;
-  for (int pairs = n >> 1; pairs > 0; --pairs, kb += 2) {
+  int kb = kb_first;
+  for (int pairs = n >> 1; pairs > 0; --pairs, kb += 2 * STRIDE) {
     bar();
     phase_v(kb, w0);
     bar();
     phase_m(kb);
     bar();
-    phase_v(kb + 1, w1);
+    phase_v(kb + STRIDE, w1);
     bar();
-    phase_m(kb + 1);
+    phase_m(kb + STRIDE);
   }
   if (n & 1) {
     bar();
@@ -172,6 +179,27 @@ __global__ __launch_bounds__(512, 1) void w4_gemm_pingpong(GemmArgs p, int split
   }
   if (grp == 0) bar();
   __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+
+  if constexpr (KS) {
+    // the halves' sum (exact int32) through LDS: group 1 stores its
+    // accumulators, group 0 adds them and runs the epilogue.  Wave gw of
+    // either group owns the same columns; quad q of lane l is at
+    // ((gw * 32 + q) * 64 + l) * 16 (each store fills 1 KiB, conflict-free).
+    __syncthreads();   // every wave is done with the ring
+    i32x4* red = reinterpret_cast<i32x4*>(lds);
+    if (grp == 1) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) red[(gw * NT * MT + nt * MT + mt) * 64 + lane] = acc[nt][mt];
+    }
+    __syncthreads();
+    if (grp == 1) return;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) acc[nt][mt] += red[(gw * NT * MT + nt * MT + mt) * 64 + lane];
+  }
 
   // Epilogue (as the tiled kernel's, per channel).
 #pragma unroll
@@ -207,28 +235,28 @@ __global__ __launch_bounds__(512, 1) void w4_gemm_pingpong(GemmArgs p, int split
   }
 }
 
-template <int MT>
+template <bool KS>
 static hipError_t launch_rows(const GemmArgs& args, bool flip, const GemmPlan& plan, hipStream_t stream) {
-  const int64_t BM = 32 * MT;
+  const int64_t BM = KS ? 128 : 256;
   const dim3 grid((unsigned)((args.M + BM - 1) / BM), (unsigned)((args.N + 255) / 256), (unsigned)plan.splitk);
   const bool part = args.mode == MODE_PARTIALS;
   if (plan.splitk > 1) {
-    if (flip) hipLaunchKernelGGL((w4_gemm_pingpong<MT, true, true, false>), grid, dim3(512), 0, stream, args, plan.splitk);
-    else hipLaunchKernelGGL((w4_gemm_pingpong<MT, false, true, false>), grid, dim3(512), 0, stream, args, plan.splitk);
+    if (flip) hipLaunchKernelGGL((w4_gemm_pingpong<KS, true, true, false>), grid, dim3(512), 0, stream, args, plan.splitk);
+    else hipLaunchKernelGGL((w4_gemm_pingpong<KS, false, true, false>), grid, dim3(512), 0, stream, args, plan.splitk);
   } else if (part) {
-    if (flip) hipLaunchKernelGGL((w4_gemm_pingpong<MT, true, false, true>), grid, dim3(512), 0, stream, args, 1);
-    else hipLaunchKernelGGL((w4_gemm_pingpong<MT, false, false, true>), grid, dim3(512), 0, stream, args, 1);
+    if (flip) hipLaunchKernelGGL((w4_gemm_pingpong<KS, true, false, true>), grid, dim3(512), 0, stream, args, 1);
+    else hipLaunchKernelGGL((w4_gemm_pingpong<KS, false, false, true>), grid, dim3(512), 0, stream, args, 1);
   } else {
-    if (flip) hipLaunchKernelGGL((w4_gemm_pingpong<MT, true, false, false>), grid, dim3(512), 0, stream, args, 1);
-    else hipLaunchKernelGGL((w4_gemm_pingpong<MT, false, false, false>), grid, dim3(512), 0, stream, args, 1);
+    if (flip) hipLaunchKernelGGL((w4_gemm_pingpong<KS, true, false, false>), grid, dim3(512), 0, stream, args, 1);
+    else hipLaunchKernelGGL((w4_gemm_pingpong<KS, false, false, false>), grid, dim3(512), 0, stream, args, 1);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_pingpong(const GemmArgs& args, bool flip, const GemmPlan& plan, hipStream_t stream) {
   if (plan.bn != 256) return hipErrorInvalidValue;
-  hipError_t e = plan.bm == 256 ? launch_rows<8>(args, flip, plan, stream)
-                 : plan.bm == 128 ? launch_rows<4>(args, flip, plan, stream)
+  hipError_t e = plan.bm == 256 ? launch_rows<false>(args, flip, plan, stream)
+                 : plan.bm == 128 ? launch_rows<true>(args, flip, plan, stream)
                                   : hipErrorInvalidValue;
   if (e != hipSuccess || plan.splitk == 1) return e;
   return launch_splitk_reduce(args, OP_I8, false, plan.splitk, stream);

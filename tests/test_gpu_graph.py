@@ -61,6 +61,7 @@ def _capture(step):
     ("w4a8_i8_g128_o", 130, 2048, 4096, 2, 4),            # grouped int8, tiled 64 x 128 + reduce
     ("w4a8_fp8_g128_28672x8192", 40, 1024, 2048, 2, 4),   # fp8 e4m3 codes, tiled + reduce
     ("w4a8_i8_pc_8192x21760", 1024, 8192, 1024, 4, 2),    # ping-pong kernel + reduce
+    ("w4a8_i8_pc_8192x21760", 500, 8192, 1024, 4, 2),     # ping-pong, halves splitting K, + reduce
 ])
 def test_w4a8_path_in_a_graph(wl, M, N, K, want_path, want_split):
     dc = DeviceCase(wl, M, N=N, K=K, with_bias=True, seed_base=71)
