@@ -408,7 +408,9 @@ def kernel_key_of(wl, plan) -> str:
         return f"w4::w4_gemm_skinny<{op}, {grouped}, false, {tn // 16}, false, false, 1, false, false>"
     nt, mt = tn // 64, tm // 16
     if path == 4:
-        return f"w4::w4_gemm_pingpong<{tm // 32}, false, {'true' if split > 1 else 'false'}, false>"
+        # 128-row tiles are the form whose two halves split K
+        return (f"w4::w4_gemm_pingpong<{'true' if tm == 128 else 'false'}, false, "
+                f"{'true' if split > 1 else 'false'}, false>")
     if path == 3:
         stages = min(8, (120 * 1024) // (mt * 16 * 128 + 4 * nt * 1024))
         return (f"w4::w4_gemm_stream<{op}, {grouped}, false, {nt}, {mt}, {stages}, "

@@ -158,18 +158,25 @@ int plan_with(int64_t M, int64_t N, int64_t K, bool grouped, int op, const Sched
   // shape at M = 32 and per channel at M = 64; fp8, whose lookup expansion
   // keeps one wave per SIMD busy, is faster tiled); larger M: the tiled kernel
   const bool stream_ok = op == OP_I8 && !zp && sg == 1 && M > 16 && M <= 64 && stream_tile_m(M, N, grouped, cu);
-  // symmetric int8 per channel with a 128 x 256 tile per two CUs or more:
-  // the ping-pong kernel (one eight-wave workgroup per CU whose two halves
-  // take turns on the MFMAs), K split until the tiles fill the CUs.  256 x 256
-  // tiles from one per two CUs (on 8192 x 21760 4-5% faster than two tiled
-  // workgroups per CU at M = 2048-8192, 3% at M = 1024 with two K splits),
-  // else 128 x 256 tiles whose halves split K between them (M = 512 with two
-  // K splits: 79 against 85 us); a forced 256-row tile selects it too
+  // symmetric int8 per channel: the ping-pong kernel (one eight-wave
+  // workgroup per CU whose two halves take turns on the MFMAs), K split by
+  // the largest power of two that keeps the workgroups within one per CU.
+  // 256 x 256 tiles from one per two CUs (on 8192 x 21760 4-5% faster than
+  // two tiled workgroups per CU at M = 2048-8192, 3% at M = 1024 with two K
+  // splits); below that, 128 x 256 tiles whose halves split K between them,
+  // when with at most 4 K splits they occupy 3/4 of the CUs or more (M = 384
+  // and 512 with two K splits: 70 and 79 against 80 and 85 us tiled); a
+  // forced 256-row tile selects it too
   const bool pc8 = op == OP_I8 && !grouped && !zp && sg == 1;
+  auto pp_split = [&](int64_t tiles, int64_t smax) {
+    int64_t s = 1;
+    while (s * 2 <= smax && tiles * s * 2 <= cu) s *= 2;
+    return s;
+  };
   const int64_t pp_tiles = ((M + 255) / 256) * ((N + 255) / 256);
   const int64_t pp_ks_tiles = ((M + 127) / 128) * ((N + 255) / 256);
-  const bool pp_ok =
-      pc8 && M > 64 && (forced.tile_m == 256 || (!forced.tile_m && !forced.strips && 2 * pp_ks_tiles >= cu));
+  const bool pp_auto = 2 * pp_tiles >= cu || 4 * pp_ks_tiles * pp_split(pp_ks_tiles, 4) >= 3LL * cu;
+  const bool pp_ok = pc8 && M > 64 && (forced.tile_m == 256 || (!forced.tile_m && !forced.strips && pp_auto));
   plan->path = fp ? (int)fp
                   : (M <= 16 ? PATH_SKINNY : stream_ok ? PATH_STREAM : pp_ok ? PATH_PINGPONG : PATH_TILED);
   tiled_tile(op, grouped, 0, &plan->bm, &plan->bn, zp);
@@ -212,8 +219,7 @@ int plan_with(int64_t M, int64_t N, int64_t K, bool grouped, int op, const Sched
     const int64_t tiles = ((M + plan->bm - 1) / plan->bm) * ((N + 255) / 256);
     int64_t s = fs;
     if (!s) {
-      s = 1;
-      while (tiles * s < cu && s * 2 <= 8) s *= 2;
+      s = pp_split(tiles, plan->bm == 128 ? 4 : 8);
       while (s > 1 && KB / s < 4) s /= 2;
     }
     if (s < 1 || s > 64 || s > KB)

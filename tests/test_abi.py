@@ -268,14 +268,17 @@ def test_plan_choices(lib, heuristic_only):
     assert plans[1][0] == plans[16][0] == 1                      # small-M kernel
     assert plans[1][3] == 32                                     # two 16-column strips per wave
     assert plans[64] == (3, 4, 64, 128)                         # streaming kernel, 64 tiles x 4 K splits
-    assert [plans[M][1] for M in (128, 256)] == [4, 4]
-    assert plans[512] == (4, 2, 128, 256)                       # ping-pong, halves splitting K: 128 tiles x 2
+    assert plans[128][:2] == (2, 4)                              # tiled: 32 K-split ping-pong tiles are too few
+    assert plans[256] == (4, 4, 128, 256)                       # ping-pong, halves splitting K: 64 tiles x 4
+    assert plans[512] == (4, 2, 128, 256)                       # ... 128 tiles x 2
+    assert w4.gemm_plan(384, 8192, 21760, -1, w4.I8) == (4, 2, 128, 256)     # 96 tiles x 2 (3/4 of the CUs)
+    assert w4.gemm_plan(640, 8192, 21760, -1, w4.I8)[0] == 2                 # 160 tiles x 1: tiled
     assert plans[1024] == (4, 2, 256, 256)                      # ping-pong: 128 tiles x 2 K splits
     assert plans[4096] == (4, 1, 256, 256)                      # ping-pong: one 256 x 256 tile per CU
     assert w4.gemm_plan(2048, 8192, 21760, -1, w4.I8) == (4, 1, 256, 256)    # 256 tiles
     assert w4.gemm_plan(2048, 4096, 21760, -1, w4.I8) == (4, 2, 256, 256)   # 128 ping-pong tiles x 2 splits
     assert w4.gemm_plan(1024, 4096, 21760, -1, w4.I8) == (4, 2, 128, 256)   # 64 x 2 < 256: halves split K
-    assert w4.gemm_plan(512, 4096, 21760, -1, w4.I8)[:3] == (2, 4, 64)      # 64 K-split tiles: tiled
+    assert w4.gemm_plan(512, 4096, 21760, -1, w4.I8) == (4, 4, 128, 256)    # 64 K-split tiles x 4
     assert w4.gemm_plan(4096, 8192, 21760, 128, w4.I8)[:3] == (2, 1, 128)   # grouped: tiled
     assert w4.gemm_plan(4096, 8192, 21760, -1, w4.FP8_E4M3)[0] == 2
     try:
@@ -285,7 +288,7 @@ def test_plan_choices(lib, heuristic_only):
             w4.gemm_plan(300, 8192, 21760, 128, w4.I8)               # grouped: the tiled kernel has no 256 rows
         w4.set_option("force_path", 4)
         w4.set_option("tiled_bm", 128)
-        assert w4.gemm_plan(300, 8192, 21760, -1, w4.I8) == (4, 4, 128, 256)    # 96 tiles x 4 K splits
+        assert w4.gemm_plan(300, 8192, 21760, -1, w4.I8) == (4, 2, 128, 256)    # 96 tiles x 2 K splits
         for bad in ((300, 8192, 21760, 128, w4.I8), (300, 8192, 21760, -1, w4.FP8_E4M3),
                     (300, 8192, 4096, -1, w4.BF16)):
             with pytest.raises(w4.W4Error):
@@ -367,7 +370,7 @@ def test_options_and_plans(lib, heuristic_only):
         assert lib.w4_set_option(b"force_path", 4) == W4_OK
         w4.set_option("force_path", 0)
         assert w4.gemm_plan(1, 8192, 21760, -1, w4.I8)[0] == 1     # small M -> skinny
-        assert w4.gemm_plan(384, 8192, 21760, -1, w4.I8)[0] == 2   # large M -> tiled
+        assert w4.gemm_plan(640, 8192, 21760, -1, w4.I8)[0] == 2   # large M -> tiled
         assert w4.gemm_plan(4096, 8192, 21760, -1, w4.I8)[0] == 4  # ... ping-pong from a 256-row tile per 2 CUs
         assert lib.w4_set_option(b"norm_exact_sum", 2) == E_SHAPE
         w4.set_option("norm_exact_sum", 1)
