@@ -35,7 +35,7 @@ class Guarded:
         self.nbytes = nbytes
         body = (nbytes + 15) // 16 * 16
         self.buf = torch.full((GUARD + body + GUARD,), CANARY, dtype=torch.uint8, device=DEV)
-        self.buf[GUARD:GUARD + body] = fill
+        self.buf[GUARD:GUARD + nbytes] = fill   # the pad to 16 bytes keeps the canary
         self.body = self.buf[GUARD:GUARD + nbytes]
 
     def tensor(self, dtype, shape):
