@@ -10,11 +10,15 @@
 namespace w4 {
 
 // ===========================================================================
-// One workgroup of eight waves per CU computes a 2 GM x 256 tile (GM = 128
-// or 64 rows) as two groups of four waves, each the tiled kernel's GM x 256
-// tile (wave w of a group owns 4 16-column n-blocks across its GM rows; its
-// own half of a three-stage LDS ring for the activation rows; weights in
-// registers, two steps ahead).  A group alternates two phases per 128-deep K step:
+// One workgroup of eight waves per CU computes a 256 x 256 tile (KS false) or
+// a 128 x 256 tile (KS true) as two groups of four waves, each the tiled
+// kernel's 128 x 256 tile (wave w of a group owns 4 16-column n-blocks across
+// its 128 rows; its own half of a three-stage LDS ring for the activation
+// rows; weights in registers, two steps ahead).  Without KS the groups take
+// rows 0-127 and 128-255; with KS both take the same rows and alternate K
+// steps (group 0 the even steps of the range, group 1 the odd ones), and
+// their exact int32 sums are added through LDS at the end.  A group
+// alternates two phases per 128-deep K step:
 //   V: wait for the step's loads, expand the weights, issue the loads of the
 //      step two ahead;
 //   M: the step's fragment reads and 64 MFMAs per wave.
