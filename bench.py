@@ -281,10 +281,26 @@ def summarize(set_name: str, trace_dir: str, fetch_dir: str, write_dir: str) -> 
     return 0
 
 
-def write_kernel_stats(set_name: str, trace_dir: str, cmd: str) -> None:
+STEP_PROFILE_ARGS = "--no-configs --no-cpu-baseline"
+
+
+def summarize_step(trace_dir: str) -> int:
+    """Kernel-time summary of a trace of the headline step itself (the timed
+    steps and the per-launch event pass of the default run, without the
+    workload sweep): the figures the bench line's roofline is taken from."""
+    cmd = (f"rocprofv3 --kernel-trace --stats --output-format csv -d {trace_dir} -o trace -- "
+           f"python -u bench.py {STEP_PROFILE_ARGS}")
+    write_kernel_stats("w4a8_i8_pc_8192x21760", trace_dir, cmd, kind="step_kernel_stats",
+                       what="the headline step (per-token quantisation and GEMM at M = 1 ... 4096, "
+                            "settle, warm-up, timed steps and the per-launch event pass)")
+    return 0
+
+
+def write_kernel_stats(set_name: str, trace_dir: str, cmd: str, kind: str = "kernel_stats",
+                       what: str = "") -> None:
     """Kernel-time summary of the trace run (rocprofv3 --kernel-trace --stats)."""
     rows = sorted(_read_csv(trace_dir, "kernel_stats.csv"), key=lambda r: -float(r["TotalDurationNs"]))
-    lines = [f"# Kernel statistics: {set_name} ({', '.join(PROFILE_SETS[set_name])})", "",
+    lines = [f"# Kernel statistics: {set_name} ({what or ', '.join(PROFILE_SETS[set_name])})", "",
              "Command (repository root, one MI355X):", "", "```", cmd, "```", "",
              "Durations are per dispatch, from the kernel trace.", "",
              "| kernel | calls | avg us | min us | max us | % time |", "|---|---|---|---|---|---|"]
@@ -306,7 +322,7 @@ def write_kernel_stats(set_name: str, trace_dir: str, cmd: str) -> None:
         med = sorted(d)[len(d) // 2]
         shown = ("..., " if len(d) > 8 else "") + ", ".join(f"{x:.1f}" for x in d[-8:])
         lines.append(f"| `{k[:110]}` | {g} | {len(d)} | {sum(d) / len(d):.1f} | {med:.1f} | {shown} |")
-    path = profile_md(set_name, "kernel_stats")
+    path = profile_md(set_name, kind)
     with open(path, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print(path)
@@ -590,11 +606,15 @@ def main(argv=None) -> int:
     ap.add_argument("--only", choices=sorted(PROFILE_SETS), help="only this set's GEMMs (for rocprofv3)")
     ap.add_argument("--summarize", nargs=4, metavar=("SET", "TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
                     help="write the kernel-time and HBM-traffic summaries from rocprofv3 outputs and exit")
+    ap.add_argument("--summarize-step", metavar="TRACE_DIR",
+                    help=f"write the kernel summary of a trace of 'bench.py {STEP_PROFILE_ARGS}' and exit")
     ap.add_argument("--summarize-counters", nargs="+", metavar="SET_AND_DIRS",
                     help="SET DIR [DIR ...]: write the MFMA/VALU counter summary and exit")
     args = ap.parse_args(argv)
     if args.summarize:
         return summarize(*args.summarize)
+    if args.summarize_step:
+        return summarize_step(args.summarize_step)
     if args.summarize_counters:
         return summarize_counters(args.summarize_counters[0], args.summarize_counters[1:])
     if args.gpus != 1:
@@ -815,7 +835,8 @@ def main(argv=None) -> int:
                 "kernel": dom_name, "launches": [pm["M"] for pm in dom], "avg_launch_us": round(dur, 2),
                 "alg_ops_per_launch": flops,
                 "note": "int8 operations (2 per multiply-add) per second; avg_launch_us from a second pass of "
-                        "the timed steps with events around each launch on the launch stream"}
+                        "the timed steps with events around each launch on the launch stream; kernel trace of "
+                        "the same step: profiles/w4a8_i8_pc_8192x21760_step_kernel_stats.md"}
     small = [pm for pm in per_m if pm["kernel"].startswith("w4_gemm_skinny")]
     roofline_small = None
     if small:
