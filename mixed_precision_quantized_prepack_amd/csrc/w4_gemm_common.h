@@ -229,14 +229,16 @@ constexpr int waitcnt_vm_lgkm0(int vm) { return (vm & 15) | ((vm >> 4) << 14) | 
 // Tile order.  Workgroups are dealt round-robin to the 8 XCDs (each with its
 // own L2) in launch order.  They are renumbered so that each XCD receives a
 // contiguous range of tile numbers t, and t runs through the (m, n) tiles in
-// groups of kGroupM m-tiles: the workgroups one XCD runs together cover a
-// near-square patch of kGroupM m-tiles x (their number / kGroupM) n-tiles, so
-// each activation and weight strip they read is shared through that L2 by
-// several of them.  The K split index is outermost.  Any permutation is
-// correct; this one only changes locality.
+// groups of GM m-tiles: the workgroups one XCD runs together cover a patch of
+// GM m-tiles x (their number / GM) n-tiles, so each activation and weight
+// strip they read is shared through that L2 by several of them.  GM balances
+// the patch's bytes per K step: an m-tile of R rows reads R x 128 activation
+// bytes, an n-tile of C columns C x 64 weight bytes.  The K split index is
+// outermost.  Any permutation is correct; this one only changes locality.
 constexpr int kXcds = 8;
-constexpr int kGroupM = 8;
+template <int GM = 8>
 __device__ __forceinline__ void tile_of_block(int& bx, int& by, int& bz) {
+  constexpr int kGroupM = GM;
   const int gx = gridDim.x, gy = gridDim.y;
   const int total = gx * gy * gridDim.z;
   const int b = blockIdx.x + gx * (blockIdx.y + gy * blockIdx.z);

@@ -55,7 +55,10 @@ __global__ __launch_bounds__(512, 1) void w4_gemm_pingpong(GemmArgs p, int split
   const int r = lane & 15;
   const int kq = lane >> 4;
   int bx, by, bz;
-  tile_of_block(bx, by, bz);
+  // 256 x 256 tiles: 32 resident per XCD as 4 m-tiles x 8 n-tiles (equal
+  // activation and weight bytes per K step); 128 x 256 tiles as the tiled
+  // kernel's
+  tile_of_block<KS ? 8 : 4>(bx, by, bz);
   // K split (KS): both groups take the same rows and alternate K steps
   const int64_t m_base = KS ? (int64_t)bx * GM : (int64_t)bx * (2 * GM) + grp * GM;
   const int64_t NB = p.N >> 4;
