@@ -160,13 +160,14 @@ int plan_with(int64_t M, int64_t N, int64_t K, bool grouped, int op, const Sched
   const bool stream_ok = op == OP_I8 && !zp && sg == 1 && M > 16 && M <= 64 && stream_tile_m(M, N, grouped, cu);
   // symmetric int8 per channel: the ping-pong kernel (one eight-wave
   // workgroup per CU whose two halves take turns on the MFMAs), K split by
-  // the largest power of two that keeps the workgroups within one per CU.
-  // 256 x 256 tiles from one per two CUs (on 8192 x 21760 4-5% faster than
-  // two tiled workgroups per CU at M = 2048-8192, 3% at M = 1024 with two K
-  // splits); below that, 128 x 256 tiles whose halves split K between them,
-  // when with at most 4 K splits they occupy 3/4 of the CUs or more (M = 384
-  // and 512 with two K splits: 70 and 79 against 80 and 85 us tiled); a
-  // forced 256-row tile selects it too
+  // the largest power of two that keeps the workgroups within one per CU,
+  // once its workgroups occupy 3/4 of the CUs or more.  256 x 256 tiles
+  // when they need at most two K splits for that (8192 x 21760: 4-5% faster
+  // than two tiled workgroups per CU at M = 2048-8192; M = 576-768 with two
+  // splits 114-118 against 128-130 us); else 128 x 256 tiles whose halves
+  // split K between them, with at most 4 K splits (M = 384 and 512 with two
+  // splits: 70 and 79 against 80 and 85 us tiled; 256 x 256 tiles with four
+  // splits took 113 us at M = 512); a forced 256-row tile selects it too
   const bool pc8 = op == OP_I8 && !grouped && !zp && sg == 1;
   auto pp_split = [&](int64_t tiles, int64_t smax) {
     int64_t s = 1;
@@ -175,7 +176,9 @@ int plan_with(int64_t M, int64_t N, int64_t K, bool grouped, int op, const Sched
   };
   const int64_t pp_tiles = ((M + 255) / 256) * ((N + 255) / 256);
   const int64_t pp_ks_tiles = ((M + 127) / 128) * ((N + 255) / 256);
-  const bool pp_auto = 2 * pp_tiles >= cu || 4 * pp_ks_tiles * pp_split(pp_ks_tiles, 4) >= 3LL * cu;
+  const int64_t pp_s256 = pp_split(pp_tiles, 8);
+  const bool pp_256 = pp_s256 <= 2 && 4 * pp_tiles * pp_s256 >= 3LL * cu;
+  const bool pp_auto = pp_256 || 4 * pp_ks_tiles * pp_split(pp_ks_tiles, 4) >= 3LL * cu;
   const bool pp_ok = pc8 && M > 64 && (forced.tile_m == 256 || (!forced.tile_m && !forced.strips && pp_auto));
   plan->path = fp ? (int)fp
                   : (M <= 16 ? PATH_SKINNY : stream_ok ? PATH_STREAM : pp_ok ? PATH_PINGPONG : PATH_TILED);
@@ -214,7 +217,7 @@ int plan_with(int64_t M, int64_t N, int64_t K, bool grouped, int op, const Sched
       return fail(W4_E_SHAPE, "ping-pong kernel: tile rows 128 or 256 (got %lld)", (long long)fbm);
     if (forced.strips && forced.strips != 4)
       return fail(W4_E_SHAPE, "ping-pong kernel: tiles are 256 columns wide (4 column blocks per wave)");
-    plan->bm = (int)(fbm ? fbm : (2 * pp_tiles >= cu ? 256 : 128));
+    plan->bm = (int)(fbm ? fbm : (pp_256 ? 256 : 128));
     plan->bn = 256;
     const int64_t tiles = ((M + plan->bm - 1) / plan->bm) * ((N + 255) / 256);
     int64_t s = fs;

@@ -272,7 +272,10 @@ def test_plan_choices(lib, heuristic_only):
     assert plans[256] == (4, 4, 128, 256)                       # ping-pong, halves splitting K: 64 tiles x 4
     assert plans[512] == (4, 2, 128, 256)                       # ... 128 tiles x 2
     assert w4.gemm_plan(384, 8192, 21760, -1, w4.I8) == (4, 2, 128, 256)     # 96 tiles x 2 (3/4 of the CUs)
-    assert w4.gemm_plan(640, 8192, 21760, -1, w4.I8)[0] == 2                 # 160 tiles x 1: tiled
+    assert w4.gemm_plan(640, 8192, 21760, -1, w4.I8) == (4, 2, 256, 256)    # 96 tiles x 2 (3/4 of the CUs)
+    assert w4.gemm_plan(520, 8192, 21760, -1, w4.I8) == (4, 2, 256, 256)
+    assert w4.gemm_plan(160, 8192, 21760, -1, w4.I8) == (4, 4, 128, 256)    # 64 K-split tiles x 4
+    assert w4.gemm_plan(640, 8192, 8192, -1, w4.I8)[0] == 4
     assert plans[1024] == (4, 2, 256, 256)                      # ping-pong: 128 tiles x 2 K splits
     assert plans[4096] == (4, 1, 256, 256)                      # ping-pong: one 256 x 256 tile per CU
     assert w4.gemm_plan(2048, 8192, 21760, -1, w4.I8) == (4, 1, 256, 256)    # 256 tiles
@@ -370,8 +373,8 @@ def test_options_and_plans(lib, heuristic_only):
         assert lib.w4_set_option(b"force_path", 4) == W4_OK
         w4.set_option("force_path", 0)
         assert w4.gemm_plan(1, 8192, 21760, -1, w4.I8)[0] == 1     # small M -> skinny
-        assert w4.gemm_plan(640, 8192, 21760, -1, w4.I8)[0] == 2   # large M -> tiled
-        assert w4.gemm_plan(4096, 8192, 21760, -1, w4.I8)[0] == 4  # ... ping-pong from a 256-row tile per 2 CUs
+        assert w4.gemm_plan(100, 8192, 21760, -1, w4.I8)[0] == 2   # larger M -> tiled
+        assert w4.gemm_plan(4096, 8192, 21760, -1, w4.I8)[0] == 4  # ... ping-pong once its tiles fill 3/4 of the CUs
         assert lib.w4_set_option(b"norm_exact_sum", 2) == E_SHAPE
         w4.set_option("norm_exact_sum", 1)
         assert w4.get_option("norm_exact_sum") == 1
