@@ -161,13 +161,18 @@ int plan_with(int64_t M, int64_t N, int64_t K, bool grouped, int op, const Sched
   // symmetric int8 per channel: the ping-pong kernel (one eight-wave
   // workgroup per CU whose two halves take turns on the MFMAs), K split by
   // the largest power of two that keeps the workgroups within one per CU,
-  // once its workgroups occupy 3/4 of the CUs or more.  256 x 256 tiles
-  // when they need at most two K splits for that (8192 x 21760: 4-5% faster
-  // than two tiled workgroups per CU at M = 2048-8192; M = 576-768 with two
-  // splits 114-118 against 128-130 us); else 128 x 256 tiles whose halves
-  // split K between them, with at most 4 K splits (M = 384 and 512 with two
-  // splits: 70 and 79 against 80 and 85 us tiled; 256 x 256 tiles with four
-  // splits took 113 us at M = 512); a forced 256-row tile selects it too
+  // once its workgroups occupy 3/4 of the CUs or more and come in whole
+  // rounds of one per CU (a partial last round leaves CUs idle for a whole
+  // tile's time; the tiled kernel, two smaller workgroups per CU, loses less
+  // there).  256 x 256 tiles when they need at most two K splits for that
+  // (8192 x 21760: 4-5% faster than two tiled workgroups per CU at M =
+  // 2048-8192; M = 576-768 with two splits 114-118 against 128-130 us; at
+  // M = 3072, 1.5 rounds, 488 against 431 us tiled); else 128 x 256 tiles
+  // whose halves split K between them, within one round, with at most 4 K
+  // splits (M = 384 and 512 with two splits: 70 and 79 against 80 and 85 us
+  // tiled; 256 x 256 tiles with four splits took 113 us at M = 512; at M =
+  // 1280, 1.25 rounds, 273 against 219 us tiled); a forced 256-row tile
+  // selects it too
   const bool pc8 = op == OP_I8 && !grouped && !zp && sg == 1;
   auto pp_split = [&](int64_t tiles, int64_t smax) {
     int64_t s = 1;
@@ -176,9 +181,10 @@ int plan_with(int64_t M, int64_t N, int64_t K, bool grouped, int op, const Sched
   };
   const int64_t pp_tiles = ((M + 255) / 256) * ((N + 255) / 256);
   const int64_t pp_ks_tiles = ((M + 127) / 128) * ((N + 255) / 256);
-  const int64_t pp_s256 = pp_split(pp_tiles, 8);
-  const bool pp_256 = pp_s256 <= 2 && 4 * pp_tiles * pp_s256 >= 3LL * cu;
-  const bool pp_auto = pp_256 || 4 * pp_ks_tiles * pp_split(pp_ks_tiles, 4) >= 3LL * cu;
+  const int64_t pp_w256 = pp_tiles * pp_split(pp_tiles, 8);       // workgroups
+  const int64_t pp_w128 = pp_ks_tiles * pp_split(pp_ks_tiles, 4);
+  const bool pp_256 = pp_w256 <= 2 * pp_tiles && 4 * pp_w256 >= 3LL * cu && (pp_w256 <= cu || pp_w256 % cu == 0);
+  const bool pp_auto = pp_256 || (4 * pp_w128 >= 3LL * cu && pp_w128 <= cu);
   const bool pp_ok = pc8 && M > 64 && (forced.tile_m == 256 || (!forced.tile_m && !forced.strips && pp_auto));
   plan->path = fp ? (int)fp
                   : (M <= 16 ? PATH_SKINNY : stream_ok ? PATH_STREAM : pp_ok ? PATH_PINGPONG : PATH_TILED);
@@ -294,9 +300,11 @@ int plan_with(int64_t M, int64_t N, int64_t K, bool grouped, int op, const Sched
     plan->splitk = (int)s;
   } else {
     // 8-bit operands: 128-row tiles when there are enough of them (int8
-    // per channel: two workgroups per CU; grouped int8, whose tall tile is
-    // 128 x 128: one; grouped fp8: half a workgroup per CU once M fills the
-    // 128 rows), 64 x 256 tiles otherwise
+    // per channel: one workgroup per CU, with K splits up to two per CU
+    // (8192 x 21760 M = 1280: 219 us, against 253 with 64 x 256 tiles);
+    // its zero-point form: two; grouped int8, whose tall tile is 128 x 128:
+    // one; grouped fp8: half a workgroup per CU once M fills the 128 rows),
+    // 64 x 256 tiles otherwise
     const bool byte = op == OP_I8 || op == OP_FP8;
     const bool fp8g = op == OP_FP8 && grouped;
     const int64_t fbm = forced.tile_m;
@@ -306,7 +314,7 @@ int plan_with(int64_t M, int64_t N, int64_t K, bool grouped, int op, const Sched
       int tall_bm, tall_bn;
       tiled_tile(op, grouped, 1, &tall_bm, &tall_bn, zp);
       const int64_t tall_tiles = ((M + tall_bm - 1) / tall_bm) * ((N + tall_bn - 1) / tall_bn);
-      const int64_t need = (op == OP_I8 && !grouped) ? 2LL * cu : (int64_t)cu;
+      const int64_t need = (op == OP_I8 && !grouped && zp) ? 2LL * cu : (int64_t)cu;
       const bool tall = fbm ? fbm == 128 : (fp8g ? M >= 128 && 2 * tall_tiles >= cu : tall_tiles >= need);
       tiled_tile(op, grouped, tall ? 1 : 0, &plan->bm, &plan->bn, zp);
       // grouped int8: 64 x 128 tiles while there are at most three per CU
