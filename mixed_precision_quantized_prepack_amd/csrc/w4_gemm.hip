@@ -78,7 +78,8 @@ namespace w4 {
 // its D rows for a K block with one 16-byte LDS read, instead of a 64-lane
 // gather from memory per block (which costs the address pipeline as much as
 // the block's weights).  The table's size is set at launch.
-template <int OP, bool GROUPED, bool FLIP, int NS, bool PARTIALS, bool ZP, int SG, bool QA, bool PZ = false>
+template <int OP, bool GROUPED, bool FLIP, int NS, bool PARTIALS, bool ZP, int SG, bool QA, bool PZ = false,
+          bool DA = false>
 __global__ __launch_bounds__(64 * skinny_max_waves(OP, GROUPED)) void w4_gemm_skinny(GemmArgs p, int S) {
   using Acc = typename OpTraits<OP>::Acc;
   constexpr int EB = OpTraits<OP>::kElemBytes;
@@ -169,6 +170,29 @@ __global__ __launch_bounds__(64 * skinny_max_waves(OP, GROUPED)) void w4_gemm_sk
   // blocks past K read
   uint8_t* const qcodes =
       reinterpret_cast<uint8_t*>(skinny_tab) + skinny_tables(OP, GROUPED, ZP) * (NS * p.G * 16 + 16) * 4;
+  // DA (8-bit activations, not fused; M >= 8): each wave stages its K
+  // blocks' 16 x 128 activation bytes in LDS by direct-to-LDS loads of whole
+  // rows (8 rows of 128 bytes per load, where a 16-row fragment load from
+  // memory touches 16 rows for 64 bytes each: int8 per channel 8192 x 21760
+  // at M = 16 19.8 -> 17.8 us), two buffers of U blocks per wave, after the
+  // tables (16-byte aligned).  Chunk c of row R is at slot c ^ swz(R), as in
+  // the tiled kernel, so the fragment reads are conflict-free.  Below M = 8
+  // the loads touch few rows either way, and the LDS round trip cost the fp8
+  // kernel 1-2% at M = 1 and 5.
+  constexpr bool kDma = DA;
+  static_assert(!DA || (EB == 1 && !QA), "staged activations: 8-bit, not fused");
+  uint8_t* const stg = reinterpret_cast<uint8_t*>(skinny_tab) +
+                       ((skinny_tables(OP, GROUPED, ZP) * (NS * p.G * 16 + 16) * 4 + 15) & ~15);
+  uint32_t dma_off[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int row = 8 * h + lane / 8;
+    dma_off[h] = (uint32_t)(row * p.K + (((lane & 7) ^ lds_swizzle<1>(row)) * 16));
+  }
+  int frag_off[AV];
+#pragma unroll
+  for (int j = 0; j < AV; ++j) frag_off[j] = r * 128 + (((kq * AV + j) ^ lds_swizzle<1>(r)) * 16);
+  auto stage_of = [&](int buf, int u) { return stg + ((wave * 2 + buf) * U + u) * 2048; };
   const uint32_t qpad = (uint32_t)(p.M * p.K);
   __shared__ uint32_t qa_max[QA ? 16 : 1];
   __shared__ float qa_s[QA ? 16 : 1];
@@ -251,17 +275,37 @@ __global__ __launch_bounds__(64 * skinny_max_waves(OP, GROUPED)) void w4_gemm_sk
       for (int j = 0; j < NS; ++j)
         wv[buf][u][j] = __builtin_amdgcn_raw_buffer_load_b128(
             rw, (int)(in ? (uint32_t)((j * KB + k) * 1024) + w_lane : kOutOfRange), 0, W4_SKINNY_WPOLICY);
+      if constexpr (kDma) {
+        // rows past M and blocks past K read zeros (no traffic)
 #pragma unroll
-      for (int a = 0; a < AV; ++a) {
-        if constexpr (QA)
-          av[buf][u][a] = *reinterpret_cast<const u32x4*>(
-              qcodes + (in && r < p.M ? a_lane + (uint32_t)(k * 128 + 16 * a) : qpad));
-        else
-          av[buf][u][a] = buffer_load16(ra, in ? a_lane + (uint32_t)(k * 128 * EB + 16 * a) : kOutOfRange);
+        for (int h = 0; h < 2; ++h)
+          buffer_load_lds16(ra, stage_of(buf, u) + h * 1024, in ? dma_off[h] + (uint32_t)(k * 128) : kOutOfRange);
+      } else {
+#pragma unroll
+        for (int a = 0; a < AV; ++a) {
+          if constexpr (QA)
+            av[buf][u][a] = *reinterpret_cast<const u32x4*>(
+                qcodes + (in && r < p.M ? a_lane + (uint32_t)(k * 128 + 16 * a) : qpad));
+          else
+            av[buf][u][a] = buffer_load16(ra, in ? a_lane + (uint32_t)(k * 128 * EB + 16 * a) : kOutOfRange);
+        }
       }
     }
   };
-  auto compute_batch = [&](int buf, int kb, bool pin) {
+  // loads a batch issues (a wait count for the batch issued before it)
+  constexpr int kBatchLoads = U * (NS + (kDma ? 2 : AV));
+  auto compute_batch = [&](int buf, int kb, bool pin, int after) {
+    if constexpr (kDma) {
+      // this batch's staged rows: its loads done (at most the next batch's
+      // still in flight), then the fragment reads
+      asm volatile("" ::: "memory");
+      if (after) __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(kBatchLoads));
+      else __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int a = 0; a < AV; ++a) av[buf][u][a] = *reinterpret_cast<const u32x4*>(stage_of(buf, u) + frag_off[a]);
+    }
     // pin: loads issued before this point stay before it, and the weight
     // words enter an asm statement here, so none of this batch's work moves
     // above the previous refill (which would make its wait cover that refill)
@@ -446,13 +490,13 @@ __global__ __launch_bounds__(64 * skinny_max_waves(OP, GROUPED)) void w4_gemm_sk
       const int nbatch = (KB - wave + S - 1) / S;   // K blocks of this wave
       int kb = 0;
       for (; kb + 2 * U < nbatch; kb += 2 * U) {
-        compute_batch(0, kb, true);
+        compute_batch(0, kb, true, 1);
         load_batch(0, kb + 2 * U);
-        compute_batch(1, kb + U, true);
+        compute_batch(1, kb + U, true, 1);
         load_batch(1, kb + 3 * U);
       }
-      compute_batch(0, kb, true);
-      compute_batch(1, kb + U, true);
+      compute_batch(0, kb, true, 1);
+      compute_batch(1, kb + U, true, 0);
     }
   } else {
     // Each step issues the next batch, then computes the current one.
@@ -462,13 +506,13 @@ __global__ __launch_bounds__(64 * skinny_max_waves(OP, GROUPED)) void w4_gemm_sk
       int kb = 0;
       for (; kb + 2 * U < nbatch; kb += 2 * U) {
         load_batch(1, kb + U);
-        compute_batch(0, kb, false);
+        compute_batch(0, kb, false, 1);
         load_batch(0, kb + 2 * U);
-        compute_batch(1, kb + U, false);
+        compute_batch(1, kb + U, false, 1);
       }
       load_batch(1, kb + U);
-      compute_batch(0, kb, false);
-      compute_batch(1, kb + U, false);
+      compute_batch(0, kb, false, 1);
+      compute_batch(1, kb + U, false, 0);
     }
   }
   // (either way: whole pairs of batches, then the last pair, whose second
@@ -1190,11 +1234,17 @@ static hipError_t launch_typed(const GemmArgs& args, const GemmPlan& plan, hipSt
     const unsigned threads = 64u * (unsigned)(S > 4 * ns ? S : 4 * ns);
     const dim3 grid((unsigned)(args.N / plan.bn));
     const bool part = args.mode == MODE_PARTIALS;
-    const size_t tab = (size_t)skinny_table_bytes(OP, GROUPED, args.G, ns, ZP);   // checked by the plan
+    // tables (checked by the plan), then (staged 8-bit activations) each
+    // wave's two staging buffers of U 2 KiB blocks
+    constexpr bool kByteAct = OP == OP_I8 || OP == OP_FP8;
+    const bool da = kByteAct && args.M >= 8;
+    const int su = GROUPED ? (ns == 1 ? W4_SKINNY_UG1 : W4_SKINNY_UG2) : W4_SKINNY_U8;
+    const size_t tab = (((size_t)skinny_table_bytes(OP, GROUPED, args.G, ns, ZP) + 15) & ~(size_t)15) +
+                       (da ? (size_t)(threads / 64) * 2 * su * 2048 : 0);
     if (args.x) {
       // fused quantisation: the codes and their pad follow the tables
       if constexpr ((OP == OP_I8 || OP == OP_FP8) && !ZP && SG == 1) {
-        const size_t lds = tab + (size_t)(args.M * args.K) + 32;
+        const size_t lds = (size_t)skinny_table_bytes(OP, GROUPED, args.G, ns, ZP) + (size_t)(args.M * args.K) + 32;
         if (ns == 2)
           hipLaunchKernelGGL((w4_gemm_skinny<OP, GROUPED, FLIP, 2, false, false, 1, true>), grid, dim3(threads), lds,
                              stream, args, S);
@@ -1204,6 +1254,26 @@ static hipError_t launch_typed(const GemmArgs& args, const GemmPlan& plan, hipSt
         return hipGetLastError();
       } else {
         return hipErrorInvalidValue;
+      }
+    }
+    if constexpr (kByteAct) {
+      if (da) {
+        if (ns == 2) {
+          if (part)
+            hipLaunchKernelGGL((w4_gemm_skinny<OP, GROUPED, FLIP, 2, true, ZP, SG, false, false, true>), grid,
+                               dim3(threads), tab, stream, args, S);
+          else
+            hipLaunchKernelGGL((w4_gemm_skinny<OP, GROUPED, FLIP, 2, false, ZP, SG, false, false, true>), grid,
+                               dim3(threads), tab, stream, args, S);
+        } else {
+          if (part)
+            hipLaunchKernelGGL((w4_gemm_skinny<OP, GROUPED, FLIP, 1, true, ZP, SG, false, false, true>), grid,
+                               dim3(threads), tab, stream, args, S);
+          else
+            hipLaunchKernelGGL((w4_gemm_skinny<OP, GROUPED, FLIP, 1, false, ZP, SG, false, false, true>), grid,
+                               dim3(threads), tab, stream, args, S);
+        }
+        return hipGetLastError();
       }
     }
     if (ns == 2) {
