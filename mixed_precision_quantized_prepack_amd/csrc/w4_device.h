@@ -51,18 +51,37 @@ constexpr uint32_t kFp8PosHi = 0x4E4C4A48u;
 constexpr uint32_t kFp8NegLo = 0xCACCCED0u;
 constexpr uint32_t kFp8NegHi = 0xB8C0C4C8u;
 
+// A constant the compiler must keep in a scalar (vector) register: the
+// three-source VALU encodings of gfx950 take no literal, so (x & c1) | c2
+// with both constants as literals costs two instructions; with c1 in a
+// scalar and c2 in a vector register it is one v_and_or_b32.  The empty asm
+// has no side effects, so the value is loaded once, outside the loops.
+__device__ __forceinline__ uint32_t in_sgpr(uint32_t v) {
+  uint32_t r;
+  asm("" : "=s"(r) : "0"(v));
+  return r;
+}
+__device__ __forceinline__ uint32_t in_vgpr(uint32_t v) {
+  uint32_t r;
+  asm("" : "=v"(r) : "0"(v));
+  return r;
+}
+
 __device__ __forceinline__ void expand_fp8(uint32_t w, uint32_t& k0123, uint32_t& k4567) {
   // table lookups on the low three bits of each nibble
+  const uint32_t w4 = w >> 4;
   const uint32_t sel_lo = w & 0x07070707u;
-  const uint32_t sel_hi = (w >> 4) & 0x07070707u;
+  const uint32_t sel_hi = w4 & 0x07070707u;
   const uint32_t p_lo = __builtin_amdgcn_perm(kFp8PosHi, kFp8PosLo, sel_lo);
   const uint32_t n_lo = __builtin_amdgcn_perm(kFp8NegHi, kFp8NegLo, sel_lo);
   const uint32_t p_hi = __builtin_amdgcn_perm(kFp8PosHi, kFp8PosLo, sel_hi);
   const uint32_t n_hi = __builtin_amdgcn_perm(kFp8NegHi, kFp8NegLo, sel_hi);
   // per byte, keep byte i of the positive result (selector i) or of the
   // negative one (selector i + 4): bit 3 of the nibble moved to bit 2
-  const uint32_t pick_lo = ((w >> 1) & 0x04040404u) | 0x03020100u;
-  const uint32_t pick_hi = ((w >> 5) & 0x04040404u) | 0x03020100u;
+  const uint32_t bit2 = in_sgpr(0x04040404u);
+  const uint32_t ident = in_vgpr(0x03020100u);
+  const uint32_t pick_lo = ((w >> 1) & bit2) | ident;
+  const uint32_t pick_hi = ((w4 >> 1) & bit2) | ident;
   k0123 = __builtin_amdgcn_perm(n_lo, p_lo, pick_lo);
   k4567 = __builtin_amdgcn_perm(n_hi, p_hi, pick_hi);
 }

@@ -204,16 +204,18 @@ def test_w4a8_outputs(wl, wtype, M, bias):
     assert_w4a8(out, ref, dc.wl.out_dtype, dc.wl.q_dtype, dc.G, label=f"{wl} M={M}")
 
 
-@pytest.mark.parametrize("wl,K", [("w4a8_i8_g128_o", 16384), ("w4a8_i8_g128_o", 106496),
+@pytest.mark.parametrize("wl,K", [("w4a8_i8_g128_o", 16384), ("w4a8_i8_g128_o", 96000), ("w4a8_i8_g128_o", 106496),
                                   ("w4a8_fp8_g128_28672x8192", 53248)])
-def test_w4a8_small_m_long_grouped_k(wl, K):
+@pytest.mark.parametrize("M", [3, 12])
+def test_w4a8_small_m_long_grouped_k(wl, K, M):
     """Grouped small-M problems with long K: the staged group-scale table
-    holds up to 384 groups per strip; past that the plan uses the tiled
-    kernel."""
-    dc = DeviceCase(wl, 3, N=64, K=K, seed_base=K % 1000)
+    holds up to 767 groups for one strip (K = 96000: 750 groups, 47 KiB);
+    past that the plan uses the tiled kernel.  M = 12 also stages the
+    activations (64 KiB for eight waves next to the table)."""
+    dc = DeviceCase(wl, M, N=64, K=K, seed_base=K % 1000 + M)
     out, *_ = run_w4a8(dc)
     codes, sa = dc.oracle_quant()
-    assert_w4a8(out, dc.oracle_w4a8(codes, sa), dc.wl.out_dtype, dc.wl.q_dtype, dc.G, label=f"{wl} K={K}")
+    assert_w4a8(out, dc.oracle_w4a8(codes, sa), dc.wl.out_dtype, dc.wl.q_dtype, dc.G, label=f"{wl} K={K} M={M}")
 
 
 @pytest.mark.parametrize("wl", ["w4a8_i8_pc_256x512", "w4a8_fp8_g128_28672x8192", "w4a8_i8_g128_down"])
