@@ -415,13 +415,15 @@ def traffic_for(set_name: str, kernel_key: str, grids) -> "float | None":
     return round(sum(vals) / len(vals)) if vals else None
 
 
-def kernel_key_of(wl, plan) -> str:
-    """The kernel trace's name of the GEMM instance a plan launches."""
+def kernel_key_of(wl, plan, M: int) -> str:
+    """The kernel trace's name of the GEMM instance a plan launches at M."""
     path, split, tm, tn = plan
     op = {"i8": 0, "fp8": 1, "f16": 2, "bf16": 3}[op_name(wl)]
     grouped = "true" if wl.group_size != wl.K else "false"
     if path == 1:
-        return f"w4::w4_gemm_skinny<{op}, {grouped}, false, {tn // 16}, false, false, 1, false, false>"
+        # 8-bit activations are staged in LDS from M = 8 (the last flag)
+        staged = "true" if op in (0, 1) and M >= 8 else "false"
+        return f"w4::w4_gemm_skinny<{op}, {grouped}, false, {tn // 16}, false, false, 1, false, false, {staged}>"
     nt, mt = tn // 64, tm // 16
     if path == 4:
         # 128-row tiles are the form whose two halves split K
@@ -830,7 +832,7 @@ def main(argv=None) -> int:
     dom_plan = plans[dom[0]["M"]]
     roofline = {"bound": "mfma", "achieved": round(ach, 2), "peak": INT8_PEAK_TOPS, "unit": "TOPS",
                 "frac": round(ach / INT8_PEAK_TOPS, 4),
-                "traffic": traffic_for("w4a8_i8_pc_8192x21760", kernel_key_of(wl, dom_plan),
+                "traffic": traffic_for("w4a8_i8_pc_8192x21760", kernel_key_of(wl, dom_plan, dom[0]["M"]),
                                        {grid_threads(wl, plans[pm["M"]], pm["M"]) for pm in dom}),
                 "kernel": dom_name, "launches": [pm["M"] for pm in dom], "avg_launch_us": round(dur, 2),
                 "alg_ops_per_launch": flops,
@@ -843,10 +845,13 @@ def main(argv=None) -> int:
         b = sum(gemm_alg_bytes(wl, pm["M"]) for pm in small) / len(small)
         dur = sum(pm["gemm_us"] for pm in small) / len(small)
         gb = b / (dur * 1e-6) / 1e9
+        # per M, its own instance's counters (M >= 8 stages the activations)
+        per = [traffic_for("w4a8_i8_pc_8192x21760", kernel_key_of(wl, plans[pm["M"]], pm["M"]),
+                           {grid_threads(wl, plans[pm["M"]], pm["M"])}) for pm in small]
+        small_traffic = round(sum(per) / len(per)) if all(t is not None for t in per) else None
         roofline_small = {"bound": "hbm", "achieved": round(gb, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                           "frac": round(gb / HBM_PEAK_GBPS, 4),
-                          "traffic": traffic_for("w4a8_i8_pc_8192x21760", kernel_key_of(wl, plans[small[0]["M"]]),
-                                                 {grid_threads(wl, plans[pm["M"]], pm["M"]) for pm in small}),
+                          "traffic": small_traffic,
                           "kernel": small[0]["kernel"], "launches": [pm["M"] for pm in small],
                           "avg_launch_us": round(dur, 2), "alg_bytes_per_launch": b,
                           "note": f"avg_launch_us from {REPS} back-to-back launches per M between two events"}
