@@ -41,6 +41,11 @@
  *     enqueued work surface at the caller's next synchronisation, as usual
  *     for HIP.
  *   - M = 0 is valid and enqueues nothing.
+ *   - Size limits of the GEMMs (and of w4_gemm_plan / w4_gemm_workspace_bytes),
+ *     from their 32-bit buffer offsets: K <= 2^22, and at most 2^29 - 4
+ *     weight scales (N x K / group_size, or N per channel); larger problems
+ *     return W4_E_SHAPE.  Per-channel int8 also needs K <= 131072 (its int32
+ *     accumulators).
  */
 #ifndef W4_H_
 #define W4_H_

@@ -150,6 +150,12 @@ int check_group(int64_t group_size, int64_t K, bool small_ok = false) {
 // kernel keeps a second (zero-point) table.
 int plan_with(int64_t M, int64_t N, int64_t K, bool grouped, int op, const Sched& forced, GemmPlan* plan,
               bool zp = false, int sg = 1) {
+  // The kernels address a tile's activation rows (up to 256 of them), a
+  // wave's weight blocks and the scale / zero-point tables with 32-bit buffer
+  // offsets into ranges of at most 2 GiB.
+  if (K > ((int64_t)1 << 22)) return fail(W4_E_SHAPE, "GEMMs with K=%lld above 2^22 are not supported", (long long)K);
+  if (N * (grouped ? (K / 128) * sg : 1) > ((int64_t)1 << 29) - 4)
+    return fail(W4_E_SHAPE, "GEMMs with more than 2^29 - 4 scales (N x groups) are not supported");
   const int64_t fp = forced.path, fs = forced.splitk;
   const int64_t KB = K / 128;
   const int cu = cu_count();

@@ -81,3 +81,15 @@ def test_plans_reject_invalid_shapes(lib):
                 (1, 16, 256, 64, w4.I8), (1, 16, 384, 256, w4.F16)):
         with pytest.raises(w4.W4Error):
             w4.gemm_plan(*bad)
+
+
+def test_plans_reject_shapes_past_32bit_offsets(lib):
+    """K above 2^22 (a 256-row tile of K bytes, or 64 rows of K fp16 values,
+    must stay within a 2 GiB buffer range), and more than 2^29 - 4 scales."""
+    w4.gemm_plan(300, 16, 1 << 22, 128, w4.FP8_E4M3)
+    w4.gemm_plan(1, 1 << 16, 1 << 16, 128, w4.I8)            # 2^25 scales
+    w4.gemm_plan(1, (1 << 29) - 16, 128, -1, w4.BF16)        # per channel: one scale per column
+    for bad in ((300, 16, (1 << 22) + 128, 128, w4.FP8_E4M3), (1, 16, 1 << 23, 128, w4.BF16),
+                (1, 1 << 20, 1 << 16, 128, w4.I8), (1, 1 << 18, 1 << 18, 64, w4.F16), (1, 1 << 29, 128, -1, w4.I8)):
+        with pytest.raises(w4.W4Error):
+            w4.gemm_plan(*bad)
