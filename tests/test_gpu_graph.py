@@ -56,6 +56,8 @@ def _capture(step):
 
 @pytest.mark.parametrize("wl,M,N,K,want_path,want_split", [
     ("w4a8_i8_pc_8192x21760", 1, 1024, 4096, 1, 8),       # small-M kernel, K split across waves
+    ("w4a8_i8_pc_8192x21760", 12, 1024, 4096, 1, 8),      # small-M, activations staged in LDS
+    ("w4a8_fp8_g128_28672x8192", 12, 1024, 2048, 1, 2),   # small-M fp8 g128, staged activations
     ("w4a8_i8_pc_8192x21760", 64, 1024, 4096, 3, 16),     # streaming kernel + split-K reduce
     ("w4a8_i8_pc_8192x21760", 300, 1024, 4096, 2, 8),     # ragged tile rows + reduce
     ("w4a8_i8_g128_o", 130, 2048, 4096, 2, 4),            # grouped int8, tiled 64 x 128 + reduce
