@@ -78,9 +78,21 @@ namespace w4 {
 // its D rows for a K block with one 16-byte LDS read, instead of a 64-lane
 // gather from memory per block (which costs the address pipeline as much as
 // the block's weights).  The table's size is set at launch.
+
+// Waves per SIMD the small-M kernel is compiled for (the second launch
+// bound): six for grouped 8-bit problems with two strips or staged
+// activations, whose eight-wave workgroups then fit three to a CU (at most
+// 84 registers, no spills); no bound otherwise (the other forms spill under
+// it).
+template <int OP, bool GROUPED, int NS, bool ZP, bool QA, bool DA>
+constexpr int skinny_min_waves() {
+  return (OP == OP_I8 || OP == OP_FP8) && GROUPED && !ZP && !QA && (NS == 2 || DA) ? 6 : 1;
+}
+
 template <int OP, bool GROUPED, bool FLIP, int NS, bool PARTIALS, bool ZP, int SG, bool QA, bool PZ = false,
           bool DA = false>
-__global__ __launch_bounds__(64 * skinny_max_waves(OP, GROUPED)) void w4_gemm_skinny(GemmArgs p, int S) {
+__global__ __launch_bounds__(64 * skinny_max_waves(OP, GROUPED), (skinny_min_waves<OP, GROUPED, NS, ZP, QA, DA>()))
+void w4_gemm_skinny(GemmArgs p, int S) {
   using Acc = typename OpTraits<OP>::Acc;
   constexpr int EB = OpTraits<OP>::kElemBytes;
   constexpr int AV = act_vecs<OP>();
