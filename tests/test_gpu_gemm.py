@@ -65,6 +65,29 @@ def test_int8_partials_bit_exact(wl, path, M, split, wtype):
     assert np.array_equal(part.cpu().numpy().astype(np.int64), want)
 
 
+@pytest.mark.parametrize("wl", ["w4a8_i8_pc_256x512", "w4a8_i8_g128_o", "w4a8_fp8_g128_28672x8192"])
+@pytest.mark.parametrize("M,waves,strips", [(8, 4, 2), (12, 8, 2), (16, 3, 1), (13, 8, 1)])
+def test_small_m_staged_partials(wl, M, waves, strips):
+    """The small-M kernel from M = 8, whose activations are staged in LDS,
+    with one and two strips (grouped two-strip forms are compiled for six
+    waves per SIMD): int8 partials bit-exact, fp8 within its MFMA bound."""
+    dc = DeviceCase(wl, M, N=512, K=1536, seed_base=M * 13 + waves)
+    q = dc.wl.q_dtype
+    packed = w4.prepack_B(dc.w_logical, "i8")
+    aq, _ = w4.quant_act_per_token(dc.a, q)
+    gs = -1 if dc.gs == dc.K else dc.gs
+    with options(1, waves, 0, strips):
+        assert w4.gemm_plan(M, dc.N, dc.K, gs, w4.I8 if q == "i8" else w4.FP8_E4M3) == (1, waves, 16, 16 * strips)
+        part = w4.w4a8_gemm_partials(aq, packed, dc.N, gs)
+    codes = aq.cpu().numpy()
+    want = O.w4a8_group_partials(codes, q, dc.case.w_logical.numpy(), dc.K, "int4", dc.gs)
+    if q == "i8":
+        assert np.array_equal(part.cpu().numpy().astype(np.int64), want)
+    else:
+        got = part.cpu().numpy().astype(np.float64)
+        assert np.all(np.abs(got - want * 2.0 ** -9) <= fp8_partials_bound(codes, dc.case.w_logical.numpy(), dc.K))
+
+
 @pytest.mark.parametrize("wl", ["w4a8_i8_pc_256x512", "w4a8_i8_g128_o"])
 @pytest.mark.parametrize("M,split", [(17, 1), (130, 1), (200, 3), (256, 2)])
 def test_int8_partials_bit_exact_tall_tiles(wl, M, split):
