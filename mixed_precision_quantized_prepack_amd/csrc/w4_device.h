@@ -55,7 +55,8 @@ constexpr uint32_t kFp8NegHi = 0xB8C0C4C8u;
 // three-source VALU encodings of gfx950 take no literal, so (x & c1) | c2
 // with both constants as literals costs two instructions; with c1 in a
 // scalar and c2 in a vector register it is one v_and_or_b32.  The empty asm
-// has no side effects, so the value is loaded once, outside the loops.
+// hides the constant from the compiler; it still sets the two registers once
+// per loop iteration (one scalar and one vector move), not once per word.
 __device__ __forceinline__ uint32_t in_sgpr(uint32_t v) {
   uint32_t r;
   asm("" : "=s"(r) : "0"(v));
