@@ -1,7 +1,8 @@
 """The C ABI's host code (argument validation, planning, options, schedule
 table: w4_api.cpp) built with AddressSanitizer and UndefinedBehaviorSanitizer
-on the host side, running the ABI tests of tests/test_abi.py on the CPU (no
-kernel is launched).  The sanitized library is loaded through W4_LIBRARY with
+on the host side, running the ABI tests of tests/test_abi.py and the planner
+properties of tests/test_plan_properties.py on the CPU (no kernel is
+launched).  The sanitized library is loaded through W4_LIBRARY with
 the sanitizer runtime preloaded into a child interpreter."""
 import os
 import subprocess
@@ -40,7 +41,8 @@ def test_sanitized_library_is_the_one_loaded(sanitized_lib):
 
 
 def test_abi_tests_pass_under_host_sanitizers(sanitized_lib):
-    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider", "tests/test_abi.py"],
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider", "tests/test_abi.py",
+                        "tests/test_plan_properties.py"],
                        cwd=ROOT, env=_env(sanitized_lib), capture_output=True, text=True, timeout=600)
     out = r.stdout + r.stderr
     assert r.returncode == 0, out[-6000:]
